@@ -1,0 +1,244 @@
+#!/usr/bin/env python3
+"""Benchmark: decode attention over a block-quantized KV cache on one MI355X.
+
+Headline workload (metric "decode-attention effective KV GB/s @64K ctx"):
+  one sequence, 24 query heads / 4 KV heads, head_dim 256, Q4_G64 K and V,
+  context 65536.  One step = kvq_append of the new token's K and V (row 65535)
+  followed by kvq_attend_decode over all 65536 rows -- the whole decode hot
+  path (quantize-on-append, split-K attention, log-sum-exp combine).
+  The timed loop rotates over 16 independent caches (>= 1 GB in total) so
+  the 256 MB last-level cache cannot serve the K/V bytes.
+
+value = algorithmic bytes per step / step time, where the algorithmic bytes
+are the quantized K+V bytes of every attended row read once per kv-head
+(65536 x 4 x (136 + 136) B) plus the query, the output and the appended row
+in/out.  Prefill (2048-token causal chunk over a 32768-token quantized prefix)
+is reported beside it in TFLOP/s when its kernel is available.
+
+Prints one JSON line.  Single GPU only: --gpus above 1 exits with a message.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+ROTATE = 16
+
+
+def _args():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=500)
+    p.add_argument("--warmup", type=int, default=50)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-prefill", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    return p.parse_args()
+
+
+def decode_bytes(cfg) -> dict:
+    from block_quantized_kv_amd import kvq_row_code_bytes
+    kc, vc = cfg.layers[0]
+    d, H, n = cfg.head_dim, cfg.n_kv_heads, cfg.ctx
+    row_k = kvq_row_code_bytes(kc, d) + 2 * d // (64 if kc == "q4_g64" else 32)
+    row_v = kvq_row_code_bytes(vc, d) + 2 * d // (64 if vc == "q4_g64" else 32)
+    kv = n * H * (row_k + row_v)
+    qo = 2 * cfg.n_seqs * cfg.n_q_heads * d * 4
+    app = H * d * 4 * 2 + H * (row_k + row_v)
+    return {"kv": kv, "q_out": qo, "append": app, "step": kv + qo + app,
+            "attend_kernel": kv + cfg.n_seqs * cfg.n_q_heads * d * 4}
+
+
+def main():
+    args = _args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no "
+              "multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import workloads
+    from block_quantized_kv_amd import (Layer, kvq_append, kvq_attend_decode,
+                                        kvq_decode_workspace_bytes, load_library)
+    load_library()
+    dev = torch.device("cuda:0")
+    cfg = workloads.CONFIGS[3]
+    kc, vc = cfg.layers[0]
+    n, H, d = cfg.ctx, cfg.n_kv_heads, cfg.head_dim
+
+    # ---- setup (untimed): fill rows 0..n-2, keep row n-1 as the step's new token
+    base = Layer.create(kc, vc, d, H, 1, cfg.capacity, device=dev)
+    k = workloads.kv_rows(cfg, 0, 0, "k", 0, n, dev)
+    v = workloads.kv_rows(cfg, 0, 0, "v", 0, n, dev)
+    for a in range(0, n - 1, 16384):
+        b = min(n - 1, a + 16384)
+        kvq_append(base, k[a:b].contiguous(), v[a:b].contiguous(),
+                   torch.zeros(b - a, dtype=torch.int32, device=dev),
+                   torch.arange(a, b, dtype=torch.int64, device=dev))
+    k_new, v_new = k[n - 1:n].contiguous(), v[n - 1:n].contiguous()
+    host_kv = (k.cpu().numpy(), v.cpu().numpy()) if not args.no_cpu_baseline else None
+    del k, v
+    caches = [base] + [base.clone() for _ in range(ROTATE - 1)]
+    q = workloads.queries(cfg, 0, dev)
+    seq_len = torch.tensor([n], dtype=torch.int64, device=dev)
+    new_seq = torch.zeros(1, dtype=torch.int32, device=dev)
+    new_pos = torch.tensor([n - 1], dtype=torch.int64, device=dev)
+    ws = torch.empty(kvq_decode_workspace_bytes(base, cfg.n_q_heads, 1, n), dtype=torch.uint8,
+                     device=dev)
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        L = caches[i % ROTATE]
+        kvq_append(L, k_new, v_new, new_seq, new_pos, stream=stream)
+        kvq_attend_decode(L, q, seq_len, n, cfg.scale, out=out, workspace=ws, stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # ---- timed region: exactly `steps` steps, synchronized on both sides
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(args.steps):
+        L = caches[i % ROTATE]
+        kvq_append(L, k_new, v_new, new_seq, new_pos, stream=stream)
+        ev[i][0].record(stream)
+        kvq_attend_decode(L, q, seq_len, n, cfg.scale, out=out, workspace=ws, stream=stream)
+        ev[i][1].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = t_start.elapsed_time(t_end)
+    attend_ms = [a.elapsed_time(b) for a, b in ev]
+    ms_per_step = total_ms / args.steps
+    nb = decode_bytes(cfg)
+    value = nb["step"] / (ms_per_step * 1e-3) / 1e9
+    att_avg_ms = float(np.mean(attend_ms))
+    achieved = nb["attend_kernel"] / (att_avg_ms * 1e-3) / 1e9
+
+    result = {
+        "metric": "decode-attention effective KV GB/s @64K ctx",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16xf16->f32 (int4 codes)",
+        "data": "synthetic, seeded (N(0,1) x log-uniform per-channel scales)",
+        "config": {"workload": cfg.name, "context": n, "n_q_heads": cfg.n_q_heads,
+                   "n_kv_heads": H, "head_dim": d, "k_codec": kc, "v_codec": vc,
+                   "step": "kvq_append(1 token) + kvq_attend_decode", "rotated_caches": ROTATE,
+                   "bytes_per_step": nb["step"], "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+                   "wall_s_timed_region": round(wall, 4)},
+        "roofline": {"bound": "hbm", "kernel": "kvq_attend_decode (decode_kernel + combine_kernel)",
+                     "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": nb["attend_kernel"], "avg_launch_ms": round(att_avg_ms, 5)},
+    }
+
+    if not args.no_prefill:
+        result["prefill"] = run_prefill(torch, dev, args)
+
+    if host_kv is not None:
+        result["cpu_baseline"] = cpu_baseline(cfg, host_kv, q.cpu().numpy(), nb, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def run_prefill(torch, dev, args):
+    """2048-token causal chunk over a 32768-token quantized prefix (q8_0 K / q4_0 V)."""
+    import workloads
+    from block_quantized_kv_amd import Layer, kvq_append, kvq_attend_prefill
+    from block_quantized_kv_amd._binding import KvqError
+    P, T = workloads.PREFILL["prefix"], workloads.PREFILL["chunk"]
+    hq, hkv, d = workloads.PREFILL["n_q_heads"], workloads.PREFILL["n_kv_heads"], workloads.PREFILL["head_dim"]
+    kc, vc = workloads.PREFILL["k_codec"], workloads.PREFILL["v_codec"]
+    layer = Layer.create(kc, vc, d, hkv, 1, P + T, device=dev)
+    q, k, v = workloads.prefill_inputs(dev)
+    for a in range(0, P + T, 16384):
+        b = min(P + T, a + 16384)
+        kvq_append(layer, k[a:b].contiguous(), v[a:b].contiguous(),
+                   torch.zeros(b - a, dtype=torch.int32, device=dev),
+                   torch.arange(a, b, dtype=torch.int64, device=dev))
+    flops = 4.0 * d * hq * sum(P + t + 1 for t in range(T))
+    try:
+        kvq_attend_prefill(layer, q, 0, P, 1.0 / d ** 0.5)
+    except KvqError as e:
+        return {"status": "unavailable", "reason": str(e)}
+    out = torch.empty(T, hq, d, device=dev)
+    for _ in range(3):
+        kvq_attend_prefill(layer, q, 0, P, 1.0 / d ** 0.5, out=out)
+    torch.cuda.synchronize()
+    reps = 10
+    a_ev, b_ev = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a_ev.record()
+    for _ in range(reps):
+        kvq_attend_prefill(layer, q, 0, P, 1.0 / d ** 0.5, out=out)
+    b_ev.record()
+    torch.cuda.synchronize()
+    ms = a_ev.elapsed_time(b_ev) / reps
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"metric": "prefill TFLOP/s", "value": round(tf, 2), "unit": "TFLOP/s",
+            "ms_per_chunk": round(ms, 4), "flop": flops,
+            "config": {"prefix": P, "chunk": T, "n_q_heads": hq, "n_kv_heads": hkv, "head_dim": d,
+                       "k_codec": kc, "v_codec": vc},
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": None}}
+
+
+def cpu_baseline(cfg, host_kv, q, nb, seconds):
+    """The CPU oracle (single-threaded C, binary64 attention) doing the same
+    decode step on the host: dequantize the cached rows of one KV head and
+    attend its 6 query heads; repeated over KV heads until ~`seconds`."""
+    import numpy as np
+
+    import oracle
+    kc, vc = cfg.layers[0]
+    k, v = host_kv
+    G = cfg.gqa
+    # the cache the oracle reads: its own codes of every row (setup, untimed)
+    codes = []
+    for g in range(cfg.n_kv_heads):
+        codes.append((oracle.quantize_rows(kc, np.ascontiguousarray(k[:, g])),
+                      oracle.quantize_rows(vc, np.ascontiguousarray(v[:, g]))))
+    done_heads = 0
+    t0 = time.perf_counter()
+    while True:
+        g = done_heads % cfg.n_kv_heads
+        (kc_, ks_), (vc_, vs_) = codes[g]
+        kh = oracle.dequant_rows(kc, kc_, ks_, cfg.head_dim)[None]
+        vh = oracle.dequant_rows(vc, vc_, vs_, cfg.head_dim)[None]
+        oracle.attend_decode(q[0][g * G:(g + 1) * G], kh, vh, cfg.ctx, cfg.scale)
+        done_heads += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    el = time.perf_counter() - t0
+    bytes_done = nb["kv"] / cfg.n_kv_heads * done_heads
+    return {"value": round(bytes_done / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done_heads} kv-head passes (dequant + fp64 attention of {G} q-heads over "
+                      f"{cfg.ctx} rows each) of the 64K-context step, {el:.1f} s",
+            "cpu": platform.processor() or platform.machine(), "host_cores": os.cpu_count()}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,28 @@
+"""block_quantized_kv_amd -- attention over a block-quantized KV cache on MI355X.
+
+The compute path is the HIP library ``libkvq.so`` (C ABI in include/kvq.h);
+this package is a thin ctypes binding over it with the same entry-point names
+(argument marshalling only).  PyTorch provides device memory and streams.
+
+There is no CPU or PyTorch fallback: importing the binding without the built
+library raises.
+"""
+from ._binding import (  # noqa: F401
+    BLOCK_ROWS,
+    CODECS,
+    KvqError,
+    Plane,
+    Layer,
+    kvq_append,
+    kvq_attend_decode,
+    kvq_attend_prefill,
+    kvq_dequant,
+    kvq_decode_workspace_bytes,
+    kvq_prefill_workspace_bytes,
+    kvq_plane_bytes,
+    kvq_row_code_bytes,
+    kvq_status_str,
+    kvq_last_error,
+    library_path,
+    load_library,
+)

@@ -1,0 +1,244 @@
+"""ctypes binding of libkvq.so: the C ABI of include/kvq.h, one Python function
+per entry point, over torch tensors (device pointers and the current stream).
+Argument marshalling only -- every step runs in the HIP library."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+BLOCK_ROWS = 32
+CODECS = {"q8_0": 0, "q4_0": 1, "q4_g64": 2}
+GROUP = {"q8_0": 32, "q4_0": 32, "q4_g64": 64}
+ROLE_K, ROLE_V = 0, 1
+
+STATUS = {0: "KVQ_OK", 1: "KVQ_EINVAL", 2: "KVQ_EUNSUPPORTED", 3: "KVQ_ERANGE",
+          4: "KVQ_EWORKSPACE", 5: "KVQ_EHIP"}
+
+
+class KvqError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+class _Plane(ctypes.Structure):
+    _fields_ = [("codec", ctypes.c_int32), ("role", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("n_seqs", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("capacity", ctypes.c_int64), ("codes", ctypes.c_void_p),
+                ("scales", ctypes.c_void_p)]
+
+
+class _Layer(ctypes.Structure):
+    _fields_ = [("k", _Plane), ("v", _Plane)]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return os.path.join(HERE, "libkvq.so")
+
+
+def load_library():
+    """Loads libkvq.so; raises if it has not been built (no fallback exists)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with block_quantized_kv_amd/build.py "
+                          "(there is no CPU or PyTorch fallback)")
+    lib = ctypes.CDLL(path)
+    P, i32, i64, sz, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+    PL, LY = ctypes.POINTER(_Plane), ctypes.POINTER(_Layer)
+    sig = {
+        "kvq_row_code_bytes": (sz, [i32, i32]),
+        "kvq_plane_bytes": (i32, [i32, i32, i32, i32, i64, ctypes.POINTER(sz), ctypes.POINTER(sz)]),
+        "kvq_append": (i32, [LY, P, P, P, P, i32, P, P]),
+        "kvq_decode_workspace_bytes": (sz, [LY, i32, i32, i64]),
+        "kvq_attend_decode": (i32, [LY, P, P, i32, i32, i64, f32, P, P, sz, P]),
+        "kvq_prefill_workspace_bytes": (sz, [LY, i32, i32]),
+        "kvq_attend_prefill": (i32, [LY, P, i32, i64, i32, i32, f32, P, P, sz, P]),
+        "kvq_dequant": (i32, [PL, i32, i64, i64, P, P]),
+        "kvq_status_str": (ctypes.c_char_p, [i32]),
+        "kvq_last_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def kvq_status_str(status: int) -> str:
+    return load_library().kvq_status_str(status).decode()
+
+
+def kvq_last_error() -> str:
+    return load_library().kvq_last_error().decode()
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise KvqError(status, kvq_last_error())
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream or None
+
+
+def kvq_row_code_bytes(codec: str, head_dim: int) -> int:
+    return int(load_library().kvq_row_code_bytes(CODECS[codec], head_dim))
+
+
+def kvq_plane_bytes(codec: str, head_dim: int, n_kv_heads: int, n_seqs: int, capacity: int):
+    c, s = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(load_library().kvq_plane_bytes(CODECS[codec], head_dim, n_kv_heads, n_seqs, capacity,
+                                          ctypes.byref(c), ctypes.byref(s)))
+    return c.value, s.value
+
+
+class Plane:
+    """One K or V cache plane (device memory owned by torch tensors)."""
+
+    def __init__(self, codec: str, role: int, head_dim: int, n_kv_heads: int, n_seqs: int,
+                 capacity: int, device="cuda", zero: bool = True):
+        cb, sb = kvq_plane_bytes(codec, head_dim, n_kv_heads, n_seqs, capacity)
+        alloc = torch.zeros if zero else torch.empty
+        self.codes = alloc(cb, dtype=torch.uint8, device=device)
+        self.scales = alloc(sb // 2, dtype=torch.int16, device=device)
+        self.codec, self.role, self.head_dim = codec, role, head_dim
+        self.n_kv_heads, self.n_seqs, self.capacity = n_kv_heads, n_seqs, capacity
+
+    def struct(self) -> _Plane:
+        return _Plane(CODECS[self.codec], self.role, self.head_dim, self.n_kv_heads, self.n_seqs,
+                      0, self.capacity, self.codes.data_ptr(), self.scales.data_ptr())
+
+    def clone(self) -> "Plane":
+        p = object.__new__(Plane)
+        p.__dict__.update(self.__dict__)
+        p.codes, p.scales = self.codes.clone(), self.scales.clone()
+        return p
+
+    @property
+    def nbytes(self) -> int:
+        return self.codes.numel() + 2 * self.scales.numel()
+
+
+class Layer:
+    """The K and V planes of one layer (codecs may differ)."""
+
+    def __init__(self, k: Plane, v: Plane):
+        assert k.role == ROLE_K and v.role == ROLE_V
+        self.k, self.v = k, v
+
+    @classmethod
+    def create(cls, k_codec: str, v_codec: str, head_dim: int, n_kv_heads: int, n_seqs: int,
+               capacity: int, device="cuda", zero: bool = True) -> "Layer":
+        return cls(Plane(k_codec, ROLE_K, head_dim, n_kv_heads, n_seqs, capacity, device, zero),
+                   Plane(v_codec, ROLE_V, head_dim, n_kv_heads, n_seqs, capacity, device, zero))
+
+    def struct(self) -> _Layer:
+        return _Layer(self.k.struct(), self.v.struct())
+
+    def clone(self) -> "Layer":
+        return Layer(self.k.clone(), self.v.clone())
+
+    @property
+    def nbytes(self) -> int:
+        return self.k.nbytes + self.v.nbytes
+
+
+def _need(t, name, dtype, shape):
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous() or not t.is_cuda:
+        raise ValueError(f"{name}: expected contiguous device {dtype} {tuple(shape)}, "
+                         f"got {t.dtype} {tuple(t.shape)} on {t.device}")
+
+
+def kvq_append(layer: Layer, k_new, v_new, seq_idx, pos, dev_status=None, stream=None) -> None:
+    """k_new/v_new fp32 [n_tokens][n_kv_heads][head_dim] (either may be None),
+    seq_idx int32 [n_tokens], pos int64 [n_tokens] -- all device tensors."""
+    n = int(seq_idx.numel())
+    _need(seq_idx, "seq_idx", torch.int32, (n,))
+    _need(pos, "pos", torch.int64, (n,))
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        if t is not None:
+            _need(t, name, torch.float32, (n, layer.k.n_kv_heads, layer.k.head_dim))
+    if dev_status is not None:
+        _need(dev_status, "dev_status", torch.int32, (1,))
+    L = layer.struct()
+    _check(load_library().kvq_append(ctypes.byref(L), _ptr(k_new), _ptr(v_new), _ptr(seq_idx),
+                                     _ptr(pos), n, _ptr(dev_status), _stream(stream)))
+
+
+def kvq_decode_workspace_bytes(layer: Layer, n_q_heads: int, n_seqs: int, max_len: int) -> int:
+    L = layer.struct()
+    return int(load_library().kvq_decode_workspace_bytes(ctypes.byref(L), n_q_heads, n_seqs, max_len))
+
+
+def kvq_attend_decode(layer: Layer, q, seq_len, max_len: int, softmax_scale: float, out=None,
+                      workspace=None, stream=None):
+    """q fp32 [n_seqs][n_q_heads][head_dim]; seq_len int64 [n_seqs] (device)."""
+    n_seqs, hq, d = q.shape
+    _need(q, "q", torch.float32, (n_seqs, hq, layer.k.head_dim))
+    _need(seq_len, "seq_len", torch.int64, (n_seqs,))
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", torch.float32, (n_seqs, hq, layer.k.head_dim))
+    if workspace is None:
+        workspace = torch.empty(max(kvq_decode_workspace_bytes(layer, hq, n_seqs, max_len), 256),
+                                dtype=torch.uint8, device=q.device)
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    L = layer.struct()
+    _check(load_library().kvq_attend_decode(ctypes.byref(L), _ptr(q), _ptr(seq_len), n_seqs, hq,
+                                            max_len, softmax_scale, _ptr(out), _ptr(workspace),
+                                            workspace.numel(), _stream(stream)))
+    return out
+
+
+def kvq_prefill_workspace_bytes(layer: Layer, n_q_heads: int, n_tokens: int) -> int:
+    L = layer.struct()
+    return int(load_library().kvq_prefill_workspace_bytes(ctypes.byref(L), n_q_heads, n_tokens))
+
+
+def kvq_attend_prefill(layer: Layer, q_bf16, seq: int, pos0: int, softmax_scale: float, out=None,
+                       workspace=None, stream=None):
+    """q_bf16 bfloat16 [n_tokens][n_q_heads][head_dim] (device); rows of the chunk
+    must already be appended at positions pos0..pos0+n_tokens-1."""
+    T, hq, d = q_bf16.shape
+    _need(q_bf16, "q_bf16", torch.bfloat16, (T, hq, layer.k.head_dim))
+    if out is None:
+        out = torch.empty((T, hq, d), dtype=torch.float32, device=q_bf16.device)
+    _need(out, "out", torch.float32, (T, hq, layer.k.head_dim))
+    ws_bytes = kvq_prefill_workspace_bytes(layer, hq, T)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q_bf16.device)
+    L = layer.struct()
+    _check(load_library().kvq_attend_prefill(ctypes.byref(L), _ptr(q_bf16), seq, pos0, T, hq,
+                                             softmax_scale, _ptr(out), _ptr(workspace),
+                                             0 if workspace is None else workspace.numel(),
+                                             _stream(stream)))
+    return out
+
+
+def kvq_dequant(plane: Plane, seq: int, row0: int, n_rows: int, out=None, stream=None):
+    """-> fp32 [n_kv_heads][n_rows][head_dim] of x_hat = code * scale."""
+    if out is None:
+        out = torch.empty((plane.n_kv_heads, n_rows, plane.head_dim), dtype=torch.float32,
+                          device=plane.codes.device)
+    _need(out, "out", torch.float32, (plane.n_kv_heads, n_rows, plane.head_dim))
+    P = plane.struct()
+    _check(load_library().kvq_dequant(ctypes.byref(P), seq, row0, n_rows, _ptr(out), _stream(stream)))
+    return out

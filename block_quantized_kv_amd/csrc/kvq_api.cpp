@@ -1,0 +1,276 @@
+// kvq_api.cpp -- the C ABI declared in include/kvq.h: argument validation on
+// the host, workspace sizing, and dispatch to the gfx950 kernels.  Nothing here
+// allocates, frees or synchronizes; on any argument error nothing is enqueued.
+#include "kvq.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "kvq_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+kvq_status fail(kvq_status st, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+kvq_status ok() {
+    g_last_error[0] = '\0';
+    return KVQ_OK;
+}
+
+bool codec_valid(int32_t c) { return c == KVQ_Q8_0 || c == KVQ_Q4_0 || c == KVQ_Q4_G64; }
+bool head_dim_valid(int32_t d) { return d == 64 || d == 128 || d == 256; }
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+kvq_status check_plane(const kvq_plane *P, const char *name, int32_t role) {
+    if (!P) return fail(KVQ_EINVAL, "%s: null plane", name);
+    if (!codec_valid(P->codec)) return fail(KVQ_EINVAL, "%s: unknown codec %d", name, P->codec);
+    if (P->role != role)
+        return fail(KVQ_EINVAL, "%s: role %d, expected %d", name, P->role, role);
+    if (!head_dim_valid(P->head_dim))
+        return fail(KVQ_EUNSUPPORTED, "%s: head_dim %d not in {64,128,256}", name, P->head_dim);
+    if (P->head_dim % kvq::group_size(P->codec) != 0)
+        return fail(KVQ_EINVAL, "%s: head_dim %d not a multiple of the group", name, P->head_dim);
+    if (P->n_kv_heads <= 0 || P->n_seqs <= 0)
+        return fail(KVQ_EINVAL, "%s: n_kv_heads=%d n_seqs=%d", name, P->n_kv_heads, P->n_seqs);
+    if (P->capacity <= 0 || P->capacity % KVQ_BLOCK_ROWS != 0)
+        return fail(KVQ_EINVAL, "%s: capacity %lld not a positive multiple of %d", name,
+                    (long long)P->capacity, KVQ_BLOCK_ROWS);
+    if (P->reserved != 0) return fail(KVQ_EINVAL, "%s: reserved field must be 0", name);
+    if (!P->codes || !P->scales) return fail(KVQ_EINVAL, "%s: null codes/scales", name);
+    if (!aligned(P->codes, 256) || !aligned(P->scales, 256))
+        return fail(KVQ_EINVAL, "%s: codes/scales not 256-byte aligned", name);
+    return KVQ_OK;
+}
+
+kvq_status check_layer(const kvq_layer *L) {
+    if (!L) return fail(KVQ_EINVAL, "null layer");
+    kvq_status st = check_plane(&L->k, "k", KVQ_ROLE_K);
+    if (st != KVQ_OK) return st;
+    st = check_plane(&L->v, "v", KVQ_ROLE_V);
+    if (st != KVQ_OK) return st;
+    if (L->k.head_dim != L->v.head_dim || L->k.n_kv_heads != L->v.n_kv_heads ||
+        L->k.n_seqs != L->v.n_seqs || L->k.capacity != L->v.capacity)
+        return fail(KVQ_EINVAL, "k and v planes differ in shape");
+    return KVQ_OK;
+}
+
+kvq::PlaneView view(const kvq_plane &P) {
+    kvq::PlaneView v;
+    v.codes = static_cast<uint8_t *>(P.codes);
+    v.scales = static_cast<uint16_t *>(P.scales);
+    v.codec = P.codec;
+    v.head_dim = P.head_dim;
+    v.n_kv_heads = P.n_kv_heads;
+    v.n_seqs = P.n_seqs;
+    v.capacity = P.capacity;
+    const int64_t blocks = P.capacity / KVQ_BLOCK_ROWS;
+    v.head_code_stride = blocks * kvq::block_code_bytes(P.codec, P.head_dim);
+    v.head_scale_stride = blocks * kvq::block_scales(P.codec, P.head_dim);
+    return v;
+}
+
+kvq_status hip_status(hipError_t e, const char *what) {
+    if (e == hipSuccess) return ok();
+    return fail(KVQ_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kvq_row_code_bytes(int32_t codec, int32_t head_dim) {
+    if (!codec_valid(codec) || head_dim <= 0 || head_dim % kvq::group_size(codec) != 0) return 0;
+    return (size_t)kvq::row_bytes(codec, head_dim);
+}
+
+kvq_status kvq_plane_bytes(int32_t codec, int32_t head_dim, int32_t n_kv_heads, int32_t n_seqs,
+                           int64_t capacity, size_t *codes_bytes, size_t *scales_bytes) {
+    if (!codes_bytes || !scales_bytes) return fail(KVQ_EINVAL, "null output pointer");
+    if (!codec_valid(codec)) return fail(KVQ_EINVAL, "unknown codec %d", codec);
+    if (!head_dim_valid(head_dim))
+        return fail(KVQ_EUNSUPPORTED, "head_dim %d not in {64,128,256}", head_dim);
+    if (n_kv_heads <= 0 || n_seqs <= 0 || capacity <= 0 || capacity % KVQ_BLOCK_ROWS != 0)
+        return fail(KVQ_EINVAL, "bad plane shape");
+    const size_t rows = (size_t)n_kv_heads * (size_t)n_seqs * (size_t)capacity;
+    *codes_bytes = rows * (size_t)kvq::row_bytes(codec, head_dim);
+    *scales_bytes = rows * (size_t)kvq::n_groups(codec, head_dim) * 2;
+    return ok();
+}
+
+kvq_status kvq_append(const kvq_layer *L, const float *k_new, const float *v_new,
+                      const int32_t *seq_idx, const int64_t *pos, int32_t n_tokens,
+                      int32_t *dev_status, void *hip_stream) {
+    kvq_status st = check_layer(L);
+    if (st != KVQ_OK) return st;
+    if (n_tokens < 0) return fail(KVQ_EINVAL, "n_tokens %d < 0", n_tokens);
+    if (!k_new && !v_new) return fail(KVQ_EINVAL, "both k_new and v_new are null");
+    if (n_tokens > 0 && (!seq_idx || !pos)) return fail(KVQ_EINVAL, "null seq_idx/pos");
+    if ((k_new && !aligned(k_new, 16)) || (v_new && !aligned(v_new, 16)))
+        return fail(KVQ_EINVAL, "k_new/v_new not 16-byte aligned");
+    if (n_tokens == 0) return ok();
+    hipStream_t s = static_cast<hipStream_t>(hip_stream);
+    for (int r = 0; r < 2; ++r) {
+        const float *x = r == 0 ? k_new : v_new;
+        if (!x) continue;
+        kvq::AppendArgs a;
+        a.plane = view(r == 0 ? L->k : L->v);
+        a.role = r == 0 ? kvq::ROLE_K : kvq::ROLE_V;
+        a.x = x;
+        a.seq_idx = seq_idx;
+        a.pos = pos;
+        a.n_tokens = n_tokens;
+        a.dev_status = dev_status;
+        hipError_t e = kvq::launch_append(a, s);
+        if (e != hipSuccess) return hip_status(e, "append launch");
+    }
+    return ok();
+}
+
+size_t kvq_decode_workspace_bytes(const kvq_layer *L, int32_t n_q_heads, int32_t n_seqs,
+                                  int64_t max_len) {
+    if (!L || n_q_heads <= 0 || n_seqs <= 0 || max_len < 0) return 0;
+    const kvq::DecodePlan p =
+        kvq::plan_decode(L->k.head_dim, L->k.n_kv_heads, n_q_heads, n_seqs, max_len);
+    return ((p.part_o_bytes + 255) / 256) * 256 + p.part_ml_bytes;
+}
+
+kvq_status kvq_attend_decode(const kvq_layer *L, const float *q, const int64_t *seq_len,
+                             int32_t n_seqs, int32_t n_q_heads, int64_t max_len,
+                             float softmax_scale, float *out, void *workspace, size_t ws_bytes,
+                             void *hip_stream) {
+    kvq_status st = check_layer(L);
+    if (st != KVQ_OK) return st;
+    if (!q || !seq_len || !out) return fail(KVQ_EINVAL, "null q/seq_len/out");
+    if (!aligned(q, 16) || !aligned(out, 16)) return fail(KVQ_EINVAL, "q/out not 16-byte aligned");
+    if (n_seqs <= 0 || n_seqs > L->k.n_seqs)
+        return fail(KVQ_EINVAL, "n_seqs %d outside [1, %d]", n_seqs, L->k.n_seqs);
+    if (n_q_heads <= 0 || n_q_heads % L->k.n_kv_heads != 0)
+        return fail(KVQ_EINVAL, "n_q_heads %d not a multiple of n_kv_heads %d", n_q_heads,
+                    L->k.n_kv_heads);
+    const int gqa = n_q_heads / L->k.n_kv_heads;
+    if (gqa > KVQ_MAX_GQA)
+        return fail(KVQ_EUNSUPPORTED, "%d q-heads per kv-head exceeds %d", gqa, KVQ_MAX_GQA);
+    if (max_len < 0 || max_len > L->k.capacity)
+        return fail(KVQ_ERANGE, "max_len %lld outside [0, capacity %lld]", (long long)max_len,
+                    (long long)L->k.capacity);
+    if (!(softmax_scale == softmax_scale)) return fail(KVQ_EINVAL, "softmax_scale is NaN");
+    if (!kvq::decode_supported(L->k.codec, L->v.codec, L->k.head_dim))
+        return fail(KVQ_EUNSUPPORTED, "no decode kernel for this codec pair/head_dim");
+    const size_t need = kvq_decode_workspace_bytes(L, n_q_heads, n_seqs, max_len);
+    if (!workspace || ws_bytes < need)
+        return fail(KVQ_EWORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
+    if (!aligned(workspace, 256)) return fail(KVQ_EINVAL, "workspace not 256-byte aligned");
+
+    const kvq::DecodePlan p =
+        kvq::plan_decode(L->k.head_dim, L->k.n_kv_heads, n_q_heads, n_seqs, max_len);
+    kvq::DecodeArgs a;
+    a.k = view(L->k);
+    a.v = view(L->v);
+    a.q = q;
+    a.seq_len = seq_len;
+    a.out = out;
+    a.part_o = static_cast<float *>(workspace);
+    a.part_ml = reinterpret_cast<float *>(static_cast<char *>(workspace) +
+                                          ((p.part_o_bytes + 255) / 256) * 256);
+    a.n_seqs = n_seqs;
+    a.n_q_heads = n_q_heads;
+    a.gqa = gqa;
+    a.max_len = max_len;
+    a.split_rows = p.split_rows;
+    a.max_splits = p.max_splits;
+    a.scale_log2 = softmax_scale * 1.4426950408889634f;
+    return hip_status(kvq::launch_decode(a, static_cast<hipStream_t>(hip_stream)), "decode launch");
+}
+
+size_t kvq_prefill_workspace_bytes(const kvq_layer *L, int32_t n_q_heads, int32_t n_tokens) {
+    (void)L;
+    (void)n_q_heads;
+    (void)n_tokens;
+    return 0;
+}
+
+kvq_status kvq_attend_prefill(const kvq_layer *L, const uint16_t *q_bf16, int32_t seq, int64_t pos0,
+                              int32_t n_tokens, int32_t n_q_heads, float softmax_scale, float *out,
+                              void *workspace, size_t ws_bytes, void *hip_stream) {
+    (void)workspace;
+    (void)ws_bytes;
+    kvq_status st = check_layer(L);
+    if (st != KVQ_OK) return st;
+    if (!q_bf16 || !out) return fail(KVQ_EINVAL, "null q/out");
+    if (!aligned(q_bf16, 16) || !aligned(out, 16)) return fail(KVQ_EINVAL, "q/out not 16-byte aligned");
+    if (seq < 0 || seq >= L->k.n_seqs) return fail(KVQ_EINVAL, "seq %d out of range", seq);
+    if (n_tokens < 0) return fail(KVQ_EINVAL, "n_tokens %d < 0", n_tokens);
+    if (pos0 < 0 || pos0 + n_tokens > L->k.capacity)
+        return fail(KVQ_ERANGE, "chunk [%lld, %lld) outside capacity %lld", (long long)pos0,
+                    (long long)(pos0 + n_tokens), (long long)L->k.capacity);
+    if (n_q_heads <= 0 || n_q_heads % L->k.n_kv_heads != 0)
+        return fail(KVQ_EINVAL, "n_q_heads %d not a multiple of n_kv_heads %d", n_q_heads,
+                    L->k.n_kv_heads);
+    const int gqa = n_q_heads / L->k.n_kv_heads;
+    if (!(softmax_scale == softmax_scale)) return fail(KVQ_EINVAL, "softmax_scale is NaN");
+    if (!kvq::prefill_supported(L->k.codec, L->v.codec, L->k.head_dim))
+        return fail(KVQ_EUNSUPPORTED, "no prefill kernel for this codec pair/head_dim");
+    if (n_tokens == 0) return ok();
+    kvq::PrefillArgs a;
+    a.k = view(L->k);
+    a.v = view(L->v);
+    a.q = q_bf16;
+    a.out = out;
+    a.seq = seq;
+    a.pos0 = pos0;
+    a.n_tokens = n_tokens;
+    a.n_q_heads = n_q_heads;
+    a.gqa = gqa;
+    a.scale_log2 = softmax_scale * 1.4426950408889634f;
+    return hip_status(kvq::launch_prefill(a, static_cast<hipStream_t>(hip_stream)),
+                      "prefill launch");
+}
+
+kvq_status kvq_dequant(const kvq_plane *P, int32_t seq, int64_t row0, int64_t n_rows, float *out,
+                       void *hip_stream) {
+    if (!P) return fail(KVQ_EINVAL, "null plane");
+    kvq_status st = check_plane(P, "plane", P->role == KVQ_ROLE_V ? KVQ_ROLE_V : KVQ_ROLE_K);
+    if (st != KVQ_OK) return st;
+    if (!out || !aligned(out, 16)) return fail(KVQ_EINVAL, "out null or not 16-byte aligned");
+    if (seq < 0 || seq >= P->n_seqs) return fail(KVQ_EINVAL, "seq %d out of range", seq);
+    if (row0 < 0 || n_rows < 0 || row0 + n_rows > P->capacity)
+        return fail(KVQ_ERANGE, "rows [%lld, %lld) outside capacity %lld", (long long)row0,
+                    (long long)(row0 + n_rows), (long long)P->capacity);
+    if (n_rows == 0) return ok();
+    kvq::DequantArgs a;
+    a.plane = view(*P);
+    a.role = P->role;
+    a.seq = seq;
+    a.row0 = row0;
+    a.n_rows = n_rows;
+    a.out = out;
+    return hip_status(kvq::launch_dequant(a, static_cast<hipStream_t>(hip_stream)),
+                      "dequant launch");
+}
+
+const char *kvq_status_str(int32_t status) {
+    switch (status) {
+        case KVQ_OK: return "KVQ_OK";
+        case KVQ_EINVAL: return "KVQ_EINVAL: invalid argument";
+        case KVQ_EUNSUPPORTED: return "KVQ_EUNSUPPORTED: unsupported combination (no fallback)";
+        case KVQ_ERANGE: return "KVQ_ERANGE: position or length outside the capacity";
+        case KVQ_EWORKSPACE: return "KVQ_EWORKSPACE: workspace missing or too small";
+        case KVQ_EHIP: return "KVQ_EHIP: HIP runtime error";
+        default: return "unknown kvq_status";
+    }
+}
+
+const char *kvq_last_error(void) { return g_last_error; }
+
+}  // extern "C"

@@ -1,0 +1,121 @@
+// kvq_device.h -- device helpers shared by the gfx950 kernels: vector types,
+// code unpacking into binary16 matrix-core operands, cross-lane reductions.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvq_layout.h"
+
+namespace kvq {
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ h2 as_h2(uint32_t w) { return __builtin_bit_cast(h2, w); }
+__device__ __forceinline__ uint32_t as_u32(h2 v) { return __builtin_bit_cast(uint32_t, v); }
+
+__device__ __forceinline__ f4 mfma16x16x32(h8 a, h8 b, f4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f4 mfma16x16x32_bf16(bf8 a, bf8 b, f4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// ---- 4-bit codes -------------------------------------------------------------
+// A word holds 8 nibbles in slot order (nibble positions 0,4,1,5,2,6,3,7 for
+// slots 0..7).  With the binary16 pattern 0x6400 (= 1024.0, unit fraction step)
+// or-ed in, the nibble n in the low 4 fraction bits reads as 1024 + n and a
+// nibble in fraction bits 4..7 reads as 1024 + 16 n; both are exact.
+// Result: slots (0,1) = 1024+n, (2,3) = 1024+16n, (4,5) = 1024+n, (6,7) = 1024+16n.
+__device__ __forceinline__ u4 nib_magic(uint32_t w) {
+    const uint32_t w8 = w >> 8;
+    u4 r;
+    r.x = (w & 0x000F000Fu) | 0x64006400u;
+    r.y = (w & 0x00F000F0u) | 0x64006400u;
+    r.z = (w8 & 0x000F000Fu) | 0x64006400u;
+    r.w = (w8 & 0x00F000F0u) | 0x64006400u;
+    return r;
+}
+
+// Offset-8 nibble n of a 4-bit word.  q4_0 stores q + 8 already; Q4_G64 stores
+// q & 0xF (two's complement), and q + 8 = (q & 0xF) ^ 8.
+template <int CODEC>
+__device__ __forceinline__ uint32_t to_offset8(uint32_t w) {
+    return CODEC == Q4_G64 ? (w ^ 0x88888888u) : w;
+}
+
+// ---- 8-bit codes -------------------------------------------------------------
+// Byte b (two's complement) becomes binary16 1152 + b = 0x6400 | (b ^ 0x80).
+__device__ __forceinline__ u2 byte_magic(uint32_t w) {
+    const uint32_t x = w ^ 0x80808080u;
+    u2 r;
+    r.x = __builtin_amdgcn_perm(0x64646464u, x, 0x04010400u);  // bytes b0, b1
+    r.y = __builtin_amdgcn_perm(0x64646464u, x, 0x04030402u);  // bytes b2, b3
+    return r;
+}
+
+// K operand (A of S^T = K Q^T) for one k-step: 8 binary16 values that equal the
+// code plus a known per-slot bias (removed through the accumulator init).
+template <int CODEC>
+__device__ __forceinline__ h8 k_operand(const uint32_t *w) {
+    if constexpr (is8(CODEC)) {
+        const u2 a = byte_magic(w[0]), b = byte_magic(w[1]);
+        const u4 r = {a.x, a.y, b.x, b.y};
+        return __builtin_bit_cast(h8, r);
+    } else {
+        return __builtin_bit_cast(h8, nib_magic(to_offset8<CODEC>(w[0])));
+    }
+}
+
+// Bias of slot s in k_operand for code 0, and the factor the query must carry
+// in that slot so that slot * factor = (code + bias) * query.
+template <int CODEC>
+__device__ __forceinline__ constexpr float k_slot_bias(int s) {
+    return is8(CODEC) ? 1152.0f : (((s >> 1) & 1) ? 1152.0f : 1032.0f);
+}
+template <int CODEC>
+__device__ __forceinline__ constexpr float k_slot_factor(int s) {
+    return is8(CODEC) ? 1.0f : (((s >> 1) & 1) ? 0.0625f : 1.0f);
+}
+
+// V operand (A of O^T = V^T P^T) for one 16-channel block: binary16 of
+// code * dq (rounded to nearest even once; exact for subnormal scales), for the
+// eight slot rows.  dq2[m] holds the scales of slots (2m, 2m+1).
+template <int CODEC>
+__device__ __forceinline__ h8 v_operand(const uint32_t *w, const h2 *dq2) {
+    h2 v0, v1, v2, v3;
+    if constexpr (is8(CODEC)) {
+        const u2 a = byte_magic(w[0]), b = byte_magic(w[1]);
+        const h2 bias = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+        v0 = (as_h2(a.x) + bias) * dq2[0];
+        v1 = (as_h2(a.y) + bias) * dq2[1];
+        v2 = (as_h2(b.x) + bias) * dq2[2];
+        v3 = (as_h2(b.y) + bias) * dq2[3];
+    } else {
+        const u4 r = nib_magic(to_offset8<CODEC>(w[0]));
+        const h2 b_lo = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+        const h2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+        const h2 b_hi = {(_Float16)-72.0f, (_Float16)-72.0f};
+        v0 = (as_h2(r.x) + b_lo) * dq2[0];
+        v1 = (as_h2(r.y) * sixteenth + b_hi) * dq2[1];
+        v2 = (as_h2(r.z) + b_lo) * dq2[2];
+        v3 = (as_h2(r.w) * sixteenth + b_hi) * dq2[3];
+    }
+    h8 out;
+    out.s01 = v0;
+    out.s23 = v1;
+    out.s45 = v2;
+    out.s67 = v3;
+    return out;
+}
+
+// ---- cross-lane ----------------------------------------------------------------
+__device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace kvq

@@ -1,0 +1,90 @@
+// kvq_internal.h -- launcher interface between the C ABI (kvq_api.cpp) and the
+// HIP kernels.  All arguments are validated by the caller before a launcher
+// runs; launchers only enqueue work and return the HIP status.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvq_layout.h"
+
+namespace kvq {
+
+// Device view of one plane for one sequence-major layout.
+struct PlaneView {
+    uint8_t *codes;
+    uint16_t *scales;
+    int codec;
+    int head_dim;
+    int n_kv_heads;
+    int n_seqs;
+    int64_t capacity;
+    int64_t head_code_stride;   // bytes per (seq, head)   = capacity/32 * block_code_bytes
+    int64_t head_scale_stride;  // binary16 per (seq, head) = capacity/32 * block_scales
+};
+
+struct AppendArgs {
+    PlaneView plane;
+    int role;
+    const float *x;          // [n_tokens][n_kv_heads][head_dim]
+    const int32_t *seq_idx;  // [n_tokens]
+    const int64_t *pos;      // [n_tokens]
+    int n_tokens;
+    int32_t *dev_status;     // nullable
+};
+
+struct DequantArgs {
+    PlaneView plane;
+    int role;
+    int seq;
+    int64_t row0;
+    int64_t n_rows;
+    float *out;  // [n_kv_heads][n_rows][head_dim]
+};
+
+struct DecodeArgs {
+    PlaneView k, v;
+    const float *q;          // [n_seqs][Hq][D]
+    const int64_t *seq_len;  // [n_seqs]
+    float *out;              // [n_seqs][Hq][D]
+    float *part_o;           // [n_seqs][Hq][max_splits][D]
+    float *part_ml;          // [n_seqs][Hq][max_splits][2]  (max in log2 units, sum)
+    int n_seqs;
+    int n_q_heads;
+    int gqa;                 // q-heads per kv-head
+    int64_t max_len;
+    int split_rows;          // multiple of 256
+    int max_splits;
+    float scale_log2;        // softmax_scale * log2(e)
+};
+
+struct PrefillArgs {
+    PlaneView k, v;
+    const uint16_t *q;       // [T][Hq][D] bf16 bits
+    float *out;              // [T][Hq][D]
+    int seq;
+    int64_t pos0;
+    int n_tokens;
+    int n_q_heads;
+    int gqa;
+    float scale_log2;
+};
+
+// Decode split size (rows per workgroup) and split count for a call.
+struct DecodePlan {
+    int split_rows;
+    int max_splits;
+    size_t part_o_bytes;
+    size_t part_ml_bytes;
+};
+DecodePlan plan_decode(int head_dim, int n_kv_heads, int n_q_heads, int n_seqs, int64_t max_len);
+
+hipError_t launch_append(const AppendArgs &a, hipStream_t s);
+hipError_t launch_dequant(const DequantArgs &a, hipStream_t s);
+// Returns hipErrorInvalidValue when no kernel instance exists for the codec
+// pair / head_dim (the API maps that to KVQ_EUNSUPPORTED before calling).
+bool decode_supported(int k_codec, int v_codec, int head_dim);
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
+bool prefill_supported(int k_codec, int v_codec, int head_dim);
+hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s);
+
+}  // namespace kvq

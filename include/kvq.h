@@ -1,0 +1,195 @@
+/*
+ * kvq.h -- C ABI of libkvq: attention over a block-quantized KV cache on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes (sources are web pages, cited by title/section):
+ *   - den_llama.cpp, "What this fork is": the Q4_G64 KV codec (signed INT4 plus
+ *     one FP16 scale per 64 values, 4.25 bits/value) with a quantizer that is
+ *     byte-identical, and a dequantizer bit-identical, to a CPU reference;
+ *     layer-wise split KV precision (some layers keep a wider codec).
+ *   - den_llama.cpp, "Results": FlashAttention reading a q8_0 K / q4_0 V cache
+ *     directly instead of falling back to f16 ("FA silently falls back" is
+ *     presented as the defect to avoid: this library never falls back).
+ *   - den_llama.cpp, "What's in the fork": quantize-on-write of new K/V rows
+ *     (set-rows / cpy), dequant (convert), FlashAttention over quantized K/V.
+ *   - Llaminar, "Graphs and Compute Stages": KV-cache append is a stage that
+ *     precedes attention; "GPU Graph Capture": KV counters stay device-owned
+ *     during captured execution; "Activation precision": FP32 activations.
+ *
+ * Codecs (groups of G consecutive channels of one row, one binary16 scale d16
+ * per group, dq = (float)d16; codes q_i = clamp(rint(x_i / dq), -Qmax-1, Qmax)
+ * with d = amax/Qmax rounded to binary16 nearest-even, saturated at 65504):
+ *   KVQ_Q8_0   : G = 32, Qmax = 127, 8-bit two's complement codes  (8.5 b/value)
+ *   KVQ_Q4_0   : G = 32, Qmax = 7,   4-bit codes stored as q + 8   (4.5 b/value)
+ *   KVQ_Q4_G64 : G = 64, Qmax = 7,   4-bit two's complement codes  (4.25 b/value)
+ * Dequantized value: x_hat_i = q_i * dq (exact in binary32).
+ *
+ * Memory model.  Every pointer argument is a device pointer unless stated;
+ * the caller owns all memory (the library never allocates, frees or
+ * synchronizes).  Every call only enqueues work on the given HIP stream
+ * (NULL = the legacy default stream) and is therefore capturable in a HIP
+ * graph.  Argument errors are detected on the host before anything is
+ * enqueued; then the call returns a non-zero kvq_status, enqueues nothing and
+ * records a message retrievable with kvq_last_error() (thread-local).
+ * An unsupported (codec, head_dim, group) combination returns
+ * KVQ_EUNSUPPORTED: there is no fallback path.  A failed kernel launch returns
+ * KVQ_EHIP.
+ *
+ * Cache layout (one "plane" = the K or the V cache of one layer).  Rows are
+ * grouped in blocks of KVQ_BLOCK_ROWS = 32 consecutive positions of one
+ * (sequence, kv-head):
+ *   codes  : [n_seqs][n_kv_heads][capacity/32][32 * row_code_bytes]  bytes
+ *   scales : [n_seqs][n_kv_heads][capacity/32][32 * head_dim/G]      binary16
+ * Inside a block the codes and scales are permuted into the order in which
+ * the matrix-core kernels consume them; the permutation depends on the plane's
+ * role (KVQ_ROLE_K or KVQ_ROLE_V) and is a pure reordering: the code of row r,
+ * channel c is stored exactly once, with the value and bit width the codec
+ * defines.  kvq_dequant() returns rows in plain [head][row][channel] order.
+ * Both base pointers must be 256-byte aligned.  Rows that were never appended
+ * hold whatever the memory held (zero-fill the planes if that matters).
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVQ_BLOCK_ROWS 32
+#define KVQ_MAX_GQA 16 /* q-heads per kv-head supported by the attention kernels */
+
+typedef enum { KVQ_Q8_0 = 0, KVQ_Q4_0 = 1, KVQ_Q4_G64 = 2 } kvq_codec;
+
+typedef enum { KVQ_ROLE_K = 0, KVQ_ROLE_V = 1 } kvq_role;
+
+typedef enum {
+    KVQ_OK = 0,
+    KVQ_EINVAL = 1,       /* bad argument (null pointer, bad size, misalignment, ...) */
+    KVQ_EUNSUPPORTED = 2, /* valid but unsupported combination (no fallback exists)   */
+    KVQ_ERANGE = 3,       /* a position/length outside the plane's capacity           */
+    KVQ_EWORKSPACE = 4,   /* workspace missing or smaller than required               */
+    KVQ_EHIP = 5          /* the HIP runtime reported an error                        */
+} kvq_status;
+
+/* One K or V cache plane of one layer.  head_dim must be 64, 128 or 256 and a
+ * multiple of the codec's group size; capacity a positive multiple of 32. */
+typedef struct {
+    int32_t codec;      /* kvq_codec                                         */
+    int32_t role;       /* kvq_role: selects the in-block permutation        */
+    int32_t head_dim;
+    int32_t n_kv_heads;
+    int32_t n_seqs;
+    int32_t reserved;   /* must be 0                                         */
+    int64_t capacity;   /* rows per (sequence, kv-head)                      */
+    void *codes;        /* device, 256-B aligned, kvq_plane_bytes() bytes    */
+    void *scales;       /* device, 256-B aligned, binary16 bit patterns      */
+} kvq_plane;
+
+/* The K and V planes of one layer.  Codecs may differ between k and v (and
+ * between layers); head_dim, n_kv_heads, n_seqs and capacity must match;
+ * k.role must be KVQ_ROLE_K and v.role KVQ_ROLE_V. */
+typedef struct {
+    kvq_plane k;
+    kvq_plane v;
+} kvq_layer;
+
+/* ---- sizing (host only, never touches the GPU) ------------------------- */
+
+/* Code bytes per row: head_dim (8-bit codec) or head_dim/2 (4-bit codecs);
+ * 0 for an invalid codec/head_dim. */
+size_t kvq_row_code_bytes(int32_t codec, int32_t head_dim);
+
+/* Bytes of the codes and scales buffers of a plane of the given shape
+ * (codes = rows * row_code_bytes, scales = rows * head_dim/G * 2 with
+ * rows = n_seqs * n_kv_heads * capacity).  For Q4_G64 the two add up to
+ * exactly 4.25 bits per cached value. */
+kvq_status kvq_plane_bytes(int32_t codec, int32_t head_dim, int32_t n_kv_heads, int32_t n_seqs,
+                           int64_t capacity, size_t *codes_bytes, size_t *scales_bytes);
+
+/* ---- append: quantize new rows into the cache (den_llama.cpp, "What's in the
+ * fork": quantize-on-write; Llaminar, "Graphs and Compute Stages": append
+ * precedes attention) ----------------------------------------------------- */
+
+/* Quantizes n_tokens new rows per kv-head into L->k and L->v.
+ *   k_new, v_new : fp32 [n_tokens][n_kv_heads][head_dim], device; either may
+ *                  be NULL to leave that plane untouched (not both).
+ *   seq_idx      : int32 [n_tokens], device: the sequence of each token.
+ *   pos          : int64 [n_tokens], device: the row (position) of each token.
+ *   dev_status   : optional int32, device: if any token has seq_idx outside
+ *                  [0, n_seqs) or pos outside [0, capacity) that token is
+ *                  skipped and KVQ_ERANGE is stored here (nothing is stored
+ *                  otherwise; the caller initializes it).
+ * Tokens of one call must target distinct (sequence, position) pairs.
+ * Inputs must be finite.  Codes and scales equal the CPU reference bit for
+ * bit (den_llama.cpp, "Results": quantizer byte-identical to the CPU ref). */
+kvq_status kvq_append(const kvq_layer *L, const float *k_new, const float *v_new,
+                      const int32_t *seq_idx, const int64_t *pos, int32_t n_tokens,
+                      int32_t *dev_status, void *hip_stream);
+
+/* ---- decode attention (den_llama.cpp, "Results" / "What's in the fork":
+ * FlashAttention reading the quantized K/V blocks directly) -------------- */
+
+/* Workspace bytes kvq_attend_decode needs for these sizes (host only). */
+size_t kvq_decode_workspace_bytes(const kvq_layer *L, int32_t n_q_heads, int32_t n_seqs,
+                                  int64_t max_len);
+
+/* One query per sequence attends rows [0, len_b) of its own cache, with
+ * len_b = min(seq_len[b], max_len):
+ *   out[b][h] = sum_j softmax_j(softmax_scale * q[b][h] . k_hat[b][g][j]) v_hat[b][g][j]
+ * with g = h / (n_q_heads / n_kv_heads) (consecutive q-heads share a kv-head).
+ *   q        : fp32 [n_seqs][n_q_heads][head_dim], device
+ *   seq_len  : int64 [n_seqs], device (lengths stay device-owned)
+ *   max_len  : host upper bound of the lengths, sizes the grid; <= capacity
+ *   out      : fp32 [n_seqs][n_q_heads][head_dim], device; zeros for len_b = 0
+ *   workspace: device scratch of at least kvq_decode_workspace_bytes() bytes,
+ *              256-B aligned; its contents are not preserved across calls
+ * n_seqs may be smaller than the planes' n_seqs (sequences 0..n_seqs-1).
+ * n_q_heads / n_kv_heads must be an integer in [1, KVQ_MAX_GQA].
+ * Precision: fp32 statistics and accumulation; the matrix-core operands are
+ * binary16 (query as a hi+lo pair, probabilities and dequantized V rounded to
+ * nearest-even).  |v_hat| must stay below 65504. */
+kvq_status kvq_attend_decode(const kvq_layer *L, const float *q, const int64_t *seq_len,
+                             int32_t n_seqs, int32_t n_q_heads, int64_t max_len,
+                             float softmax_scale, float *out, void *workspace, size_t ws_bytes,
+                             void *hip_stream);
+
+/* ---- chunked-prefill attention (den_llama.cpp, "Results": prefill with the
+ * quantized cache and 2048-token micro-batches; Llaminar, "GPU Graph
+ * Capture": prefill runs in chunks) --------------------------------------- */
+
+/* Workspace bytes kvq_attend_prefill needs (host only). */
+size_t kvq_prefill_workspace_bytes(const kvq_layer *L, int32_t n_q_heads, int32_t n_tokens);
+
+/* A chunk of n_tokens queries of sequence `seq` at absolute positions
+ * pos0 .. pos0+n_tokens-1, whose K/V rows were already appended; token t
+ * attends rows [0, pos0 + t] (causal, itself included).
+ *   q_bf16 : bfloat16 bit patterns [n_tokens][n_q_heads][head_dim], device
+ *   out    : fp32 [n_tokens][n_q_heads][head_dim], device
+ * The dequantized K and V tiles are rounded to bfloat16 for the bf16 matrix
+ * cores, as are the probabilities; accumulation and softmax are fp32. */
+kvq_status kvq_attend_prefill(const kvq_layer *L, const uint16_t *q_bf16, int32_t seq, int64_t pos0,
+                              int32_t n_tokens, int32_t n_q_heads, float softmax_scale, float *out,
+                              void *workspace, size_t ws_bytes, void *hip_stream);
+
+/* ---- dequant (den_llama.cpp, "What's in the fork": convert; "Results":
+ * dequant bit-identical to the CPU reference) ----------------------------- */
+
+/* Writes x_hat = q * dq for rows [row0, row0 + n_rows) of sequence `seq`:
+ *   out : fp32 [n_kv_heads][n_rows][head_dim], device. */
+kvq_status kvq_dequant(const kvq_plane *P, int32_t seq, int64_t row0, int64_t n_rows, float *out,
+                       void *hip_stream);
+
+/* ---- diagnostics --------------------------------------------------------- */
+
+const char *kvq_status_str(int32_t status);
+/* Message of the last failing call on this thread ("" if none). */
+const char *kvq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

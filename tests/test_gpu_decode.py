@@ -1,0 +1,176 @@
+"""GPU decode-attention parity against the oracle (binary64 attention over the
+oracle's own quantization of the same fp32 rows).
+
+Bar: max|gpu - oracle| / max|oracle| <= 1e-3 over the outputs of one call
+(per layer), the decode tolerance of the workload statement.  Covered: all
+9 codec pairs, head_dim 64/128/256, GQA 1..16, lengths 0, 1, ragged tails and
+several tiles, split-count sweeps, softmax invariants, and the five workload
+configurations at full size (sampled q-heads where the oracle would be slow).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from block_quantized_kv_amd import Layer, kvq_attend_decode
+from gpu_helpers import append_rows, rel_err
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-3
+CODECS = ["q8_0", "q4_0", "q4_g64"]
+
+
+def _oracle_decode(kc, vc, q, k_rows, v_rows, length, scale, heads=None):
+    """q [Hq][d] np; k_rows/v_rows np [n][H][d] fp32 -> oracle output."""
+    kh = oracle.quant_dequant(kc, np.ascontiguousarray(k_rows.transpose(1, 0, 2)))
+    vh = oracle.quant_dequant(vc, np.ascontiguousarray(v_rows.transpose(1, 0, 2)))
+    return oracle.attend_decode(q, kh, vh, length, scale, heads=heads)
+
+
+def _run_case(gpu, kc, vc, d, hq, hkv, lens, cap=None, seed=0, max_len=None, kv_scale=1.0):
+    rng = np.random.default_rng(seed)
+    S = len(lens)
+    cap = cap or max(32, (max(lens) + 31) // 32 * 32)
+    layer = Layer.create(kc, vc, d, hkv, S, cap, device=gpu)
+    q = rng.standard_normal((S, hq, d)).astype(np.float32)
+    ks, vs = [], []
+    for s, n in enumerate(lens):
+        k = (rng.standard_normal((cap, hkv, d)) * kv_scale).astype(np.float32)
+        v = (rng.standard_normal((cap, hkv, d)) * kv_scale).astype(np.float32)
+        append_rows(layer, torch.from_numpy(k).to(gpu), torch.from_numpy(v).to(gpu), s, 0)
+        ks.append(k)
+        vs.append(v)
+    scale = 1.0 / np.sqrt(d)
+    ml = max_len if max_len is not None else max(max(lens), 0)
+    out = kvq_attend_decode(layer, torch.from_numpy(q).to(gpu),
+                            torch.tensor(lens, dtype=torch.int64, device=gpu), ml, scale)
+    out = out.cpu().numpy()
+    for s, n in enumerate(lens):
+        if n == 0:
+            assert np.array_equal(out[s], np.zeros_like(out[s]))
+            continue
+        ref = _oracle_decode(kc, vc, q[s], ks[s], vs[s], n, scale)
+        err = rel_err(out[s], ref)
+        assert err <= TOL, (kc, vc, d, hq, hkv, n, err)
+    return out
+
+
+@pytest.mark.parametrize("kc", CODECS)
+@pytest.mark.parametrize("vc", CODECS)
+def test_codec_pairs_small(gpu, kc, vc):
+    d = {"q8_0": 128, "q4_0": 64, "q4_g64": 256}[kc]
+    _run_case(gpu, kc, vc, d, hq=8, hkv=2, lens=[1000, 33], seed=CODECS.index(kc) * 3 + CODECS.index(vc))
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("gqa", [1, 4, 6, 16])
+def test_head_dims_and_gqa(gpu, d, gqa):
+    _run_case(gpu, "q4_g64", "q4_0", d, hq=2 * gqa, hkv=2, lens=[257], seed=d + gqa)
+
+
+@pytest.mark.parametrize("lens", [[1], [31, 32, 33], [0, 5, 64], [4097], [300, 0]])
+def test_lengths_and_empty(gpu, lens):
+    _run_case(gpu, "q8_0", "q4_g64", 128, hq=4, hkv=1, lens=lens, seed=sum(lens))
+
+
+@pytest.mark.parametrize("max_len_factor", [1, 2, 8])
+def test_split_sweep(gpu, max_len_factor):
+    # max_len changes the split size and count; the result must not
+    n = 3000
+    _run_case(gpu, "q4_0", "q8_0", 128, hq=8, hkv=2, lens=[n], cap=n * 8 + 32,
+              max_len=n * max_len_factor, seed=11)
+
+
+def test_large_and_small_magnitudes(gpu):
+    _run_case(gpu, "q8_0", "q4_g64", 64, hq=4, hkv=1, lens=[500], kv_scale=1e-5, seed=3)
+    _run_case(gpu, "q8_0", "q4_g64", 64, hq=4, hkv=1, lens=[500], kv_scale=300.0, seed=4)
+
+
+def test_invariants_constant_v_and_single_row(gpu):
+    d, H, n = 128, 1, 700
+    layer = Layer.create("q4_g64", "q8_0", d, H, 1, 704, device=gpu)
+    rng = np.random.default_rng(9)
+    k = rng.standard_normal((n, H, d)).astype(np.float32)
+    row = np.round(rng.standard_normal(d) * 4).astype(np.float32)  # exactly representable codes
+    row[0] = 127.0
+    v = np.broadcast_to(row, (n, H, d)).copy()
+    append_rows(layer, torch.from_numpy(k).to(gpu), torch.from_numpy(v).to(gpu), 0, 0)
+    q = torch.randn(1, 4, d, device=gpu)
+    v_hat = oracle.quant_dequant("q8_0", row[None])[0]   # what the cache holds
+    out = kvq_attend_decode(layer, q, torch.tensor([n], device=gpu), n, 0.125).cpu().numpy()
+    assert rel_err(out[0], np.broadcast_to(v_hat, (4, d))) <= TOL
+    out1 = kvq_attend_decode(layer, q, torch.tensor([1], device=gpu), n, 0.125).cpu().numpy()
+    assert rel_err(out1[0], np.broadcast_to(v_hat, (4, d))) <= TOL
+
+
+def test_workspace_poison_does_not_leak(gpu):
+    d, H, n = 128, 2, 2000
+    layer = Layer.create("q8_0", "q4_0", d, H, 1, 2016, device=gpu)
+    k = torch.randn(n, H, d, device=gpu)
+    append_rows(layer, k, k, 0, 0)
+    q = torch.randn(1, 8, d, device=gpu)
+    lens = torch.tensor([n], device=gpu)
+    from block_quantized_kv_amd import kvq_decode_workspace_bytes
+    ws = torch.empty(kvq_decode_workspace_bytes(layer, 8, 1, n), dtype=torch.uint8, device=gpu)
+    ws.view(torch.float32)[: ws.numel() // 4].fill_(float("nan"))
+    a = kvq_attend_decode(layer, q, lens, n, 0.1, workspace=ws)
+    b = kvq_attend_decode(layer, q, lens, n, 0.1)
+    assert torch.isfinite(a).all() and torch.equal(a, b)
+
+
+# ---- the five workload configurations at full size ------------------------------
+
+def _full_config(gpu, cid, layer_idx=0, heads_per_seq=None, append_last=False):
+    cfg = workloads.CONFIGS[cid]
+    kc, vc = cfg.layers[layer_idx]
+    lens = workloads.seq_lengths(cfg, "cpu").tolist()
+    layer = Layer.create(kc, vc, cfg.head_dim, cfg.n_kv_heads, cfg.n_seqs, cfg.capacity, device=gpu)
+    q = workloads.queries(cfg, layer_idx, gpu)
+    host_rows = []
+    for s, n in enumerate(lens):
+        k = workloads.kv_rows(cfg, layer_idx, s, "k", 0, n, gpu)
+        v = workloads.kv_rows(cfg, layer_idx, s, "v", 0, n, gpu)
+        if append_last:  # pre-fill n-1 rows, then the step's own one-row append
+            append_rows(layer, k[:-1], v[:-1], s, 0)
+            append_rows(layer, k[-1:], v[-1:], s, n - 1)
+        else:
+            append_rows(layer, k, v, s, 0)
+        host_rows.append((k, v))
+    out = kvq_attend_decode(layer, q, torch.tensor(lens, dtype=torch.int64, device=gpu),
+                            max(lens), cfg.scale).cpu().numpy()
+    qn = q.cpu().numpy()
+    G = cfg.gqa
+    worst = 0.0
+    for s, n in enumerate(lens):
+        kv_heads = range(cfg.n_kv_heads) if heads_per_seq is None else heads_per_seq(s)
+        for g in kv_heads:
+            k, v = host_rows[s]
+            kh = k[:, g:g + 1].cpu().numpy()
+            vh = v[:, g:g + 1].cpu().numpy()
+            heads = list(range(g * G, (g + 1) * G))
+            ref = _oracle_decode(kc, vc, qn[s][heads], kh, vh, n, cfg.scale)
+            worst = max(worst, rel_err(out[s][heads], ref))
+    assert worst <= TOL, (cid, layer_idx, worst)
+    return worst
+
+
+def test_config1_tiny_full(gpu):
+    _full_config(gpu, 1)
+
+
+def test_config2_decode_32k_full(gpu):
+    _full_config(gpu, 2, heads_per_seq=lambda s: [0, 3, 7])
+
+
+def test_config3_decode_64k_with_append(gpu):
+    _full_config(gpu, 3, heads_per_seq=lambda s: [0, 3], append_last=True)
+
+
+@pytest.mark.parametrize("layer_idx", [0, 1])
+def test_config4_decode_196k_split_kv(gpu, layer_idx):
+    _full_config(gpu, 4, layer_idx=layer_idx, heads_per_seq=lambda s: [layer_idx + 1])
+
+
+def test_config5_batched_decode(gpu):
+    _full_config(gpu, 5, heads_per_seq=lambda s: [s % 8])

@@ -1,0 +1,138 @@
+"""CPU checks of the HIP library's host side: the C-ABI library loads and
+exports every symbol include/kvq.h declares, host-only sizing, argument
+validation (which returns before anything touches a GPU), and the in-block
+permutation used by the planes."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from block_quantized_kv_amd import _binding as B
+from block_quantized_kv_amd import layout
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvq.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvq_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = B.load_library()
+    names = _declared_functions()
+    assert {"kvq_append", "kvq_attend_decode", "kvq_attend_prefill", "kvq_dequant"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+@pytest.mark.parametrize("codec,bpv", [("q4_g64", 4.25), ("q4_0", 4.5), ("q8_0", 8.5)])
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_plane_bytes_bits_per_value(codec, bpv, d):
+    # den_llama.cpp, "What this fork is": Q4_G64 is 4.25 bits per value.
+    c, s = B.kvq_plane_bytes(codec, d, 4, 2, 1024)
+    assert (c + s) * 8 == bpv * 4 * 2 * 1024 * d
+    assert B.kvq_row_code_bytes(codec, d) == (d if codec == "q8_0" else d // 2)
+
+
+def test_plane_bytes_decode_config_sizes():
+    # One K plane of the 64K-context Q4_G64 workload: 65536 rows x 4 heads x 136 B.
+    c, s = B.kvq_plane_bytes("q4_g64", 256, 4, 1, 65536)
+    assert c + s == 35_651_584
+
+
+def _fake_plane(codec="q8_0", role=0, d=128, heads=2, seqs=1, cap=64, codes=0x10000, scales=0x20000):
+    return B._Plane(B.CODECS[codec], role, d, heads, seqs, 0, cap, codes, scales)
+
+
+def _call_decode(L, q=0x1000, seq_len=0x2000, n_seqs=1, hq=4, max_len=64, out=0x3000, ws=0x4000,
+                 ws_bytes=1 << 30):
+    lib = B.load_library()
+    return lib.kvq_attend_decode(ctypes.byref(L), q, seq_len, n_seqs, hq, max_len, 0.1, out, ws,
+                                 ws_bytes, None)
+
+
+def test_validation_errors_return_before_launch():
+    lib = B.load_library()
+    good = B._Layer(_fake_plane(role=0), _fake_plane(codec="q4_0", role=1, codes=0x30000, scales=0x40000))
+    # decode: every failing argument -> exact status, nothing enqueued (no GPU here)
+    assert lib.kvq_attend_decode(None, 1, 1, 1, 4, 64, 0.1, 1, 1, 1, None) == 1
+    assert _call_decode(good, q=0) == 1
+    assert _call_decode(good, q=0x1004) == 1                      # misaligned q
+    assert _call_decode(good, hq=3) == 1                          # not a multiple of Hkv
+    assert _call_decode(good, hq=2 * 17) == 2                     # GQA 17 > 16
+    assert _call_decode(good, max_len=65) == 3                    # beyond capacity
+    assert _call_decode(good, n_seqs=2) == 1                      # more than the plane holds
+    assert _call_decode(good, ws_bytes=16) == 4                   # workspace too small
+    assert _call_decode(good, ws=0) == 4
+    bad_role = B._Layer(_fake_plane(role=1), good.v)
+    assert _call_decode(bad_role) == 1
+    bad_shape = B._Layer(good.k, _fake_plane(codec="q4_0", role=1, cap=96, codes=0x30000, scales=0x40000))
+    assert _call_decode(bad_shape) == 1
+    bad_d = B._Layer(_fake_plane(d=96), _fake_plane(role=1, d=96, codes=0x30000, scales=0x40000))
+    assert _call_decode(bad_d) == 2
+    bad_cap = B._Layer(_fake_plane(cap=40), _fake_plane(role=1, cap=40, codes=0x30000, scales=0x40000))
+    assert _call_decode(bad_cap) == 1
+    misaligned = B._Layer(_fake_plane(codes=0x10010), good.v)
+    assert _call_decode(misaligned) == 1
+    assert "aligned" in B.kvq_last_error()
+    # append
+    assert lib.kvq_append(ctypes.byref(good), 0, 0, 0x5000, 0x6000, 4, None, None) == 1
+    assert lib.kvq_append(ctypes.byref(good), 0x7000, 0, 0x5000, 0x6000, -1, None, None) == 1
+    assert lib.kvq_append(ctypes.byref(good), 0x7000, 0, 0, 0x6000, 4, None, None) == 1
+    assert lib.kvq_append(ctypes.byref(good), 0x7000, 0, 0x5000, 0x6000, 0, None, None) == 0
+    # prefill
+    assert lib.kvq_attend_prefill(ctypes.byref(good), 0x1000, 0, 60, 8, 4, 0.1, 0x3000, 0, 0, None) == 3
+    assert lib.kvq_attend_prefill(ctypes.byref(good), 0x1000, 1, 0, 8, 4, 0.1, 0x3000, 0, 0, None) == 1
+    # dequant
+    p = _fake_plane()
+    assert lib.kvq_dequant(ctypes.byref(p), 0, 60, 8, 0x3000, None) == 3
+    assert lib.kvq_dequant(ctypes.byref(p), 0, 0, 8, 0, None) == 1
+    assert lib.kvq_dequant(ctypes.byref(p), 0, 0, 0, 0x3000, None) == 0
+    assert B.kvq_status_str(4).startswith("KVQ_EWORKSPACE")
+
+
+def test_decode_workspace_grows_with_length():
+    good = B._Layer(_fake_plane(cap=1 << 17), _fake_plane(role=1, cap=1 << 17, codes=0x30000, scales=0x40000))
+    lib = B.load_library()
+    a = lib.kvq_decode_workspace_bytes(ctypes.byref(good), 4, 1, 1024)
+    b = lib.kvq_decode_workspace_bytes(ctypes.byref(good), 4, 1, 1 << 17)
+    assert 0 < a <= b
+
+
+@pytest.mark.parametrize("codec", ["q8_0", "q4_0", "q4_g64"])
+@pytest.mark.parametrize("role", ["k", "v"])
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_block_permutation_is_a_bijection(codec, role, d):
+    byte, shift = layout.code_positions(codec, role, d)
+    rb = layout.row_bytes(codec, d)
+    slot = byte * 2 + shift // 4 if codec != "q8_0" else byte
+    n_slots = 32 * rb * (2 if codec != "q8_0" else 1)
+    assert slot.min() == 0 and slot.max() == n_slots - 1
+    assert np.unique(slot).size == slot.size == n_slots
+    sidx = layout.scale_positions(codec, role, d)
+    assert np.unique(sidx).size == sidx.size == 32 * (d // layout.GROUP[codec])
+
+
+@pytest.mark.parametrize("codec", ["q8_0", "q4_0", "q4_g64"])
+@pytest.mark.parametrize("role", ["k", "v"])
+def test_unpack_inverts_a_scatter(codec, role):
+    d, nb = 128, 3
+    rng = np.random.default_rng(0)
+    rb = layout.row_bytes(codec, d)
+    rows = rng.integers(0, 256, size=(nb * 32, rb), dtype=np.uint8)
+    # scatter row-major codes into blocks with the documented positions
+    byte, shift = layout.code_positions(codec, role, d)
+    blocks = np.zeros((nb, 32 * rb), np.uint8)
+    for bi in range(nb):
+        for j in range(32):
+            r = rows[bi * 32 + j]
+            for c in range(d):
+                v = r[c] if codec == "q8_0" else (r[c // 2] >> (4 * (c % 2))) & 0xF
+                blocks[bi, byte[j, c]] |= np.uint8(v << shift[j, c])
+    back = layout.unpack_codes(codec, role, d, blocks)
+    assert np.array_equal(back, rows)
