@@ -18,6 +18,7 @@ from ._binding import (  # noqa: F401
     kvq_attend_prefill,
     kvq_dequant,
     kvq_decode_workspace_bytes,
+    decode_workspace,
     kvq_prefill_workspace_bytes,
     kvq_plane_bytes,
     kvq_row_code_bytes,

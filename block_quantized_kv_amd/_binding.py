@@ -187,6 +187,12 @@ def kvq_decode_workspace_bytes(layer: Layer, n_q_heads: int, n_seqs: int, max_le
     return int(load_library().kvq_decode_workspace_bytes(ctypes.byref(L), n_q_heads, n_seqs, max_len))
 
 
+def decode_workspace(layer: Layer, n_q_heads: int, n_seqs: int, max_len: int):
+    """A decode workspace (scratch for the split partials)."""
+    nbytes = max(kvq_decode_workspace_bytes(layer, n_q_heads, n_seqs, max_len), 256)
+    return torch.zeros(nbytes, dtype=torch.uint8, device=layer.k.codes.device)
+
+
 def kvq_attend_decode(layer: Layer, q, seq_len, max_len: int, softmax_scale: float, out=None,
                       workspace=None, stream=None):
     """q fp32 [n_seqs][n_q_heads][head_dim]; seq_len int64 [n_seqs] (device)."""
@@ -197,8 +203,7 @@ def kvq_attend_decode(layer: Layer, q, seq_len, max_len: int, softmax_scale: flo
         out = torch.empty_like(q)
     _need(out, "out", torch.float32, (n_seqs, hq, layer.k.head_dim))
     if workspace is None:
-        workspace = torch.empty(max(kvq_decode_workspace_bytes(layer, hq, n_seqs, max_len), 256),
-                                dtype=torch.uint8, device=q.device)
+        workspace = decode_workspace(layer, hq, n_seqs, max_len)
     if not workspace.is_cuda or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous device tensor")
     L = layer.struct()

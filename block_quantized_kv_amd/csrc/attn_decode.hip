@@ -30,7 +30,9 @@
 //  * All K/V scales of the split are staged in LDS by the whole workgroup up
 //    front; code words are prefetched one block ahead in registers.
 //  * The 8 waves merge through LDS; each workgroup writes one partial
-//    (unnormalized O, max, sum) per query head; attn_combine merges splits.
+//    (unnormalized O, max, sum) per query head, or the final output when the
+//    sequence fits in one split; combine_kernel merges the splits
+//    (log-sum-exp) with all partial loads in flight at once.
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -107,7 +109,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     int64_t len = a.seq_len[b];
     len = len < 0 ? 0 : (len > a.max_len ? a.max_len : len);
     const int64_t r0 = (int64_t)sp * a.split_rows;
-    if (r0 >= len) return;  // whole workgroup: no barrier reached
+    if (r0 >= len) {  // whole workgroup: no barrier reached
+        if (len == 0 && sp == 0) {  // an empty sequence attends nothing: output 0
+            float *dst = a.out + ((int64_t)b * a.n_q_heads + (int64_t)kvh * a.gqa) * D;
+            for (int i = threadIdx.x; i < a.gqa * D; i += kThreads) dst[i] = 0.0f;
+        }
+        return;
+    }
     const int64_t r1 = (r0 + a.split_rows < len) ? r0 + a.split_rows : len;
     const int nblk = (int)((r1 - r0 + kBlockRows - 1) / kBlockRows);
     const int64_t blk0 = r0 / kBlockRows;
@@ -193,6 +201,18 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     const float c_h = a.scale_log2 * ldexpf(1.0f, qexp);
 
     __syncthreads();  // scales staged
+    if ((r1 & (kBlockRows - 1)) != 0) {
+        // Rows past the end of the last block may never have been written:
+        // zero their V scales so that 0 * V_hat stays 0 whatever the bytes hold.
+        uint16_t *svl = sv + (nblk - 1) * C::V_BLOCK_SCALES;
+        const int valid = (int)(r1 & (kBlockRows - 1));
+        for (int i = tid; i < C::V_BLOCK_SCALES; i += kThreads) {
+            const int kq = i / (8 * C::VNG), sl = i % 8;
+            const int j = (sl >> 2) * 16 + 4 * kq + (sl & 3);
+            if (j >= valid) svl[i] = 0;
+        }
+        __syncthreads();
+    }
 
     f4 O[C::CB];
 #pragma unroll
@@ -295,6 +315,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
         }
     }
     __syncthreads();
+    const int nsp = (int)((len + a.split_rows - 1) / a.split_rows);
     for (int idx = tid; idx < G * D; idx += kThreads) {
         const int hh = idx / D, c = idx % D;
         float M = -INFINITY;
@@ -307,7 +328,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
             o = fmaf(e, so[(w * G + hh) * D + c], o);
             L = fmaf(e, sl[w * G + hh], L);
         }
-        const int64_t ph = ((int64_t)b * a.n_q_heads + (int64_t)kvh * G + hh) * a.max_splits + sp;
+        const int64_t qh = (int64_t)b * a.n_q_heads + (int64_t)kvh * G + hh;
+        if (nsp == 1) {
+            a.out[qh * D + c] = o / L;
+            continue;
+        }
+        const int64_t ph = qh * a.max_splits + sp;
         a.part_o[ph * D + c] = o;
         if (c == 0) {
             a.part_ml[2 * ph] = M;
@@ -316,28 +342,54 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     }
 }
 
-// One workgroup per (query head, sequence): log-sum-exp merge of the splits.
+// Log-sum-exp merge of the splits of one (sequence, query head), 64 channels
+// per workgroup: 4 thread groups take every 4th split with independent loads,
+// the per-split weights exp2(m_s - M) are computed once into LDS.
 template <int D>
-__global__ __launch_bounds__(D) void combine_kernel(DecodeArgs a) {
-    const int hq = blockIdx.x, b = blockIdx.y, c = threadIdx.x;
+__global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
+    extern __shared__ float sw[];  // [nsp] weights, then [4][64] partial sums
+    __shared__ float s_red[256];
+    const int hq = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
     int64_t len = a.seq_len[b];
     len = len < 0 ? 0 : (len > a.max_len ? a.max_len : len);
     const int nsp = (int)((len + a.split_rows - 1) / a.split_rows);
-    float *dst = a.out + ((int64_t)b * a.n_q_heads + hq) * D;
-    if (nsp == 0) {
-        dst[c] = 0.0f;
-        return;
-    }
-    const int64_t ph0 = ((int64_t)b * a.n_q_heads + hq) * a.max_splits;
+    if (nsp <= 1) return;  // the decode kernel wrote the output itself
+    const int64_t qh = (int64_t)b * a.n_q_heads + hq;
+    const float *ml = a.part_ml + 2 * qh * a.max_splits;
+    // M = max_s m_s
     float M = -INFINITY;
-    for (int s = 0; s < nsp; ++s) M = fmaxf(M, a.part_ml[2 * (ph0 + s)]);
-    float num = 0.0f, den = 0.0f;
-    for (int s = 0; s < nsp; ++s) {
-        const float e = fast_exp2(a.part_ml[2 * (ph0 + s)] - M);
-        num = fmaf(e, a.part_o[(ph0 + s) * D + c], num);
-        den = fmaf(e, a.part_ml[2 * (ph0 + s) + 1], den);
+    for (int s2 = tid; s2 < nsp; s2 += 256) M = fmaxf(M, ml[2 * s2]);
+    s_red[tid] = M;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if (tid < w) s_red[tid] = fmaxf(s_red[tid], s_red[tid + w]);
+        __syncthreads();
     }
-    dst[c] = num / den;
+    M = s_red[0];
+    __syncthreads();
+    float L = 0.0f;
+    for (int s2 = tid; s2 < nsp; s2 += 256) {
+        const float w = fast_exp2(ml[2 * s2] - M);
+        sw[s2] = w;
+        L = fmaf(w, ml[2 * s2 + 1], L);
+    }
+    s_red[tid] = L;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if (tid < w) s_red[tid] += s_red[tid + w];
+        __syncthreads();
+    }
+    L = s_red[0];
+    __syncthreads();
+    const int c = blockIdx.x * 64 + (tid & 63), sg = tid >> 6;
+    const float *po = a.part_o + qh * a.max_splits * D + c;
+    float o = 0.0f;
+#pragma unroll 8
+    for (int s2 = sg; s2 < nsp; s2 += 4) o = fmaf(sw[s2], po[(int64_t)s2 * D], o);
+    s_red[tid] = o;
+    __syncthreads();
+    if (sg == 0)
+        a.out[qh * D + c] = (s_red[tid] + s_red[tid + 64] + s_red[tid + 128] + s_red[tid + 192]) / L;
 }
 
 template <int D, int KC, int VC>
@@ -355,8 +407,9 @@ hipError_t launch_typed(const DecodeArgs &a, hipStream_t s) {
     }
     decode_kernel<D, KC, VC><<<grid, dim3(kThreads), lds, s>>>(a);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    combine_kernel<D><<<dim3((unsigned)a.n_q_heads, (unsigned)a.n_seqs), dim3(D), 0, s>>>(a);
+    if (e != hipSuccess || a.max_splits <= 1) return e;
+    combine_kernel<D><<<dim3(D / 64, (unsigned)a.n_q_heads, (unsigned)a.n_seqs), dim3(256),
+                        (size_t)a.max_splits * sizeof(float), s>>>(a);
     return hipGetLastError();
 }
 
@@ -392,8 +445,12 @@ DecodePlan plan_decode(int head_dim, int n_kv_heads, int n_q_heads, int n_seqs, 
     p.split_rows = (int)(per_split * kBlockRows);
     p.max_splits = (int)((max_len + p.split_rows - 1) / p.split_rows);
     if (p.max_splits < 1) p.max_splits = 1;
-    p.part_o_bytes = (size_t)n_seqs * n_q_heads * p.max_splits * head_dim * sizeof(float);
+    auto up = [](size_t x) { return (x + 255) / 256 * 256; };
     p.part_ml_bytes = (size_t)n_seqs * n_q_heads * p.max_splits * 2 * sizeof(float);
+    p.part_o_bytes = (size_t)n_seqs * n_q_heads * p.max_splits * head_dim * sizeof(float);
+    p.off_part_ml = 0;
+    p.off_part_o = p.off_part_ml + up(p.part_ml_bytes);
+    p.total_bytes = p.off_part_o + up(p.part_o_bytes);
     return p;
 }
 

@@ -56,23 +56,25 @@ __device__ __forceinline__ void store_codes(uint8_t *blk, int d, int j, int c0, 
     }
 }
 
+// Quantizes and stores this thread's 8 channels of one row of one plane.
 template <int CODEC, int ROLE>
-__global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
-    const int d = a.plane.head_dim;
-    const int chunks = d / 8;                      // threads per row
-    const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t n_rows = (int64_t)a.n_tokens * a.plane.n_kv_heads;
+__device__ __forceinline__ void append_plane(const PlaneView &pl, const float *xsrc,
+                                             const int32_t *seq_idx, const int64_t *pos_arr,
+                                             int n_tokens, int32_t *dev_status, int64_t tid) {
+    const int d = pl.head_dim;
+    const int chunks = d / 8;  // threads per row
+    const int64_t n_rows = (int64_t)n_tokens * pl.n_kv_heads;
     // Threads past the end still take part in the shuffles below (a group is
     // always inside one wave because G/8 divides 64 and d/8).
     const bool live = tid < n_rows * chunks;
     const int64_t row = live ? tid / chunks : 0;
     const int chunk = (int)(tid % chunks);
-    const int tok = (int)(row / a.plane.n_kv_heads);
-    const int head = (int)(row % a.plane.n_kv_heads);
+    const int tok = (int)(row / pl.n_kv_heads);
+    const int head = (int)(row % pl.n_kv_heads);
 
     float x[8];
     if (live) {
-        const float4 *src = reinterpret_cast<const float4 *>(a.x + row * d + chunk * 8);
+        const float4 *src = reinterpret_cast<const float4 *>(xsrc + row * d + chunk * 8);
         const float4 v0 = src[0], v1 = src[1];
         x[0] = v0.x; x[1] = v0.y; x[2] = v0.z; x[3] = v0.w;
         x[4] = v1.x; x[5] = v1.y; x[6] = v1.z; x[7] = v1.w;
@@ -96,24 +98,35 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
     }
     if (!live) return;
 
-    const int32_t sq = a.seq_idx[tok];
-    const int64_t pos = a.pos[tok];
-    if (sq < 0 || sq >= a.plane.n_seqs || pos < 0 || pos >= a.plane.capacity) {
-        if (a.dev_status) *a.dev_status = 3;  // KVQ_ERANGE
+    const int32_t sq = seq_idx[tok];
+    const int64_t pos = pos_arr[tok];
+    if (sq < 0 || sq >= pl.n_seqs || pos < 0 || pos >= pl.capacity) {
+        if (dev_status) *dev_status = 3;  // KVQ_ERANGE
         return;
     }
     const int64_t blk_idx = pos / kBlockRows;
     const int j = (int)(pos % kBlockRows);
-    const int64_t head_lin = (int64_t)sq * a.plane.n_kv_heads + head;
-    uint8_t *blk = a.plane.codes + head_lin * a.plane.head_code_stride +
-                   blk_idx * block_code_bytes(CODEC, d);
-    uint16_t *sblk = a.plane.scales + head_lin * a.plane.head_scale_stride +
-                     blk_idx * block_scales(CODEC, d);
+    const int64_t head_lin = (int64_t)sq * pl.n_kv_heads + head;
+    uint8_t *blk = pl.codes + head_lin * pl.head_code_stride + blk_idx * block_code_bytes(CODEC, d);
+    uint16_t *sblk = pl.scales + head_lin * pl.head_scale_stride + blk_idx * block_scales(CODEC, d);
     store_codes<CODEC, ROLE>(blk, d, j, chunk * 8, q);
     if (chunk % lanes_per_group == 0) {
         const int g = chunk / lanes_per_group;
         const int si = ROLE == ROLE_K ? k_scale_index(CODEC, d, j, g) : v_scale_index(CODEC, d, j, g);
         sblk[si] = __builtin_bit_cast(uint16_t, d16);
+    }
+}
+
+// grid.y = 0: K plane, 1: V plane (one launch appends both).
+template <int KC, int VC>
+__global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
+    const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (blockIdx.y == 0) {
+        if (a.x[0]) append_plane<KC, ROLE_K>(a.plane[0], a.x[0], a.seq_idx, a.pos, a.n_tokens,
+                                             a.dev_status, tid);
+    } else {
+        if (a.x[1]) append_plane<VC, ROLE_V>(a.plane[1], a.x[1], a.seq_idx, a.pos, a.n_tokens,
+                                             a.dev_status, tid);
     }
 }
 
@@ -159,16 +172,20 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
 }  // namespace
 
 hipError_t launch_append(const AppendArgs &a, hipStream_t s) {
-    const int64_t threads = (int64_t)a.n_tokens * a.plane.n_kv_heads * (a.plane.head_dim / 8);
+    const int64_t threads =
+        (int64_t)a.n_tokens * a.plane[0].n_kv_heads * (a.plane[0].head_dim / 8);
     if (threads == 0) return hipSuccess;
-    const dim3 block(256), grid((unsigned)((threads + 255) / 256));
-    switch (a.plane.codec * 2 + a.role) {
-        case Q8_0 * 2 + ROLE_K: append_kernel<Q8_0, ROLE_K><<<grid, block, 0, s>>>(a); break;
-        case Q8_0 * 2 + ROLE_V: append_kernel<Q8_0, ROLE_V><<<grid, block, 0, s>>>(a); break;
-        case Q4_0 * 2 + ROLE_K: append_kernel<Q4_0, ROLE_K><<<grid, block, 0, s>>>(a); break;
-        case Q4_0 * 2 + ROLE_V: append_kernel<Q4_0, ROLE_V><<<grid, block, 0, s>>>(a); break;
-        case Q4_G64 * 2 + ROLE_K: append_kernel<Q4_G64, ROLE_K><<<grid, block, 0, s>>>(a); break;
-        case Q4_G64 * 2 + ROLE_V: append_kernel<Q4_G64, ROLE_V><<<grid, block, 0, s>>>(a); break;
+    const dim3 block(256), grid((unsigned)((threads + 255) / 256), 2);
+    switch (a.plane[0].codec * 3 + a.plane[1].codec) {
+        case Q8_0 * 3 + Q8_0: append_kernel<Q8_0, Q8_0><<<grid, block, 0, s>>>(a); break;
+        case Q8_0 * 3 + Q4_0: append_kernel<Q8_0, Q4_0><<<grid, block, 0, s>>>(a); break;
+        case Q8_0 * 3 + Q4_G64: append_kernel<Q8_0, Q4_G64><<<grid, block, 0, s>>>(a); break;
+        case Q4_0 * 3 + Q8_0: append_kernel<Q4_0, Q8_0><<<grid, block, 0, s>>>(a); break;
+        case Q4_0 * 3 + Q4_0: append_kernel<Q4_0, Q4_0><<<grid, block, 0, s>>>(a); break;
+        case Q4_0 * 3 + Q4_G64: append_kernel<Q4_0, Q4_G64><<<grid, block, 0, s>>>(a); break;
+        case Q4_G64 * 3 + Q8_0: append_kernel<Q4_G64, Q8_0><<<grid, block, 0, s>>>(a); break;
+        case Q4_G64 * 3 + Q4_0: append_kernel<Q4_G64, Q4_0><<<grid, block, 0, s>>>(a); break;
+        case Q4_G64 * 3 + Q4_G64: append_kernel<Q4_G64, Q4_G64><<<grid, block, 0, s>>>(a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -119,22 +119,16 @@ kvq_status kvq_append(const kvq_layer *L, const float *k_new, const float *v_new
     if ((k_new && !aligned(k_new, 16)) || (v_new && !aligned(v_new, 16)))
         return fail(KVQ_EINVAL, "k_new/v_new not 16-byte aligned");
     if (n_tokens == 0) return ok();
-    hipStream_t s = static_cast<hipStream_t>(hip_stream);
-    for (int r = 0; r < 2; ++r) {
-        const float *x = r == 0 ? k_new : v_new;
-        if (!x) continue;
-        kvq::AppendArgs a;
-        a.plane = view(r == 0 ? L->k : L->v);
-        a.role = r == 0 ? kvq::ROLE_K : kvq::ROLE_V;
-        a.x = x;
-        a.seq_idx = seq_idx;
-        a.pos = pos;
-        a.n_tokens = n_tokens;
-        a.dev_status = dev_status;
-        hipError_t e = kvq::launch_append(a, s);
-        if (e != hipSuccess) return hip_status(e, "append launch");
-    }
-    return ok();
+    kvq::AppendArgs a;
+    a.plane[0] = view(L->k);
+    a.plane[1] = view(L->v);
+    a.x[0] = k_new;
+    a.x[1] = v_new;
+    a.seq_idx = seq_idx;
+    a.pos = pos;
+    a.n_tokens = n_tokens;
+    a.dev_status = dev_status;
+    return hip_status(kvq::launch_append(a, static_cast<hipStream_t>(hip_stream)), "append launch");
 }
 
 size_t kvq_decode_workspace_bytes(const kvq_layer *L, int32_t n_q_heads, int32_t n_seqs,
@@ -142,7 +136,7 @@ size_t kvq_decode_workspace_bytes(const kvq_layer *L, int32_t n_q_heads, int32_t
     if (!L || n_q_heads <= 0 || n_seqs <= 0 || max_len < 0) return 0;
     const kvq::DecodePlan p =
         kvq::plan_decode(L->k.head_dim, L->k.n_kv_heads, n_q_heads, n_seqs, max_len);
-    return ((p.part_o_bytes + 255) / 256) * 256 + p.part_ml_bytes;
+    return p.total_bytes;
 }
 
 kvq_status kvq_attend_decode(const kvq_layer *L, const float *q, const int64_t *seq_len,
@@ -174,15 +168,18 @@ kvq_status kvq_attend_decode(const kvq_layer *L, const float *q, const int64_t *
 
     const kvq::DecodePlan p =
         kvq::plan_decode(L->k.head_dim, L->k.n_kv_heads, n_q_heads, n_seqs, max_len);
+    if (p.max_splits > 16384)
+        return fail(KVQ_EUNSUPPORTED, "max_len %lld needs %d splits (limit 16384)",
+                    (long long)max_len, p.max_splits);
     kvq::DecodeArgs a;
     a.k = view(L->k);
     a.v = view(L->v);
     a.q = q;
     a.seq_len = seq_len;
     a.out = out;
-    a.part_o = static_cast<float *>(workspace);
-    a.part_ml = reinterpret_cast<float *>(static_cast<char *>(workspace) +
-                                          ((p.part_o_bytes + 255) / 256) * 256);
+    char *ws = static_cast<char *>(workspace);
+    a.part_ml = reinterpret_cast<float *>(ws + p.off_part_ml);
+    a.part_o = reinterpret_cast<float *>(ws + p.off_part_o);
     a.n_seqs = n_seqs;
     a.n_q_heads = n_q_heads;
     a.gqa = gqa;

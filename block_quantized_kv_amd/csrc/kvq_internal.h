@@ -22,10 +22,10 @@ struct PlaneView {
     int64_t head_scale_stride;  // binary16 per (seq, head) = capacity/32 * block_scales
 };
 
+// Both planes of a layer are appended by one launch (grid.y = plane).
 struct AppendArgs {
-    PlaneView plane;
-    int role;
-    const float *x;          // [n_tokens][n_kv_heads][head_dim]
+    PlaneView plane[2];      // K, V
+    const float *x[2];       // [n_tokens][n_kv_heads][head_dim]; null = skip that plane
     const int32_t *seq_idx;  // [n_tokens]
     const int64_t *pos;      // [n_tokens]
     int n_tokens;
@@ -75,6 +75,8 @@ struct DecodePlan {
     int max_splits;
     size_t part_o_bytes;
     size_t part_ml_bytes;
+    // byte offsets inside the workspace
+    size_t off_part_ml, off_part_o, total_bytes;
 };
 DecodePlan plan_decode(int head_dim, int n_kv_heads, int n_q_heads, int n_seqs, int64_t max_len);
 

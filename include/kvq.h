@@ -145,7 +145,8 @@ size_t kvq_decode_workspace_bytes(const kvq_layer *L, int32_t n_q_heads, int32_t
  *   max_len  : host upper bound of the lengths, sizes the grid; <= capacity
  *   out      : fp32 [n_seqs][n_q_heads][head_dim], device; zeros for len_b = 0
  *   workspace: device scratch of at least kvq_decode_workspace_bytes() bytes,
- *              256-B aligned; its contents are not preserved across calls
+ *              256-B aligned; its contents are not preserved across calls and
+ *              calls that run concurrently must not share it.
  * n_seqs may be smaller than the planes' n_seqs (sequences 0..n_seqs-1).
  * n_q_heads / n_kv_heads must be an integer in [1, KVQ_MAX_GQA].
  * Precision: fp32 statistics and accumulation; the matrix-core operands are

@@ -117,6 +117,61 @@ def test_workspace_poison_does_not_leak(gpu):
     a = kvq_attend_decode(layer, q, lens, n, 0.1, workspace=ws)
     b = kvq_attend_decode(layer, q, lens, n, 0.1)
     assert torch.isfinite(a).all() and torch.equal(a, b)
+    c = kvq_attend_decode(layer, q, lens, n, 0.1, workspace=ws)  # reuse
+    assert torch.equal(a, c)
+
+
+def test_garbage_rows_past_length_are_ignored(gpu):
+    """Rows past len_b inside the last block may hold anything (never appended):
+    NaN/Inf scale bit patterns there must not reach the output."""
+    d, H, n = 128, 1, 45
+    layer = Layer.create("q8_0", "q4_0", d, H, 1, 64, device=gpu)
+    layer.k.scales.fill_(0x7E00)  # binary16 NaN everywhere
+    layer.v.scales.fill_(0x7C00)  # binary16 +inf everywhere
+    layer.v.codes.fill_(0x3C)
+    rng = np.random.default_rng(2)
+    k = rng.standard_normal((n, H, d)).astype(np.float32)
+    v = rng.standard_normal((n, H, d)).astype(np.float32)
+    append_rows(layer, torch.from_numpy(k).to(gpu), torch.from_numpy(v).to(gpu), 0, 0)
+    q = rng.standard_normal((1, 4, d)).astype(np.float32)
+    out = kvq_attend_decode(layer, torch.from_numpy(q).to(gpu), torch.tensor([n], device=gpu), n,
+                            0.1).cpu().numpy()
+    ref = _oracle_decode("q8_0", "q4_0", q[0], k, v, n, 0.1)
+    assert np.isfinite(out).all() and rel_err(out[0], ref) <= TOL
+
+
+def test_graph_replay_matches_eager(gpu):
+    """append + decode captured in a HIP graph: every replay equals the eager call
+    (the library only enqueues kernels: no allocation, sync or memset)."""
+    d, H, n = 256, 4, 4000
+    layer = Layer.create("q4_g64", "q4_g64", d, H, 1, 4032, device=gpu)
+    k = torch.randn(n, H, d, device=gpu)
+    v = torch.randn(n, H, d, device=gpu)
+    append_rows(layer, k[:-1], v[:-1], 0, 0)
+    q = torch.randn(1, 24, d, device=gpu)
+    lens = torch.tensor([n], device=gpu)
+    from block_quantized_kv_amd import decode_workspace, kvq_append
+    ws = decode_workspace(layer, 24, 1, n)
+    sq = torch.zeros(1, dtype=torch.int32, device=gpu)
+    pos = torch.tensor([n - 1], dtype=torch.int64, device=gpu)
+    out = torch.empty_like(q)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        kvq_append(layer, k[-1:].contiguous(), v[-1:].contiguous(), sq, pos, stream=s)
+        kvq_attend_decode(layer, q, lens, n, 0.0625, out=out, workspace=ws, stream=s)
+    torch.cuda.synchronize()
+    eager = out.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        kvq_append(layer, k[-1:].contiguous(), v[-1:].contiguous(), sq, pos, stream=s)
+        kvq_attend_decode(layer, q, lens, n, 0.0625, out=out, workspace=ws, stream=s)
+    for i in range(4):
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), i
+        kvq_attend_decode(layer, q, lens, n, 0.0625, workspace=ws)  # eager work between replays
 
 
 # ---- the five workload configurations at full size ------------------------------
