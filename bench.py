@@ -43,7 +43,22 @@ def _args():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="only run plain 256 MiB device copies (HBM counter calibration)")
     return p.parse_args()
+
+
+def calibrate_copy():
+    """Plain device-to-device copies of a known size: what FETCH_SIZE /
+    WRITE_SIZE read for exactly 256 MiB in and 256 MiB out per dispatch."""
+    import torch
+    n = 256 << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(8):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "copy", "bytes_per_dispatch": n, "dispatches": 8}))
 
 
 def decode_bytes(cfg) -> dict:
@@ -61,6 +76,9 @@ def decode_bytes(cfg) -> dict:
 
 def main():
     args = _args()
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no "
               "multi-GPU path", file=sys.stderr)

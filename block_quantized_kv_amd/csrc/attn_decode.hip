@@ -27,12 +27,17 @@
 //  * Online softmax in log2 units; the running max is only raised when a
 //    block exceeds it by more than 8 (probabilities stay <= 256), so the
 //    64-register rescale of O is rare.
-//  * All K/V scales of the split are staged in LDS by the whole workgroup up
-//    front; code words are prefetched one block ahead in registers.
+//  * Each wave prefetches its next 32-row block (code words and a slice of
+//    the block's scales) into registers while it computes the current one;
+//    the scales go through a per-wave LDS slot to reach operand order.
+//    Blocks are handed out dynamically inside the workgroup (LDS counter), so
+//    the 8 waves finish together.
+//  * The workgroup's query rows are staged once in LDS (coalesced), so the
+//    many workgroups of one kv-head do not all hammer the same few lines.
 //  * The 8 waves merge through LDS; each workgroup writes one partial
 //    (unnormalized O, max, sum) per query head, or the final output when the
 //    sequence fits in one split; combine_kernel merges the splits
-//    (log-sum-exp) with all partial loads in flight at once.
+//    (log-sum-exp) with many partial loads in flight at once.
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -64,6 +69,16 @@ struct Cfg {
     static constexpr int V_BLOCK_BYTES = block_code_bytes(VC, D);
     static constexpr int K_BLOCK_SCALES = block_scales(KC, D);
     static constexpr int V_BLOCK_SCALES = block_scales(VC, D);
+    static constexpr int KS_WORDS = K_BLOCK_SCALES / 2;  // 32-bit words of K scales per block
+    static constexpr int VS_WORDS = V_BLOCK_SCALES / 2;
+    static constexpr int KS_PER_LANE = (KS_WORDS + 63) / 64;
+    static constexpr int VS_PER_LANE = (VS_WORDS + 63) / 64;
+    // head_dim 256: the query's low half lives in a per-wave LDS copy (read
+    // once per k-step) to leave registers for two blocks in flight
+    static constexpr bool QLO_LDS = D == 256;
+    static constexpr int SLOT_WORDS = KS_WORDS + VS_WORDS;
+    static constexpr int QLO_BYTES = QLO_LDS ? KSTEPS * 64 * 16 : 0;  // per wave
+    static constexpr int QOFF = kWaves * (SLOT_WORDS * 4 + QLO_BYTES);  // staged query rows
 };
 
 // Loads the LB bytes lane `lane` owns in a chunk-major region into words.
@@ -85,25 +100,43 @@ __device__ __forceinline__ void load_lane_words(const uint8_t *region, int lane,
     }
 }
 
+// Everything one wave needs from HBM for one 32-row block: its K and V code
+// words and one slice of the block's K and V scales (the whole wave loads each
+// block's scales with one coalesced pass, then stages them in its own LDS slot
+// to read them back in operand order).
 template <int D, int KC, int VC>
-struct BlockCodes {
-    uint32_t k[2][Cfg<D, KC, VC>::K_WORDS];
-    uint32_t v[Cfg<D, KC, VC>::V_WORDS];
+struct Buf {
+    using C = Cfg<D, KC, VC>;
+    uint32_t k[2][C::K_WORDS];
+    uint32_t v[C::V_WORDS];
+    uint32_t ks[C::KS_PER_LANE];
+    uint32_t vs[C::VS_PER_LANE];
 };
 
 template <int D, int KC, int VC>
-__device__ __forceinline__ void load_block(BlockCodes<D, KC, VC> &bc, const uint8_t *kblk,
-                                           const uint8_t *vblk, int lane) {
+__device__ __forceinline__ void load_buf(Buf<D, KC, VC> &bf, const uint8_t *kblk, const uint8_t *vblk,
+                                         const uint32_t *ksb, const uint32_t *vsb, int lane) {
     using C = Cfg<D, KC, VC>;
-    load_lane_words<C::K_LB>(kblk, lane, bc.k[0]);
-    load_lane_words<C::K_LB>(kblk + C::K_TILE_BYTES, lane, bc.k[1]);
-    load_lane_words<C::V_LB>(vblk, lane, bc.v);
+    load_lane_words<C::K_LB>(kblk, lane, bf.k[0]);
+    load_lane_words<C::K_LB>(kblk + C::K_TILE_BYTES, lane, bf.k[1]);
+    load_lane_words<C::V_LB>(vblk, lane, bf.v);
+#pragma unroll
+    for (int i = 0; i < C::KS_PER_LANE; ++i) {
+        const int w = lane + 64 * i;
+        bf.ks[i] = w < C::KS_WORDS ? ksb[w] : 0u;
+    }
+#pragma unroll
+    for (int i = 0; i < C::VS_PER_LANE; ++i) {
+        const int w = lane + 64 * i;
+        bf.vs[i] = w < C::VS_WORDS ? vsb[w] : 0u;
+    }
 }
 
 template <int D, int KC, int VC>
 __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     using C = Cfg<D, KC, VC>;
     extern __shared__ __align__(16) unsigned char smem[];
+    __shared__ int s_next;
 
     const int sp = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
     int64_t len = a.seq_len[b];
@@ -116,8 +149,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
         }
         return;
     }
-    const int64_t r1 = (r0 + a.split_rows < len) ? r0 + a.split_rows : len;
-    const int nblk = (int)((r1 - r0 + kBlockRows - 1) / kBlockRows);
+    const int nrows = (int)((r0 + a.split_rows < len) ? a.split_rows : len - r0);
+    const int nblk = (nrows + kBlockRows - 1) / kBlockRows;
     const int64_t blk0 = r0 / kBlockRows;
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -127,42 +160,55 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     const int64_t head_lin = (int64_t)b * a.k.n_kv_heads + kvh;
     const uint8_t *kcodes = a.k.codes + head_lin * a.k.head_code_stride + blk0 * C::K_BLOCK_BYTES;
     const uint8_t *vcodes = a.v.codes + head_lin * a.v.head_code_stride + blk0 * C::V_BLOCK_BYTES;
-    const uint16_t *kscales = a.k.scales + head_lin * a.k.head_scale_stride + blk0 * C::K_BLOCK_SCALES;
-    const uint16_t *vscales = a.v.scales + head_lin * a.v.head_scale_stride + blk0 * C::V_BLOCK_SCALES;
+    const uint32_t *kscales = reinterpret_cast<const uint32_t *>(
+        a.k.scales + head_lin * a.k.head_scale_stride + blk0 * C::K_BLOCK_SCALES);
+    const uint32_t *vscales = reinterpret_cast<const uint32_t *>(
+        a.v.scales + head_lin * a.v.head_scale_stride + blk0 * C::V_BLOCK_SCALES);
+    auto issue = [&](Buf<D, KC, VC> &bf, int idx) {
+        load_buf<D, KC, VC>(bf, kcodes + (int64_t)idx * C::K_BLOCK_BYTES,
+                            vcodes + (int64_t)idx * C::V_BLOCK_BYTES,
+                            kscales + (int64_t)idx * C::KS_WORDS, vscales + (int64_t)idx * C::VS_WORDS,
+                            lane);
+    };
 
-    // Prefetch this wave's first block of codes.
-    BlockCodes<D, KC, VC> cur;
-    if (wave < nblk) load_block<D, KC, VC>(cur, kcodes + (int64_t)wave * C::K_BLOCK_BYTES,
-                                           vcodes + (int64_t)wave * C::V_BLOCK_BYTES, lane);
-
-    // Stage every K and V scale of the split in LDS (contiguous in memory).
-    uint16_t *sk = reinterpret_cast<uint16_t *>(smem);
-    uint16_t *sv = sk + (a.split_rows / kBlockRows) * C::K_BLOCK_SCALES;
+    // ---- the workgroup's G query rows (G*D fp32, contiguous) go to LDS once
+    // with coalesced loads; each wave then reads its operand slice from there.
+    float *sq = reinterpret_cast<float *>(smem + C::QOFF);
     {
-        const int kw = nblk * C::K_BLOCK_SCALES / 8;  // 16-byte units (block scales are 64k B)
-        const int vw = nblk * C::V_BLOCK_SCALES / 8;
-        const u4 *ks4 = reinterpret_cast<const u4 *>(kscales);
-        const u4 *vs4 = reinterpret_cast<const u4 *>(vscales);
-        for (int i = tid; i < kw; i += kThreads) reinterpret_cast<u4 *>(sk)[i] = ks4[i];
-        for (int i = tid; i < vw; i += kThreads) reinterpret_cast<u4 *>(sv)[i] = vs4[i];
+        const float4 *qsrc = reinterpret_cast<const float4 *>(
+            a.q + ((int64_t)b * a.n_q_heads + (int64_t)kvh * G) * D);
+        for (int i = tid; i < G * D / 4; i += kThreads) reinterpret_cast<float4 *>(sq)[i] = qsrc[i];
     }
-
-    // Query operand: this lane's head h, channels 32t + 8*q4 + s of k-step t.
+    // ---- blocks are handed out dynamically inside the workgroup: wave w
+    // starts with block w, then each wave takes the next unclaimed block.
+    if (tid == 0) s_next = kWaves;
+    Buf<D, KC, VC> bufA, bufB;
+    int cur = wave;
+    if (cur < nblk) issue(bufA, cur);
+    __syncthreads();  // s_next initialised, query staged
     float qv[C::KSTEPS][8];
     {
         const bool real = h < G;
-        const float *qp = a.q + ((int64_t)b * a.n_q_heads + (int64_t)kvh * G + (real ? h : 0)) * D;
+        const float *qp = sq + (real ? h : 0) * D;
 #pragma unroll
         for (int t = 0; t < C::KSTEPS; ++t) {
             const float4 x0 = *reinterpret_cast<const float4 *>(qp + 32 * t + 8 * q4);
             const float4 x1 = *reinterpret_cast<const float4 *>(qp + 32 * t + 8 * q4 + 4);
-            qv[t][0] = x0.x; qv[t][1] = x0.y; qv[t][2] = x0.z; qv[t][3] = x0.w;
-            qv[t][4] = x1.x; qv[t][5] = x1.y; qv[t][6] = x1.z; qv[t][7] = x1.w;
-            if (!real)
-#pragma unroll
-                for (int s = 0; s < 8; ++s) qv[t][s] = 0.0f;
+            qv[t][0] = real ? x0.x : 0.f; qv[t][1] = real ? x0.y : 0.f;
+            qv[t][2] = real ? x0.z : 0.f; qv[t][3] = real ? x0.w : 0.f;
+            qv[t][4] = real ? x1.x : 0.f; qv[t][5] = real ? x1.y : 0.f;
+            qv[t][6] = real ? x1.z : 0.f; qv[t][7] = real ? x1.w : 0.f;
         }
     }
+    auto grab = [&]() -> int {
+        int v = 0;
+        if (lane == 0) v = atomicAdd(&s_next, 1);
+        return __builtin_amdgcn_readfirstlane(v);
+    };
+    int nxt = cur < nblk ? grab() : nblk;
+    if (nxt < nblk) issue(bufB, nxt);
+
+    // ---- query operand: power-of-two normalised hi + lo binary16 halves
     float qmaxabs = 0.0f;
 #pragma unroll
     for (int t = 0; t < C::KSTEPS; ++t)
@@ -170,101 +216,108 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
         for (int s = 0; s < 8; ++s) qmaxabs = fmaxf(qmaxabs, fabsf(qv[t][s]));
     qmaxabs = fmaxf(qmaxabs, shfl_xor(qmaxabs, 16));
     qmaxabs = fmaxf(qmaxabs, shfl_xor(qmaxabs, 32));
-    // Power-of-two normalisation keeps the binary16 query halves in range.
     const int qexp = qmaxabs > 0.0f ? ilogbf(qmaxabs) : 0;
     const float qnorm = ldexpf(1.0f, -qexp);
-    h8 qhi[C::KSTEPS], qlo[C::KSTEPS];
-    double corr_d[C::KNG];
+    h8 qhi[C::KSTEPS], qlo[C::QLO_LDS ? 1 : C::KSTEPS];
+    h8 *qlo_lds = reinterpret_cast<h8 *>(smem + kWaves * C::SLOT_WORDS * 4) +
+                  (size_t)wave * C::KSTEPS * 64 + lane;
+    float corr[C::KNG];
 #pragma unroll
-    for (int g = 0; g < C::KNG; ++g) corr_d[g] = 0.0;
+    for (int g = 0; g < C::KNG; ++g) corr[g] = 0.0f;
 #pragma unroll
     for (int t = 0; t < C::KSTEPS; ++t) {
+        float cpart = 0.0f;  // exact: at most 8 products of 11-bit values and a 5-bit bias
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
             const float x = qv[t][s] * qnorm * k_slot_factor<KC>(s);
             const _Float16 hi = (_Float16)x;
             const _Float16 lo = (_Float16)(x - (float)hi);
             qhi[t][s] = hi;
-            qlo[t][s] = lo;
-            corr_d[t / C::STEPS_PER_KGROUP] +=
-                ((double)(float)hi + (double)(float)lo) * (double)k_slot_bias<KC>(s);
+            qlo[C::QLO_LDS ? 0 : t][s] = lo;
+            cpart = fmaf((float)hi + (float)lo, k_slot_bias<KC>(s), cpart);
         }
+        if constexpr (C::QLO_LDS) qlo_lds[t * 64] = qlo[0];
+        corr[t / C::STEPS_PER_KGROUP] += cpart;
     }
-    float corr[C::KNG];
 #pragma unroll
     for (int g = 0; g < C::KNG; ++g) {
-        double c = corr_d[g];
-        c += __shfl_xor(c, 16, 64);
-        c += __shfl_xor(c, 32, 64);
-        corr[g] = (float)c;
+        corr[g] += shfl_xor(corr[g], 16);
+        corr[g] += shfl_xor(corr[g], 32);
     }
     const float c_h = a.scale_log2 * ldexpf(1.0f, qexp);
+    f4 cinit[C::KNG];  // accumulator start values: cancel the operand bias
+#pragma unroll
+    for (int g = 0; g < C::KNG; ++g) cinit[g] = f4{-corr[g], -corr[g], -corr[g], -corr[g]};
 
-    __syncthreads();  // scales staged
-    if ((r1 & (kBlockRows - 1)) != 0) {
-        // Rows past the end of the last block may never have been written:
-        // zero their V scales so that 0 * V_hat stays 0 whatever the bytes hold.
-        uint16_t *svl = sv + (nblk - 1) * C::V_BLOCK_SCALES;
-        const int valid = (int)(r1 & (kBlockRows - 1));
-        for (int i = tid; i < C::V_BLOCK_SCALES; i += kThreads) {
-            const int kq = i / (8 * C::VNG), sl = i % 8;
-            const int j = (sl >> 2) * 16 + 4 * kq + (sl & 3);
-            if (j >= valid) svl[i] = 0;
-        }
-        __syncthreads();
-    }
+    // per-wave LDS slot for one block's scales
+    uint32_t *slot = reinterpret_cast<uint32_t *>(smem) + wave * C::SLOT_WORDS;
 
     f4 O[C::CB];
 #pragma unroll
     for (int cb = 0; cb < C::CB; ++cb) O[cb] = f4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.0f;
 
-    for (int bi = wave; bi < nblk; bi += kWaves) {
-        BlockCodes<D, KC, VC> nxt;
-        const bool more = bi + kWaves < nblk;
-        if (more) load_block<D, KC, VC>(nxt, kcodes + (int64_t)(bi + kWaves) * C::K_BLOCK_BYTES,
-                                        vcodes + (int64_t)(bi + kWaves) * C::V_BLOCK_BYTES, lane);
-
+    auto process = [&](const Buf<D, KC, VC> &bf, int idx) {
+        // stage this block's scales, read them back in operand order
+        const int rows_here = nrows - idx * kBlockRows;  // > 0
+#pragma unroll
+        for (int i = 0; i < C::KS_PER_LANE; ++i)
+            if (lane + 64 * i < C::KS_WORDS) slot[lane + 64 * i] = bf.ks[i];
+#pragma unroll
+        for (int i = 0; i < C::VS_PER_LANE; ++i) {
+            const int w = lane + 64 * i;
+            if (w < C::VS_WORDS) {
+                uint32_t word = bf.vs[i];
+                if (rows_here < kBlockRows) {
+                    // rows past the end get a zero V scale, so that bytes that
+                    // were never written cannot turn 0 * V into NaN
+                    const int m = w & 3;
+                    const int j0 = (m >> 1) * 16 + 4 * (w / (4 * C::VNG)) + 2 * (m & 1);
+                    if (j0 >= rows_here) word &= 0xFFFF0000u;
+                    if (j0 + 1 >= rows_here) word &= 0x0000FFFFu;
+                }
+                slot[C::KS_WORDS + w] = word;
+            }
+        }
         // ---- scores S^T for the two 16-row tiles
-        const uint16_t *skb = sk + bi * C::K_BLOCK_SCALES;
         float S[2][4];
 #pragma unroll
         for (int tau = 0; tau < 2; ++tau) {
-            const _Float16 *ksc = reinterpret_cast<const _Float16 *>(skb + tau * 16 * C::KNG +
-                                                                      q4 * 4 * C::KNG);
+            const _Float16 *ksc = reinterpret_cast<const _Float16 *>(slot) + tau * 16 * C::KNG +
+                                  q4 * 4 * C::KNG;
             float sacc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int g = 0; g < C::KNG; ++g) {
-                f4 acc = f4{-corr[g], -corr[g], -corr[g], -corr[g]};
+                f4 acc = cinit[g];
 #pragma unroll
                 for (int st = 0; st < C::STEPS_PER_KGROUP; ++st) {
                     const int t = g * C::STEPS_PER_KGROUP + st;
-                    const h8 kop = k_operand<KC>(&cur.k[tau][is8(KC) ? 2 * t : t]);
+                    const h8 kop = k_operand<KC>(&bf.k[tau][is8(KC) ? 2 * t : t]);
                     acc = mfma16x16x32(kop, qhi[t], acc);
-                    acc = mfma16x16x32(kop, qlo[t], acc);
+                    if constexpr (C::QLO_LDS) acc = mfma16x16x32(kop, qlo_lds[t * 64], acc);
+                    else acc = mfma16x16x32(kop, qlo[t], acc);
                 }
+                if (C::KNG >= 4 && (g & 1) == 1) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) sacc[r] = fmaf(acc[r], (float)ksc[g * 4 + r], sacc[r]);
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) S[tau][r] = sacc[r] * c_h;
+            __builtin_amdgcn_sched_barrier(0);  // keep one tile's operands live at a time
         }
-        // mask rows past the end of the split
-        const int64_t rowbase = r0 + (int64_t)bi * kBlockRows;
-        if (rowbase + kBlockRows > r1) {
+        if (rows_here < kBlockRows) {
+            const int lim = rows_here - 4 * q4;  // row 16*tau + 4*q4 + r is valid iff 16*tau + r < lim
 #pragma unroll
             for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
-                    if (rowbase + 16 * tau + 4 * q4 + r >= r1) S[tau][r] = -INFINITY;
+                    if (16 * tau + r >= lim) S[tau][r] = -INFINITY;
         }
+        const h2 *svb = reinterpret_cast<const h2 *>(slot + C::KS_WORDS) + q4 * 4 * C::VNG;
 
         // ---- online softmax (log2 domain)
-        float mx = S[0][0];
-#pragma unroll
-        for (int tau = 0; tau < 2; ++tau)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) mx = fmaxf(mx, S[tau][r]);
+        float mx = fmaxf(fmaxf(fmaxf(S[0][0], S[0][1]), fmaxf(S[0][2], S[0][3])),
+                         fmaxf(fmaxf(S[1][0], S[1][1]), fmaxf(S[1][2], S[1][3])));
         mx = fmaxf(mx, shfl_xor(mx, 16));
         mx = fmaxf(mx, shfl_xor(mx, 32));
         const bool raise = mx > m_run + kRescaleThreshold;
@@ -286,29 +339,38 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
                 P[4 * tau + r] = (_Float16)p;
             }
 
+        __builtin_amdgcn_sched_barrier(0);
         // ---- O^T += V^T P^T, one 16-channel block at a time
-        const h2 *svb = reinterpret_cast<const h2 *>(sv + bi * C::V_BLOCK_SCALES + q4 * 8 * C::VNG);
 #pragma unroll
         for (int cb = 0; cb < C::CB; ++cb) {
             const int gv = cb * 16 / C::VG;
-            const h8 vop = v_operand<VC>(&cur.v[is8(VC) ? 2 * cb : cb], svb + gv * 4);
+            const h8 vop = v_operand<VC>(&bf.v[is8(VC) ? 2 * cb : cb], svb + gv * 4);
             O[cb] = mfma16x16x32(vop, P, O[cb]);
+            if ((cb & 3) == 3) __builtin_amdgcn_sched_barrier(0);  // bound the unpacked operands in flight
         }
-        if (more) cur = nxt;
+    };
+
+    while (cur < nblk) {
+        process(bufA, cur);
+        cur = nxt;
+        if (cur >= nblk) break;
+        bufA = bufB;  // register renames after full unrolling of the copy
+        nxt = grab();
+        if (nxt < nblk) issue(bufB, nxt);
     }
 
-    // ---- merge the 8 waves through LDS (reuses the scale area)
+    // ---- merge the 8 waves through LDS
     l_run += shfl_xor(l_run, 16);
     l_run += shfl_xor(l_run, 32);
     __syncthreads();
-    float *so = reinterpret_cast<float *>(smem);           // [wave][G][D]
-    float *sm = so + kWaves * G * D;                        // [wave][G]
+    constexpr int DP = D + 4;                               // padded head stride
+    float *so = reinterpret_cast<float *>(smem);           // [wave][G][DP]
+    float *sm = so + kWaves * G * DP;                       // [wave][G]
     float *sl = sm + kWaves * G;                            // [wave][G]
     if (h < G) {
 #pragma unroll
         for (int cb = 0; cb < C::CB; ++cb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) so[(wave * G + h) * D + 16 * cb + 4 * q4 + r] = O[cb][r];
+            *reinterpret_cast<f4 *>(&so[(wave * G + h) * DP + 16 * cb + 4 * q4]) = O[cb];
         if (q4 == 0) {
             sm[wave * G + h] = m_run;
             sl[wave * G + h] = l_run;
@@ -325,7 +387,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
             const float e = fast_exp2(sm[w * G + hh] - M);  // 0 for waves without rows
-            o = fmaf(e, so[(w * G + hh) * D + c], o);
+            o = fmaf(e, so[(w * G + hh) * DP + c], o);
             L = fmaf(e, sl[w * G + hh], L);
         }
         const int64_t qh = (int64_t)b * a.n_q_heads + (int64_t)kvh * G + hh;
@@ -343,61 +405,71 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
 }
 
 // Log-sum-exp merge of the splits of one (sequence, query head), 64 channels
-// per workgroup: 4 thread groups take every 4th split with independent loads,
-// the per-split weights exp2(m_s - M) are computed once into LDS.
+// per workgroup: 4 thread groups take every 4th split; each thread issues the
+// loads of 16 splits at once and folds them into a running (max, sum, output)
+// triple, then the 4 groups merge through LDS.
 template <int D>
 __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
-    extern __shared__ float sw[];  // [nsp] weights, then [4][64] partial sums
-    __shared__ float s_red[256];
+    __shared__ float s_o[4][64], s_m[4][64], s_l[4][64];
     const int hq = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
     int64_t len = a.seq_len[b];
     len = len < 0 ? 0 : (len > a.max_len ? a.max_len : len);
     const int nsp = (int)((len + a.split_rows - 1) / a.split_rows);
     if (nsp <= 1) return;  // the decode kernel wrote the output itself
     const int64_t qh = (int64_t)b * a.n_q_heads + hq;
+    const int cl = tid & 63, sg = tid >> 6, c = blockIdx.x * 64 + cl;
     const float *ml = a.part_ml + 2 * qh * a.max_splits;
-    // M = max_s m_s
-    float M = -INFINITY;
-    for (int s2 = tid; s2 < nsp; s2 += 256) M = fmaxf(M, ml[2 * s2]);
-    s_red[tid] = M;
-    __syncthreads();
-    for (int w = 128; w > 0; w >>= 1) {
-        if (tid < w) s_red[tid] = fmaxf(s_red[tid], s_red[tid + w]);
-        __syncthreads();
-    }
-    M = s_red[0];
-    __syncthreads();
-    float L = 0.0f;
-    for (int s2 = tid; s2 < nsp; s2 += 256) {
-        const float w = fast_exp2(ml[2 * s2] - M);
-        sw[s2] = w;
-        L = fmaf(w, ml[2 * s2 + 1], L);
-    }
-    s_red[tid] = L;
-    __syncthreads();
-    for (int w = 128; w > 0; w >>= 1) {
-        if (tid < w) s_red[tid] += s_red[tid + w];
-        __syncthreads();
-    }
-    L = s_red[0];
-    __syncthreads();
-    const int c = blockIdx.x * 64 + (tid & 63), sg = tid >> 6;
     const float *po = a.part_o + qh * a.max_splits * D + c;
-    float o = 0.0f;
-#pragma unroll 8
-    for (int s2 = sg; s2 < nsp; s2 += 4) o = fmaf(sw[s2], po[(int64_t)s2 * D], o);
-    s_red[tid] = o;
+    constexpr int U = 16;
+    float M = -INFINITY, o = 0.0f, L = 0.0f;
+    for (int s0 = sg; s0 < nsp; s0 += 4 * U) {
+        float mv[U], lv[U], ov[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int s2 = s0 + 4 * u;
+            const bool ok = s2 < nsp;
+            mv[u] = ok ? ml[2 * s2] : -INFINITY;
+            lv[u] = ok ? ml[2 * s2 + 1] : 0.0f;
+            ov[u] = ok ? po[(int64_t)s2 * D] : 0.0f;
+        }
+        float mb = M;
+#pragma unroll
+        for (int u = 0; u < U; ++u) mb = fmaxf(mb, mv[u]);  // finite: split s0 exists
+        const float sc = fast_exp2(M - mb);                  // 0 on the first chunk
+        o *= sc;
+        L *= sc;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const float e = fast_exp2(mv[u] - mb);
+            o = fmaf(e, ov[u], o);
+            L = fmaf(e, lv[u], L);
+        }
+        M = mb;
+    }
+    s_o[sg][cl] = o;
+    s_m[sg][cl] = M;
+    s_l[sg][cl] = L;
     __syncthreads();
-    if (sg == 0)
-        a.out[qh * D + c] = (s_red[tid] + s_red[tid + 64] + s_red[tid + 128] + s_red[tid + 192]) / L;
+    if (sg == 0) {
+        float Mt = s_m[0][cl];
+#pragma unroll
+        for (int g = 1; g < 4; ++g) Mt = fmaxf(Mt, s_m[g][cl]);
+        float on = 0.0f, Ln = 0.0f;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const float e = fast_exp2(s_m[g][cl] - Mt);  // 0 for a group without splits
+            on = fmaf(e, s_o[g][cl], on);
+            Ln = fmaf(e, s_l[g][cl], Ln);
+        }
+        a.out[qh * D + c] = on / Ln;
+    }
 }
 
 template <int D, int KC, int VC>
 hipError_t launch_typed(const DecodeArgs &a, hipStream_t s) {
     using C = Cfg<D, KC, VC>;
-    const size_t scale_lds = (size_t)(a.split_rows / kBlockRows) *
-                             (C::K_BLOCK_SCALES + C::V_BLOCK_SCALES) * sizeof(uint16_t);
-    const size_t merge_lds = (size_t)kWaves * a.gqa * (D + 2) * sizeof(float);
+    const size_t scale_lds = (size_t)C::QOFF + (size_t)a.gqa * D * sizeof(float);
+    const size_t merge_lds = (size_t)kWaves * a.gqa * (D + 4 + 2) * sizeof(float);
     const size_t lds = scale_lds > merge_lds ? scale_lds : merge_lds;
     const dim3 grid((unsigned)a.max_splits, (unsigned)a.k.n_kv_heads, (unsigned)a.n_seqs);
     if (lds > 65536) {
@@ -408,8 +480,7 @@ hipError_t launch_typed(const DecodeArgs &a, hipStream_t s) {
     decode_kernel<D, KC, VC><<<grid, dim3(kThreads), lds, s>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.max_splits <= 1) return e;
-    combine_kernel<D><<<dim3(D / 64, (unsigned)a.n_q_heads, (unsigned)a.n_seqs), dim3(256),
-                        (size_t)a.max_splits * sizeof(float), s>>>(a);
+    combine_kernel<D><<<dim3(D / 64, (unsigned)a.n_q_heads, (unsigned)a.n_seqs), dim3(256), 0, s>>>(a);
     return hipGetLastError();
 }
 

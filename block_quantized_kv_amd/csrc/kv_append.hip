@@ -38,8 +38,9 @@ __device__ __forceinline__ void store_codes(uint8_t *blk, int d, int j, int c0, 
     } else {
         // V role: each channel lives in a different lane word, shared with
         // seven other rows.  Bytes are stored directly; a nibble is replaced
-        // with an atomic xor of (old ^ new) << shift, which leaves the other
-        // nibbles of the word untouched whatever other threads do to them.
+        // with an atomic and (clear) followed by an atomic or (set) on its
+        // word, which leave the other nibbles untouched whatever other threads
+        // do to them (one thread's two atomics to one address stay in order).
         for (int s = 0; s < 8; ++s) {
             const CodePos p = v_code_pos(CODEC, d, j, c0 + s);
             if constexpr (is8(CODEC)) {
@@ -48,9 +49,9 @@ __device__ __forceinline__ void store_codes(uint8_t *blk, int d, int j, int c0, 
                 const uint32_t nib = CODEC == Q4_0 ? (uint32_t)(q[s] + 8) : ((uint32_t)q[s] & 0xFu);
                 uint32_t *word = reinterpret_cast<uint32_t *>(blk + (p.byte & ~3));
                 const int sh = 8 * (p.byte & 3) + p.shift;
-                const uint32_t old = (*word >> sh) & 0xFu;  // this nibble is ours alone
-                const uint32_t delta = (old ^ nib) << sh;
-                if (delta) atomicXor(word, delta);
+                // clear then set this nibble; neither needs the old value back
+                atomicAnd(word, ~(0xFu << sh));
+                atomicOr(word, nib << sh);
             }
         }
     }
@@ -71,6 +72,9 @@ __device__ __forceinline__ void append_plane(const PlaneView &pl, const float *x
     const int chunk = (int)(tid % chunks);
     const int tok = (int)(row / pl.n_kv_heads);
     const int head = (int)(row % pl.n_kv_heads);
+    // destination first: its loads overlap the row's
+    const int32_t sq = live ? seq_idx[tok] : 0;
+    const int64_t pos = live ? pos_arr[tok] : 0;
 
     float x[8];
     if (live) {
@@ -97,9 +101,6 @@ __device__ __forceinline__ void append_plane(const PlaneView &pl, const float *x
         q[s] = (int)r;
     }
     if (!live) return;
-
-    const int32_t sq = seq_idx[tok];
-    const int64_t pos = pos_arr[tok];
     if (sq < 0 || sq >= pl.n_seqs || pos < 0 || pos >= pl.capacity) {
         if (dev_status) *dev_status = 3;  // KVQ_ERANGE
         return;

@@ -28,24 +28,26 @@ __device__ __forceinline__ f4 mfma16x16x32_bf16(bf8 a, bf8 b, f4 c) {
 // ---- 4-bit codes -------------------------------------------------------------
 // A word holds 8 nibbles in slot order (nibble positions 0,4,1,5,2,6,3,7 for
 // slots 0..7).  With the binary16 pattern 0x6400 (= 1024.0, unit fraction step)
-// or-ed in, the nibble n in the low 4 fraction bits reads as 1024 + n and a
+// merged in, a nibble n in the low 4 fraction bits reads as 1024 + n and a
 // nibble in fraction bits 4..7 reads as 1024 + 16 n; both are exact.
+// n is the offset-8 code q + 8: q4_0 stores it; Q4_G64 stores q & 0xF
+// (two's complement), and q + 8 = (q & 0xF) ^ 8.  One v_bitop3 per pair does
+// mask, sign flip and merge: f(w, M, K) = M ? (w ^ K) : K with K holding the
+// magic outside M and the flip bit inside it.
 // Result: slots (0,1) = 1024+n, (2,3) = 1024+16n, (4,5) = 1024+n, (6,7) = 1024+16n.
+template <int CODEC>
 __device__ __forceinline__ u4 nib_magic(uint32_t w) {
+    constexpr uint32_t flip = CODEC == Q4_G64 ? 0x8u : 0x0u;
+    constexpr uint32_t M_LO = 0x000F000Fu, M_HI = 0x00F000F0u;
+    constexpr uint32_t K_LO = 0x64006400u | (flip * 0x00010001u);
+    constexpr uint32_t K_HI = 0x64006400u | (flip * 0x00100010u);
     const uint32_t w8 = w >> 8;
     u4 r;
-    r.x = (w & 0x000F000Fu) | 0x64006400u;
-    r.y = (w & 0x00F000F0u) | 0x64006400u;
-    r.z = (w8 & 0x000F000Fu) | 0x64006400u;
-    r.w = (w8 & 0x00F000F0u) | 0x64006400u;
+    r.x = __builtin_amdgcn_bitop3_b32(w, M_LO, K_LO, 0x6A);
+    r.y = __builtin_amdgcn_bitop3_b32(w, M_HI, K_HI, 0x6A);
+    r.z = __builtin_amdgcn_bitop3_b32(w8, M_LO, K_LO, 0x6A);
+    r.w = __builtin_amdgcn_bitop3_b32(w8, M_HI, K_HI, 0x6A);
     return r;
-}
-
-// Offset-8 nibble n of a 4-bit word.  q4_0 stores q + 8 already; Q4_G64 stores
-// q & 0xF (two's complement), and q + 8 = (q & 0xF) ^ 8.
-template <int CODEC>
-__device__ __forceinline__ uint32_t to_offset8(uint32_t w) {
-    return CODEC == Q4_G64 ? (w ^ 0x88888888u) : w;
 }
 
 // ---- 8-bit codes -------------------------------------------------------------
@@ -67,7 +69,7 @@ __device__ __forceinline__ h8 k_operand(const uint32_t *w) {
         const u4 r = {a.x, a.y, b.x, b.y};
         return __builtin_bit_cast(h8, r);
     } else {
-        return __builtin_bit_cast(h8, nib_magic(to_offset8<CODEC>(w[0])));
+        return __builtin_bit_cast(h8, nib_magic<CODEC>(w[0]));
     }
 }
 
@@ -96,7 +98,7 @@ __device__ __forceinline__ h8 v_operand(const uint32_t *w, const h2 *dq2) {
         v2 = (as_h2(b.x) + bias) * dq2[2];
         v3 = (as_h2(b.y) + bias) * dq2[3];
     } else {
-        const u4 r = nib_magic(to_offset8<CODEC>(w[0]));
+        const u4 r = nib_magic<CODEC>(w[0]);
         const h2 b_lo = {(_Float16)-1032.0f, (_Float16)-1032.0f};
         const h2 sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
         const h2 b_hi = {(_Float16)-72.0f, (_Float16)-72.0f};
