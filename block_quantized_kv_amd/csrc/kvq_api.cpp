@@ -211,6 +211,8 @@ kvq_status kvq_attend_prefill(const kvq_layer *L, const uint16_t *q_bf16, int32_
     if (pos0 < 0 || pos0 + n_tokens > L->k.capacity)
         return fail(KVQ_ERANGE, "chunk [%lld, %lld) outside capacity %lld", (long long)pos0,
                     (long long)(pos0 + n_tokens), (long long)L->k.capacity);
+    if (pos0 + n_tokens > (int64_t)INT32_MAX)
+        return fail(KVQ_EUNSUPPORTED, "prefill positions beyond 2^31 rows");
     if (n_q_heads <= 0 || n_q_heads % L->k.n_kv_heads != 0)
         return fail(KVQ_EINVAL, "n_q_heads %d not a multiple of n_kv_heads %d", n_q_heads,
                     L->k.n_kv_heads);

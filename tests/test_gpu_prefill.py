@@ -1,0 +1,85 @@
+"""GPU chunked-prefill parity against the oracle (binary64 causal attention over
+the oracle's own quantization of the same rows; bf16 queries widened exactly).
+
+Bar: max|gpu - oracle| / max|oracle| <= 1e-2, the prefill tolerance of the
+workload statement (the matrix cores see K_hat, V_hat and P rounded to bf16).
+Covered: the tiny prefill enumerated in full, ragged prefix/chunk lengths,
+every codec pair, head_dim 64/128/256, several GQA ratios, a chunk at
+position 0, and the 2048-token chunk over a 32768-token prefix on 256
+sampled (token, head) rows including the first and last 64 tokens.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from block_quantized_kv_amd import Layer, kvq_append, kvq_attend_prefill
+from gpu_helpers import append_rows, rel_err
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-2
+CODECS = ["q8_0", "q4_0", "q4_g64"]
+
+
+def _run(gpu, kc, vc, d, hq, hkv, P, T, seed=0, sample=None, cap_extra=0):
+    q, k, v = workloads.prefill_inputs(gpu, seed_layer=seed, prefix=P, chunk=T, n_q_heads=hq,
+                                       n_kv_heads=hkv, head_dim=d)
+    cap = (P + T + 31) // 32 * 32 + cap_extra
+    layer = Layer.create(kc, vc, d, hkv, 1, cap, device=gpu)
+    append_rows(layer, k, v, 0, 0)                      # prefix and chunk rows
+    out = kvq_attend_prefill(layer, q, 0, P, 1.0 / np.sqrt(d)).cpu().numpy()
+    kh = oracle.quant_dequant(kc, k.cpu().numpy().transpose(1, 0, 2).copy())
+    vh = oracle.quant_dequant(vc, v.cpu().numpy().transpose(1, 0, 2).copy())
+    qn = q.float().cpu().numpy()
+    if sample is None:
+        ref = oracle.attend_prefill(qn, kh, vh, P, 1.0 / np.sqrt(d))
+        got = out
+    else:
+        toks, heads = sample
+        ref = oracle.attend_prefill(qn, kh, vh, P, 1.0 / np.sqrt(d), tokens=toks, heads=heads)
+        got = out[toks, heads]
+    err = rel_err(got, ref)
+    assert np.isfinite(out).all()
+    assert err <= TOL, (kc, vc, d, hq, hkv, P, T, err)
+    return err
+
+
+def test_tiny_prefill_enumerated(gpu):
+    _run(gpu, "q8_0", "q4_0", 128, 32, 8, 64, 16)
+
+
+@pytest.mark.parametrize("kc", CODECS)
+@pytest.mark.parametrize("vc", CODECS)
+def test_codec_pairs(gpu, kc, vc):
+    d = {"q8_0": 64, "q4_0": 128, "q4_g64": 256}[vc]
+    _run(gpu, kc, vc, d, 8, 2, 100, 37, seed=CODECS.index(kc) * 3 + CODECS.index(vc))
+
+
+@pytest.mark.parametrize("P,T", [(0, 1), (0, 70), (1, 1), (31, 33), (63, 65), (200, 300), (1000, 129)])
+def test_ragged_lengths(gpu, P, T):
+    _run(gpu, "q4_g64", "q8_0", 128, 6, 1, P, T, seed=P + T)
+
+
+@pytest.mark.parametrize("gqa", [1, 3, 4, 16])
+def test_gqa_ratios(gpu, gqa):
+    _run(gpu, "q8_0", "q4_0", 64, 2 * gqa, 2, 90, 50, seed=gqa)
+
+
+def test_capacity_slack_rows_ignored(gpu):
+    # capacity beyond the chunk: never-written rows after it must not matter
+    _run(gpu, "q8_0", "q4_0", 128, 8, 2, 40, 30, cap_extra=64)
+
+
+def test_workload_prefill_2048_over_32768(gpu):
+    """The chunked-prefill workload (q8_0 K / q4_0 V, 32/8 heads, d 128) on
+    256 sampled rows: the first and last 64 tokens (cycling through the heads)
+    and 128 random (token, head) pairs."""
+    W = workloads.PREFILL
+    P, T, hq = W["prefix"], W["chunk"], W["n_q_heads"]
+    rng = np.random.default_rng(5)
+    edge = list(range(64)) + list(range(T - 64, T))
+    toks = edge + list(rng.integers(0, T, 128))
+    heads = [t % hq for t in edge] + list(rng.integers(0, hq, 128))
+    _run(gpu, W["k_codec"], W["v_codec"], W["head_dim"], hq, W["n_kv_heads"], P, T,
+         sample=(np.array(toks), np.array(heads)))
