@@ -11,6 +11,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkvq.so")
 SOURCES = ["kvq_api.cpp", "kv_append.hip", "attn_decode.hip", "attn_prefill.hip"]
 ARCH = "gfx950"
+PER_SOURCE_FLAGS: dict = {}
 
 
 def hipcc() -> str:
@@ -24,16 +25,19 @@ def build(verbose: bool = False) -> str:
     """Compile every source with hipcc and link libkvq.so in place."""
     objdir = os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
-    common = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",
+    common = ["-O3", "-fPIC", "-std=c++20", f"--offload-arch={ARCH}",
               "-I", os.path.join(ROOT, "include"), "-I", CSRC,
               # no packed fp32 arithmetic anywhere in the device code
               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+              # LDS and global words are re-read through other types
+              "-fno-strict-aliasing",
               "-Wall", "-Wno-unused-function"]
     objs = []
     for src in SOURCES:
         obj = os.path.join(objdir, src.replace(".", "_") + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmd = [hipcc()] + common + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+        extra = PER_SOURCE_FLAGS.get(src, [])
+        cmd = [hipcc()] + common + extra + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         subprocess.run(cmd, check=True, stderr=None if verbose else subprocess.PIPE)

@@ -7,7 +7,7 @@
 //   rows j < len_b of kv-head h / gqa.
 //
 // Design (one workgroup = 8 waves = one split of `split_rows` rows of one
-// (sequence, kv-head); each wave takes every 8th 32-row block of the split):
+// (sequence, kv-head); the waves share the split's 32-row blocks):
 //  * The GQA group (<= 16 query heads) is the N side of 16x16x32 f16 matrix
 //    products, so every K/V byte is read once per kv-head:
 //      S^T[row][head] = K[row][:] . Q'[:][head]   (A = K codes, B = query)
@@ -17,27 +17,36 @@
 //    V-role block layout puts each lane's eight V rows where its probabilities
 //    are, so no data moves between the two products.
 //  * K codes enter the matrix cores as exact binary16 "1024 + n" / "1152 + b"
-//    values (two masks, a shift or a byte permute per word); the constant
-//    bias is cancelled by starting the accumulator at -sum(query * bias).
-//    The query is scaled by a power of two and split into hi + lo binary16
-//    halves (two products), so the score keeps ~22 bits.  K group scales are
-//    applied in fp32 to each group's partial dot product.
+//    values (one bit-select per pair, or a byte permute); the constant bias is
+//    cancelled by starting the accumulator at -sum(query * bias).  The query
+//    is scaled by a power of two and split into hi + lo binary16 halves (two
+//    products), so the score keeps ~22 bits.  K group scales are applied in
+//    fp32 to each group's partial dot product.  Both 16-row tiles of a block
+//    walk the channel steps together (two independent accumulator chains).
 //  * V enters as binary16 code * dq (one rounding, exact for subnormal dq);
 //    probabilities enter as binary16.  Statistics and sums are fp32.
 //  * Online softmax in log2 units; the running max is only raised when a
 //    block exceeds it by more than 8 (probabilities stay <= 256), so the
-//    64-register rescale of O is rare.
-//  * Each wave prefetches its next 32-row block (code words and a slice of
-//    the block's scales) into registers while it computes the current one;
-//    the scales go through a per-wave LDS slot to reach operand order.
-//    Blocks are handed out dynamically inside the workgroup (LDS counter), so
-//    the 8 waves finish together.
-//  * The workgroup's query rows are staged once in LDS (coalesced), so the
-//    many workgroups of one kv-head do not all hammer the same few lines.
+//    rescale of O is rare.
+//  * Streaming: blocks travel HBM -> LDS by buffer-to-LDS DMA, which holds no
+//    registers while in flight.  Each wave owns a ring of NS block slots in
+//    LDS (byte layout = the cache's); it copies the oldest slot into
+//    registers, immediately refills that slot with the block NS*8 further on
+//    and computes from the registers, so NS blocks per wave are always on
+//    their way.  The compiler cannot see which LDS bytes a DMA writes (it
+//    would wait for every DMA before any LDS read), so the slot reads are
+//    hand-issued with an explicit wait for exactly the DMAs of that slot.
+//    Every DMA is issued unconditionally: one past the end of the split is
+//    cut off by the buffer range check and touches no memory.
+//  * The query operand (hi/lo halves for every channel step) and the bias
+//    corrections are prepared once per workgroup, each wave taking one channel
+//    step, and shared through LDS.
 //  * The 8 waves merge through LDS; each workgroup writes one partial
 //    (unnormalized O, max, sum) per query head, or the final output when the
 //    sequence fits in one split; combine_kernel merges the splits
 //    (log-sum-exp) with many partial loads in flight at once.
+#include <utility>
+
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -47,7 +56,12 @@ namespace {
 
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
+constexpr int kLdsBytes = 160 * 1024;  // per workgroup on gfx950
 constexpr float kRescaleThreshold = 8.0f;
+
+// number of DMA instructions that copy a region of B bytes (1 KB per dwordx4
+// DMA, 256 B per dword DMA, a lane-masked dword DMA for a shorter tail)
+constexpr int dma_count(int B) { return B / 1024 + (B % 1024) / 256 + ((B % 256) ? 1 : 0); }
 
 template <int D, int KC, int VC>
 struct Cfg {
@@ -69,74 +83,184 @@ struct Cfg {
     static constexpr int V_BLOCK_BYTES = block_code_bytes(VC, D);
     static constexpr int K_BLOCK_SCALES = block_scales(KC, D);
     static constexpr int V_BLOCK_SCALES = block_scales(VC, D);
-    static constexpr int KS_WORDS = K_BLOCK_SCALES / 2;  // 32-bit words of K scales per block
-    static constexpr int VS_WORDS = V_BLOCK_SCALES / 2;
-    static constexpr int KS_PER_LANE = (KS_WORDS + 63) / 64;
-    static constexpr int VS_PER_LANE = (VS_WORDS + 63) / 64;
-    // head_dim 256: the query's low half lives in a per-wave LDS copy (read
-    // once per k-step) to leave registers for two blocks in flight
-    static constexpr bool QLO_LDS = D == 256;
-    static constexpr int SLOT_WORDS = KS_WORDS + VS_WORDS;
-    static constexpr int QLO_BYTES = QLO_LDS ? KSTEPS * 64 * 16 : 0;  // per wave
-    static constexpr int QOFF = kWaves * (SLOT_WORDS * 4 + QLO_BYTES);  // staged query rows
+    // one block slot in LDS: [K codes][V codes][K scales][V scales]
+    static constexpr int SL_K = 0;
+    static constexpr int SL_V = SL_K + K_BLOCK_BYTES;
+    static constexpr int SL_KS = SL_V + V_BLOCK_BYTES;
+    static constexpr int SL_VS = SL_KS + 2 * K_BLOCK_SCALES;
+    static constexpr int SLOT = SL_VS + 2 * V_BLOCK_SCALES;
+    static constexpr int N_DMA = dma_count(K_BLOCK_BYTES) + dma_count(V_BLOCK_BYTES) +
+                                 dma_count(2 * K_BLOCK_SCALES) + dma_count(2 * V_BLOCK_SCALES);
+    // per-lane scale words of one block: K (4 rows x KNG groups per tile),
+    // V (8 rows x VNG groups)
+    static constexpr int KS_LANE_BYTES = 8 * KNG;   // per tile
+    static constexpr int VS_LANE_BYTES = 16 * VNG;
+    // head_dim 256: the query operand is read from LDS at every channel step,
+    // leaving the registers to the output accumulator and one block
+    static constexpr bool Q_LDS = D == 256;
+    // LDS layout (bytes); the final merge reuses it
+    static constexpr int OFF_QOP = 0;                                 // [KSTEPS][hi,lo][64 lanes] h8
+    static constexpr int OFF_TMAX = OFF_QOP + KSTEPS * 2 * 64 * 16;   // [KSTEPS][16] fp32
+    static constexpr int OFF_CORR = OFF_TMAX + KSTEPS * 16 * 4;       // [KSTEPS][16] fp32
+    static constexpr int OFF_CNT = OFF_CORR + KSTEPS * 16 * 4;        // block hand-out counter
+    static constexpr int OFF_SLOTS = OFF_CNT + 16;                    // [wave][NS] slots
+    static constexpr int NS_FIT = (kLdsBytes - OFF_SLOTS) / (kWaves * SLOT);
+    static constexpr int NS = NS_FIT > 3 ? 3 : NS_FIT;
+    static_assert(NS >= 1, "one block slot per wave must fit in LDS");
+    static_assert((NS - 1) * N_DMA <= 63, "DMAs in flight exceed the wait counter");
+    static_assert(SL_V % 16 == 0 && SL_KS % 16 == 0 && SL_VS % 16 == 0 && SLOT % 16 == 0, "slot alignment");
+    static_assert((NS - 1) * SLOT + SLOT <= 65535, "slot offsets fit the DS immediate");
+    static constexpr int LDS_STREAM = OFF_SLOTS + kWaves * NS * SLOT;
 };
 
-// Loads the LB bytes lane `lane` owns in a chunk-major region into words.
+// Raw buffer descriptor (base in SGPRs, byte range checked by the hardware).
+// The whole byte offset goes in the VGPR offset, which the range check covers:
+// a DMA of a block past the end of the split touches no memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
+}
+
+struct Streams {
+    __amdgpu_buffer_rsrc_t kc, vc, ks, vs;
+};
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Copies B bytes at byte goff of stream r to LDS at dst (a plain copy; lane
+// l carries bytes [16 l, 16 l + 16) of each 1 KB piece).
+template <int B>
+__device__ __forceinline__ void dma_region(__amdgpu_buffer_rsrc_t r, uint32_t goff, unsigned char *dst, int lane) {
+    constexpr int N16 = B / 1024, N4 = (B % 1024) / 256, TAIL = B % 256;
+#pragma unroll
+    for (int c = 0; c < N16; ++c)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(dst + c * 1024), 16, goff + c * 1024 + lane * 16, 0, 0, 0);
+#pragma unroll
+    for (int c = 0; c < N4; ++c)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(dst + N16 * 1024 + c * 256), 4,
+                                                 goff + N16 * 1024 + c * 256 + lane * 4, 0, 0, 0);
+    if constexpr (TAIL != 0) {
+        static_assert(TAIL % 4 == 0, "scale regions are whole words");
+        if (lane * 4 < TAIL)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(dst + N16 * 1024 + N4 * 256), 4,
+                                                     goff + N16 * 1024 + N4 * 256 + lane * 4, 0, 0, 0);
+    }
+}
+
+template <int D, int KC, int VC>
+__device__ __forceinline__ void dma_block(const Streams &st, int idx, unsigned char *slot, int lane) {
+    using C = Cfg<D, KC, VC>;
+    dma_region<C::K_BLOCK_BYTES>(st.kc, (uint32_t)idx * C::K_BLOCK_BYTES, slot + C::SL_K, lane);
+    dma_region<C::V_BLOCK_BYTES>(st.vc, (uint32_t)idx * C::V_BLOCK_BYTES, slot + C::SL_V, lane);
+    dma_region<2 * C::K_BLOCK_SCALES>(st.ks, (uint32_t)idx * C::K_BLOCK_SCALES * 2, slot + C::SL_KS, lane);
+    dma_region<2 * C::V_BLOCK_SCALES>(st.vs, (uint32_t)idx * C::V_BLOCK_SCALES * 2, slot + C::SL_VS, lane);
+}
+
+// ---- hand-issued LDS reads (no wait; see lds_wait).  `off` must fold to a
+// constant after inlining and unrolling (it becomes the DS immediate).
+__device__ __forceinline__ void ds_rd(u4 &x, uint32_t a, int off) {
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(x) : "v"(a), "i"(off) : "memory");
+}
+__device__ __forceinline__ void ds_rd(u2 &x, uint32_t a, int off) {
+    asm volatile("ds_read_b64 %0, %1 offset:%2" : "=v"(x) : "v"(a), "i"(off) : "memory");
+}
+__device__ __forceinline__ void ds_rd(uint32_t &x, uint32_t a, int off) {
+    asm volatile("ds_read_b32 %0, %1 offset:%2" : "=v"(x) : "v"(a), "i"(off) : "memory");
+}
+// Reads the LB bytes a lane owns at byte offset `off` of an LDS copy of a
+// chunk-major region into words (a16/a8/a4: region base + lane * width).
 template <int LB>
-__device__ __forceinline__ void load_lane_words(const uint8_t *region, int lane, uint32_t *w) {
+__device__ __forceinline__ void ds_rd_lane(uint32_t *w, uint32_t a16, uint32_t a8, uint32_t a4, int off) {
     constexpr int W = chunk_width(LB);
     if constexpr (W == 16) {
 #pragma unroll
         for (int c = 0; c < LB / 16; ++c) {
-            const u4 v = *reinterpret_cast<const u4 *>(region + c * 1024 + lane * 16);
+            u4 v;
+            ds_rd(v, a16, off + c * 1024);
             w[4 * c + 0] = v.x; w[4 * c + 1] = v.y; w[4 * c + 2] = v.z; w[4 * c + 3] = v.w;
         }
     } else if constexpr (W == 8) {
-        const u2 v = *reinterpret_cast<const u2 *>(region + lane * 8);
+        u2 v;
+        ds_rd(v, a8, off);
         w[0] = v.x; w[1] = v.y;
     } else {
-        static_assert(W == 4, "lane chunk width");
-        w[0] = *reinterpret_cast<const uint32_t *>(region + lane * 4);
+        ds_rd(w[0], a4, off);
     }
 }
+// Reads NB contiguous bytes (a multiple of 8) at a + off into words.
+template <int NB>
+__device__ __forceinline__ void ds_rd_span(uint32_t *w, uint32_t a, int off) {
+#pragma unroll
+    for (int c = 0; c < NB / 16; ++c) {
+        u4 v;
+        ds_rd(v, a, off + c * 16);
+        w[4 * c + 0] = v.x; w[4 * c + 1] = v.y; w[4 * c + 2] = v.z; w[4 * c + 3] = v.w;
+    }
+    if constexpr (NB % 16 == 8) {
+        u2 v;
+        ds_rd(v, a, off + (NB / 16) * 16);
+        w[4 * (NB / 16)] = v.x;
+        w[4 * (NB / 16) + 1] = v.y;
+    }
+}
+__device__ __forceinline__ void ds_wr(uint32_t a, uint32_t x, int off) {
+    asm volatile("ds_write_b32 %0, %1 offset:%2" ::"v"(a), "v"(x), "i"(off) : "memory");
+}
+__device__ __forceinline__ void ds_wr(uint32_t a, u4 x, int off) {
+    asm volatile("ds_write_b128 %0, %1 offset:%2" ::"v"(a), "v"(x), "i"(off) : "memory");
+}
+// Atomic add on an LDS word, returning the old value (waits for it).
+__device__ __forceinline__ uint32_t ds_add_rtn(uint32_t a, uint32_t x, int off) {
+    uint32_t r;
+    asm volatile("ds_add_rtn_u32 %0, %1, %2 offset:%3\n\ts_waitcnt lgkmcnt(0)" : "=v"(r) : "v"(a), "v"(x), "i"(off) : "memory");
+    return r;
+}
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS accesses,
+// not for its memory loads (a __syncthreads would also wait for every DMA).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// Everything one wave needs from HBM for one 32-row block: its K and V code
-// words and one slice of the block's K and V scales (the whole wave loads each
-// block's scales with one coalesced pass, then stages them in its own LDS slot
-// to read them back in operand order).
+// Completes the hand-issued LDS reads: waits for them and makes every word
+// read so far a fresh value for the compiler (N words).
+template <int N>
+__device__ __forceinline__ void lds_wait(uint32_t *w) {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < N; ++i) asm volatile("" : "+v"(w[i]));
+}
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"i"(N) : "memory");
+}
+
+// One block's words for one lane, copied out of its LDS slot.
 template <int D, int KC, int VC>
-struct Buf {
+struct Payload {
     using C = Cfg<D, KC, VC>;
-    uint32_t k[2][C::K_WORDS];
-    uint32_t v[C::V_WORDS];
-    uint32_t ks[C::KS_PER_LANE];
-    uint32_t vs[C::VS_PER_LANE];
+    static constexpr int NW = 2 * C::K_WORDS + C::V_WORDS + C::KS_LANE_BYTES / 2 + C::VS_LANE_BYTES / 4;
+    uint32_t w[NW];
+    __device__ __forceinline__ uint32_t *k(int tau) { return w + tau * C::K_WORDS; }
+    __device__ __forceinline__ uint32_t *v() { return w + 2 * C::K_WORDS; }
+    __device__ __forceinline__ uint32_t *ks(int tau) { return w + 2 * C::K_WORDS + C::V_WORDS + tau * (C::KS_LANE_BYTES / 4); }
+    __device__ __forceinline__ uint32_t *vs() { return w + 2 * C::K_WORDS + C::V_WORDS + C::KS_LANE_BYTES / 2; }
 };
 
 template <int D, int KC, int VC>
-__device__ __forceinline__ void load_buf(Buf<D, KC, VC> &bf, const uint8_t *kblk, const uint8_t *vblk,
-                                         const uint32_t *ksb, const uint32_t *vsb, int lane) {
+__device__ __forceinline__ void read_slot(Payload<D, KC, VC> &pl, uint32_t a16, uint32_t a8, uint32_t a4,
+                                          uint32_t aks, uint32_t avs, int soff) {
     using C = Cfg<D, KC, VC>;
-    load_lane_words<C::K_LB>(kblk, lane, bf.k[0]);
-    load_lane_words<C::K_LB>(kblk + C::K_TILE_BYTES, lane, bf.k[1]);
-    load_lane_words<C::V_LB>(vblk, lane, bf.v);
-#pragma unroll
-    for (int i = 0; i < C::KS_PER_LANE; ++i) {
-        const int w = lane + 64 * i;
-        bf.ks[i] = w < C::KS_WORDS ? ksb[w] : 0u;
-    }
-#pragma unroll
-    for (int i = 0; i < C::VS_PER_LANE; ++i) {
-        const int w = lane + 64 * i;
-        bf.vs[i] = w < C::VS_WORDS ? vsb[w] : 0u;
-    }
+    ds_rd_lane<C::K_LB>(pl.k(0), a16, a8, a4, soff + C::SL_K);
+    ds_rd_lane<C::K_LB>(pl.k(1), a16, a8, a4, soff + C::SL_K + C::K_TILE_BYTES);
+    ds_rd_lane<C::V_LB>(pl.v(), a16, a8, a4, soff + C::SL_V);
+    ds_rd_span<C::KS_LANE_BYTES>(pl.ks(0), aks, soff + C::SL_KS);
+    ds_rd_span<C::KS_LANE_BYTES>(pl.ks(1), aks, soff + C::SL_KS + 32 * C::KNG);
+    ds_rd_span<C::VS_LANE_BYTES>(pl.vs(), avs, soff + C::SL_VS);
+    lds_wait<Payload<D, KC, VC>::NW>(pl.w);
 }
 
 template <int D, int KC, int VC>
 __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     using C = Cfg<D, KC, VC>;
+    constexpr int NS = C::NS;
     extern __shared__ __align__(16) unsigned char smem[];
-    __shared__ int s_next;
 
     const int sp = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
     int64_t len = a.seq_len[b];
@@ -153,158 +277,161 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     const int nblk = (nrows + kBlockRows - 1) / kBlockRows;
     const int64_t blk0 = r0 / kBlockRows;
 
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane & 15, q4 = lane >> 4;
     const int G = a.gqa;
 
     const int64_t head_lin = (int64_t)b * a.k.n_kv_heads + kvh;
-    const uint8_t *kcodes = a.k.codes + head_lin * a.k.head_code_stride + blk0 * C::K_BLOCK_BYTES;
-    const uint8_t *vcodes = a.v.codes + head_lin * a.v.head_code_stride + blk0 * C::V_BLOCK_BYTES;
-    const uint32_t *kscales = reinterpret_cast<const uint32_t *>(
-        a.k.scales + head_lin * a.k.head_scale_stride + blk0 * C::K_BLOCK_SCALES);
-    const uint32_t *vscales = reinterpret_cast<const uint32_t *>(
-        a.v.scales + head_lin * a.v.head_scale_stride + blk0 * C::V_BLOCK_SCALES);
-    auto issue = [&](Buf<D, KC, VC> &bf, int idx) {
-        load_buf<D, KC, VC>(bf, kcodes + (int64_t)idx * C::K_BLOCK_BYTES,
-                            vcodes + (int64_t)idx * C::V_BLOCK_BYTES,
-                            kscales + (int64_t)idx * C::KS_WORDS, vscales + (int64_t)idx * C::VS_WORDS,
-                            lane);
-    };
+    Streams st;
+    st.kc = make_rsrc(a.k.codes + head_lin * a.k.head_code_stride + blk0 * C::K_BLOCK_BYTES,
+                      (uint32_t)nblk * C::K_BLOCK_BYTES);
+    st.vc = make_rsrc(a.v.codes + head_lin * a.v.head_code_stride + blk0 * C::V_BLOCK_BYTES,
+                      (uint32_t)nblk * C::V_BLOCK_BYTES);
+    st.ks = make_rsrc(a.k.scales + head_lin * a.k.head_scale_stride + blk0 * C::K_BLOCK_SCALES,
+                      (uint32_t)nblk * C::K_BLOCK_SCALES * 2);
+    st.vs = make_rsrc(a.v.scales + head_lin * a.v.head_scale_stride + blk0 * C::V_BLOCK_SCALES,
+                      (uint32_t)nblk * C::V_BLOCK_SCALES * 2);
+    unsigned char *myslots = smem + C::OFF_SLOTS + wave * NS * C::SLOT;
 
-    // ---- the workgroup's G query rows (G*D fp32, contiguous) go to LDS once
-    // with coalesced loads; each wave then reads its operand slice from there.
-    float *sq = reinterpret_cast<float *>(smem + C::QOFF);
+    // ---- query prologue, part 1: wave w loads the slice of channel step w
+    // (8 channels per lane)
+    const bool preps = wave < C::KSTEPS;
+    const bool real = h < G;
+    float qv[8];
     {
-        const float4 *qsrc = reinterpret_cast<const float4 *>(
-            a.q + ((int64_t)b * a.n_q_heads + (int64_t)kvh * G) * D);
-        for (int i = tid; i < G * D / 4; i += kThreads) reinterpret_cast<float4 *>(sq)[i] = qsrc[i];
+        const float *qp = a.q + ((int64_t)b * a.n_q_heads + (int64_t)kvh * G + (real ? h : 0)) * D +
+                          32 * (preps ? wave : 0) + 8 * q4;
+        const float4 x0 = *reinterpret_cast<const float4 *>(qp);
+        const float4 x1 = *reinterpret_cast<const float4 *>(qp + 4);
+        const bool use = real && preps;
+        qv[0] = use ? x0.x : 0.f; qv[1] = use ? x0.y : 0.f; qv[2] = use ? x0.z : 0.f; qv[3] = use ? x0.w : 0.f;
+        qv[4] = use ? x1.x : 0.f; qv[5] = use ? x1.y : 0.f; qv[6] = use ? x1.z : 0.f; qv[7] = use ? x1.w : 0.f;
     }
-    // ---- blocks are handed out dynamically inside the workgroup: wave w
-    // starts with block w, then each wave takes the next unclaimed block.
-    if (tid == 0) s_next = kWaves;
-    Buf<D, KC, VC> bufA, bufB;
-    int cur = wave;
-    if (cur < nblk) issue(bufA, cur);
-    __syncthreads();  // s_next initialised, query staged
-    float qv[C::KSTEPS][8];
-    {
-        const bool real = h < G;
-        const float *qp = sq + (real ? h : 0) * D;
+    // the whole ring starts streaming once the query is in (queued behind
+    // the ring's DMAs the query would arrive late); the prologue below
+    // touches LDS only through hand-issued accesses, so it never waits for
+    // these DMAs
+    asm volatile("s_waitcnt vmcnt(0)" : "+v"(qv[0]), "+v"(qv[1]), "+v"(qv[2]), "+v"(qv[3]), "+v"(qv[4]),
+                 "+v"(qv[5]), "+v"(qv[6]), "+v"(qv[7])::"memory");
 #pragma unroll
-        for (int t = 0; t < C::KSTEPS; ++t) {
-            const float4 x0 = *reinterpret_cast<const float4 *>(qp + 32 * t + 8 * q4);
-            const float4 x1 = *reinterpret_cast<const float4 *>(qp + 32 * t + 8 * q4 + 4);
-            qv[t][0] = real ? x0.x : 0.f; qv[t][1] = real ? x0.y : 0.f;
-            qv[t][2] = real ? x0.z : 0.f; qv[t][3] = real ? x0.w : 0.f;
-            qv[t][4] = real ? x1.x : 0.f; qv[t][5] = real ? x1.y : 0.f;
-            qv[t][6] = real ? x1.z : 0.f; qv[t][7] = real ? x1.w : 0.f;
-        }
-    }
-    auto grab = [&]() -> int {
-        int v = 0;
-        if (lane == 0) v = atomicAdd(&s_next, 1);
-        return __builtin_amdgcn_readfirstlane(v);
-    };
-    int nxt = cur < nblk ? grab() : nblk;
-    if (nxt < nblk) issue(bufB, nxt);
+    for (int s = 0; s < NS; ++s) dma_block<D, KC, VC>(st, wave + s * kWaves, myslots + s * C::SLOT, lane);
 
-    // ---- query operand: power-of-two normalised hi + lo binary16 halves
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void *)smem;
+    if (preps) {
+        float m = 0.0f;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) m = fmaxf(m, fabsf(qv[s]));
+        m = fmaxf(m, shfl_xor(m, 16));
+        m = fmaxf(m, shfl_xor(m, 32));
+        if (q4 == 0) ds_wr(lds0 + (wave * 16 + h) * 4, __builtin_bit_cast(uint32_t, m), C::OFF_TMAX);
+    }
+    if (tid == 0) ds_wr(lds0, (uint32_t)(NS * kWaves), C::OFF_CNT);
+    lds_barrier();
+
+    // ---- part 2: power-of-two normalisation per head, hi + lo binary16
+    // halves of channel step w, and that step's share of the bias correction
+    uint32_t tmaxw[C::KSTEPS];
+#pragma unroll
+    for (int t = 0; t < C::KSTEPS; ++t) ds_rd(tmaxw[t], lds0 + h * 4, C::OFF_TMAX + t * 64);
+    lds_wait<C::KSTEPS>(tmaxw);
     float qmaxabs = 0.0f;
 #pragma unroll
-    for (int t = 0; t < C::KSTEPS; ++t)
-#pragma unroll
-        for (int s = 0; s < 8; ++s) qmaxabs = fmaxf(qmaxabs, fabsf(qv[t][s]));
-    qmaxabs = fmaxf(qmaxabs, shfl_xor(qmaxabs, 16));
-    qmaxabs = fmaxf(qmaxabs, shfl_xor(qmaxabs, 32));
+    for (int t = 0; t < C::KSTEPS; ++t) qmaxabs = fmaxf(qmaxabs, __builtin_bit_cast(float, tmaxw[t]));
     const int qexp = qmaxabs > 0.0f ? ilogbf(qmaxabs) : 0;
-    const float qnorm = ldexpf(1.0f, -qexp);
-    h8 qhi[C::KSTEPS], qlo[C::QLO_LDS ? 1 : C::KSTEPS];
-    h8 *qlo_lds = reinterpret_cast<h8 *>(smem + kWaves * C::SLOT_WORDS * 4) +
-                  (size_t)wave * C::KSTEPS * 64 + lane;
-    float corr[C::KNG];
-#pragma unroll
-    for (int g = 0; g < C::KNG; ++g) corr[g] = 0.0f;
-#pragma unroll
-    for (int t = 0; t < C::KSTEPS; ++t) {
-        float cpart = 0.0f;  // exact: at most 8 products of 11-bit values and a 5-bit bias
+    if (preps) {
+        const float qnorm = ldexpf(1.0f, -qexp);
+        h8 hi8, lo8;
+        float cpart = 0.0f;
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
-            const float x = qv[t][s] * qnorm * k_slot_factor<KC>(s);
+            const float x = qv[s] * qnorm * k_slot_factor<KC>(s);
             const _Float16 hi = (_Float16)x;
             const _Float16 lo = (_Float16)(x - (float)hi);
-            qhi[t][s] = hi;
-            qlo[C::QLO_LDS ? 0 : t][s] = lo;
+            hi8[s] = hi;
+            lo8[s] = lo;
             cpart = fmaf((float)hi + (float)lo, k_slot_bias<KC>(s), cpart);
         }
-        if constexpr (C::QLO_LDS) qlo_lds[t * 64] = qlo[0];
-        corr[t / C::STEPS_PER_KGROUP] += cpart;
+        ds_wr(lds0 + wave * 2048 + lane * 16, __builtin_bit_cast(u4, hi8), C::OFF_QOP);
+        ds_wr(lds0 + wave * 2048 + lane * 16, __builtin_bit_cast(u4, lo8), C::OFF_QOP + 1024);
+        cpart += shfl_xor(cpart, 16);
+        cpart += shfl_xor(cpart, 32);
+        if (q4 == 0) ds_wr(lds0 + (wave * 16 + h) * 4, __builtin_bit_cast(uint32_t, cpart), C::OFF_CORR);
     }
+    lds_barrier();
+
+    uint32_t corrw[C::KSTEPS];
 #pragma unroll
-    for (int g = 0; g < C::KNG; ++g) {
-        corr[g] += shfl_xor(corr[g], 16);
-        corr[g] += shfl_xor(corr[g], 32);
-    }
-    const float c_h = a.scale_log2 * ldexpf(1.0f, qexp);
+    for (int t = 0; t < C::KSTEPS; ++t) ds_rd(corrw[t], lds0 + h * 4, C::OFF_CORR + t * 64);
+    lds_wait<C::KSTEPS>(corrw);
     f4 cinit[C::KNG];  // accumulator start values: cancel the operand bias
 #pragma unroll
-    for (int g = 0; g < C::KNG; ++g) cinit[g] = f4{-corr[g], -corr[g], -corr[g], -corr[g]};
+    for (int g = 0; g < C::KNG; ++g) {
+        float corr = 0.0f;
+#pragma unroll
+        for (int st2 = 0; st2 < C::STEPS_PER_KGROUP; ++st2)
+            corr += __builtin_bit_cast(float, corrw[g * C::STEPS_PER_KGROUP + st2]);
+        cinit[g] = f4{-corr, -corr, -corr, -corr};
+    }
+    const float c_h = a.scale_log2 * ldexpf(1.0f, qexp);
+    h8 qreg[C::Q_LDS ? 1 : 2 * C::KSTEPS];
+    if constexpr (!C::Q_LDS) {
+#pragma unroll
+        for (int i = 0; i < 2 * C::KSTEPS; ++i) ds_rd(*reinterpret_cast<u4 *>(&qreg[i]), lds0 + lane * 16, C::OFF_QOP + i * 1024);
+        lds_wait<8 * C::KSTEPS>(reinterpret_cast<uint32_t *>(qreg));
+    }
 
-    // per-wave LDS slot for one block's scales
-    uint32_t *slot = reinterpret_cast<uint32_t *>(smem) + wave * C::SLOT_WORDS;
+    // LDS byte addresses for the hand-issued reads
+    const uint32_t lds_slots = (uint32_t)(uintptr_t)(lds_void *)myslots;
+    const uint32_t a16 = lds_slots + lane * 16, a8 = lds_slots + lane * 8, a4 = lds_slots + lane * 4;
+    const uint32_t aks = lds_slots + q4 * C::KS_LANE_BYTES, avs = lds_slots + q4 * C::VS_LANE_BYTES;
+    const uint32_t aq = lds0 + C::OFF_QOP + lane * 16;
 
     f4 O[C::CB];
 #pragma unroll
     for (int cb = 0; cb < C::CB; ++cb) O[cb] = f4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.0f;
 
-    auto process = [&](const Buf<D, KC, VC> &bf, int idx) {
-        // stage this block's scales, read them back in operand order
+    // Computes block idx from its words.
+    auto process = [&](Payload<D, KC, VC> &pl, int idx) {
         const int rows_here = nrows - idx * kBlockRows;  // > 0
+        // ---- scores S^T for the two 16-row tiles, channel steps in lockstep
+        const f16_alias *ksc0 = reinterpret_cast<const f16_alias *>(pl.ks(0));
+        const f16_alias *ksc1 = reinterpret_cast<const f16_alias *>(pl.ks(1));
+        float S[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-        for (int i = 0; i < C::KS_PER_LANE; ++i)
-            if (lane + 64 * i < C::KS_WORDS) slot[lane + 64 * i] = bf.ks[i];
+        for (int g = 0; g < C::KNG; ++g) {
+            f4 acc0 = cinit[g], acc1 = cinit[g];
+            h8 qg[2 * C::STEPS_PER_KGROUP];
+            if constexpr (C::Q_LDS) {
 #pragma unroll
-        for (int i = 0; i < C::VS_PER_LANE; ++i) {
-            const int w = lane + 64 * i;
-            if (w < C::VS_WORDS) {
-                uint32_t word = bf.vs[i];
-                if (rows_here < kBlockRows) {
-                    // rows past the end get a zero V scale, so that bytes that
-                    // were never written cannot turn 0 * V into NaN
-                    const int m = w & 3;
-                    const int j0 = (m >> 1) * 16 + 4 * (w / (4 * C::VNG)) + 2 * (m & 1);
-                    if (j0 >= rows_here) word &= 0xFFFF0000u;
-                    if (j0 + 1 >= rows_here) word &= 0x0000FFFFu;
-                }
-                slot[C::KS_WORDS + w] = word;
-            }
-        }
-        // ---- scores S^T for the two 16-row tiles
-        float S[2][4];
-#pragma unroll
-        for (int tau = 0; tau < 2; ++tau) {
-            const _Float16 *ksc = reinterpret_cast<const _Float16 *>(slot) + tau * 16 * C::KNG +
-                                  q4 * 4 * C::KNG;
-            float sacc[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int g = 0; g < C::KNG; ++g) {
-                f4 acc = cinit[g];
-#pragma unroll
-                for (int st = 0; st < C::STEPS_PER_KGROUP; ++st) {
-                    const int t = g * C::STEPS_PER_KGROUP + st;
-                    const h8 kop = k_operand<KC>(&bf.k[tau][is8(KC) ? 2 * t : t]);
-                    acc = mfma16x16x32(kop, qhi[t], acc);
-                    if constexpr (C::QLO_LDS) acc = mfma16x16x32(kop, qlo_lds[t * 64], acc);
-                    else acc = mfma16x16x32(kop, qlo[t], acc);
-                }
-                if (C::KNG >= 4 && (g & 1) == 1) __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) sacc[r] = fmaf(acc[r], (float)ksc[g * 4 + r], sacc[r]);
+                for (int i = 0; i < 2 * C::STEPS_PER_KGROUP; ++i)
+                    ds_rd(*reinterpret_cast<u4 *>(&qg[i]), aq, (2 * g * C::STEPS_PER_KGROUP + i) * 1024);
+                lds_wait<8 * C::STEPS_PER_KGROUP>(reinterpret_cast<uint32_t *>(qg));
             }
 #pragma unroll
-            for (int r = 0; r < 4; ++r) S[tau][r] = sacc[r] * c_h;
-            __builtin_amdgcn_sched_barrier(0);  // keep one tile's operands live at a time
+            for (int st2 = 0; st2 < C::STEPS_PER_KGROUP; ++st2) {
+                const int t = g * C::STEPS_PER_KGROUP + st2;
+                const h8 qh = C::Q_LDS ? qg[2 * st2] : qreg[2 * t];
+                const h8 ql = C::Q_LDS ? qg[2 * st2 + 1] : qreg[2 * t + 1];
+                const h8 k0 = k_operand<KC>(&pl.k(0)[is8(KC) ? 2 * t : t]);
+                const h8 k1 = k_operand<KC>(&pl.k(1)[is8(KC) ? 2 * t : t]);
+                acc0 = mfma16x16x32(k0, qh, acc0);
+                acc1 = mfma16x16x32(k1, qh, acc1);
+                acc0 = mfma16x16x32(k0, ql, acc0);
+                acc1 = mfma16x16x32(k1, ql, acc1);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                S[0][r] = fmaf(acc0[r], (float)ksc0[g * 4 + r], S[0][r]);
+                S[1][r] = fmaf(acc1[r], (float)ksc1[g * 4 + r], S[1][r]);
+            }
         }
+#pragma unroll
+        for (int tau = 0; tau < 2; ++tau)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) S[tau][r] *= c_h;
+        uint32_t *vsw = pl.vs();
         if (rows_here < kBlockRows) {
             const int lim = rows_here - 4 * q4;  // row 16*tau + 4*q4 + r is valid iff 16*tau + r < lim
 #pragma unroll
@@ -312,8 +439,21 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     if (16 * tau + r >= lim) S[tau][r] = -INFINITY;
+            // rows past the end get a zero V scale, so that bytes that were
+            // never written cannot turn 0 * V into NaN; word g*4+m holds the
+            // scales of rows (m/2)*16 + 4*q4 + 2*(m%2) + {0, 1}
+#pragma unroll
+            for (int g = 0; g < C::VNG; ++g)
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const int j0 = (m >> 1) * 16 + 2 * (m & 1);
+                    uint32_t word = vsw[g * 4 + m];
+                    if (j0 >= lim) word &= 0xFFFF0000u;
+                    if (j0 + 1 >= lim) word &= 0x0000FFFFu;
+                    vsw[g * 4 + m] = word;
+                }
         }
-        const h2 *svb = reinterpret_cast<const h2 *>(slot + C::KS_WORDS) + q4 * 4 * C::VNG;
+        const h2_alias *svb = reinterpret_cast<const h2_alias *>(vsw);
 
         // ---- online softmax (log2 domain)
         float mx = fmaxf(fmaxf(fmaxf(S[0][0], S[0][1]), fmaxf(S[0][2], S[0][3])),
@@ -339,27 +479,50 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
                 P[4 * tau + r] = (_Float16)p;
             }
 
-        __builtin_amdgcn_sched_barrier(0);
         // ---- O^T += V^T P^T, one 16-channel block at a time
 #pragma unroll
         for (int cb = 0; cb < C::CB; ++cb) {
             const int gv = cb * 16 / C::VG;
-            const h8 vop = v_operand<VC>(&bf.v[is8(VC) ? 2 * cb : cb], svb + gv * 4);
+            const h8 vop = v_operand<VC>(&pl.v()[is8(VC) ? 2 * cb : cb], svb + gv * 4);
             O[cb] = mfma16x16x32(vop, P, O[cb]);
-            if ((cb & 3) == 3) __builtin_amdgcn_sched_barrier(0);  // bound the unpacked operands in flight
         }
     };
 
-    while (cur < nblk) {
-        process(bufA, cur);
-        cur = nxt;
-        if (cur >= nblk) break;
-        bufA = bufB;  // register renames after full unrolling of the copy
-        nxt = grab();
-        if (nxt < nblk) issue(bufB, nxt);
+    // ---- the ring.  Slot s starts with block w + 8 s; each refill takes the
+    // next unclaimed block of the split from the workgroup's LDS counter, so
+    // waves whose blocks arrive early take more of them.  A wave's slots hold
+    // increasing block indices, so the first one past the end ends the wave.
+    // At the top of a slot the DMAs issued after its own are those of the
+    // NS - 1 other slots: waiting until at most that many remain is exact.
+    auto grab = [&]() -> int {
+        uint32_t v = 0;
+        if (lane == 0) v = ds_add_rtn(lds0, 1u, C::OFF_CNT);
+        return __builtin_amdgcn_readfirstlane((int)v);
+    };
+    int sidx[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) sidx[s] = wave + s * kWaves;
+    bool live = true;
+    while (live) {
+        [&]<int... S>(std::integer_sequence<int, S...>) {
+            (([&] {
+                 if (!live) return;
+                 const int idx = sidx[S];
+                 if (idx >= nblk) { live = false; return; }
+                 vm_wait<(NS - 1) * C::N_DMA>();
+                 Payload<D, KC, VC> pl;
+                 read_slot<D, KC, VC>(pl, a16, a8, a4, aks, avs, S * C::SLOT);
+                 const int nxt = grab();
+                 sidx[S] = nxt;
+                 dma_block<D, KC, VC>(st, nxt, myslots + S * C::SLOT, lane);
+                 process(pl, idx);
+             }()),
+             ...);
+        }(std::make_integer_sequence<int, NS>{});
     }
 
-    // ---- merge the 8 waves through LDS
+    // ---- merge the waves through LDS (the compiler waits for any DMA still
+    // in flight before these LDS accesses)
     l_run += shfl_xor(l_run, 16);
     l_run += shfl_xor(l_run, 32);
     __syncthreads();
@@ -468,9 +631,9 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
 template <int D, int KC, int VC>
 hipError_t launch_typed(const DecodeArgs &a, hipStream_t s) {
     using C = Cfg<D, KC, VC>;
-    const size_t scale_lds = (size_t)C::QOFF + (size_t)a.gqa * D * sizeof(float);
+    const size_t stream_lds = (size_t)C::LDS_STREAM;
     const size_t merge_lds = (size_t)kWaves * a.gqa * (D + 4 + 2) * sizeof(float);
-    const size_t lds = scale_lds > merge_lds ? scale_lds : merge_lds;
+    const size_t lds = stream_lds > merge_lds ? stream_lds : merge_lds;
     const dim3 grid((unsigned)a.max_splits, (unsigned)a.k.n_kv_heads, (unsigned)a.n_seqs);
     if (lds > 65536) {
         hipError_t e = hipFuncSetAttribute((const void *)decode_kernel<D, KC, VC>,

@@ -14,6 +14,11 @@ typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+// Views for reading back LDS words that were stored as uint32_t: the
+// may_alias attribute keeps the compiler from reordering (or hoisting out of
+// a loop) such a read past the store under type-based alias rules.
+typedef _Float16 f16_alias __attribute__((may_alias));
+typedef _Float16 h2_alias __attribute__((ext_vector_type(2), may_alias));
 
 __device__ __forceinline__ h2 as_h2(uint32_t w) { return __builtin_bit_cast(h2, w); }
 __device__ __forceinline__ uint32_t as_u32(h2 v) { return __builtin_bit_cast(uint32_t, v); }
@@ -88,7 +93,7 @@ __device__ __forceinline__ constexpr float k_slot_factor(int s) {
 // code * dq (rounded to nearest even once; exact for subnormal scales), for the
 // eight slot rows.  dq2[m] holds the scales of slots (2m, 2m+1).
 template <int CODEC>
-__device__ __forceinline__ h8 v_operand(const uint32_t *w, const h2 *dq2) {
+__device__ __forceinline__ h8 v_operand(const uint32_t *w, const h2_alias *dq2) {
     h2 v0, v1, v2, v3;
     if constexpr (is8(CODEC)) {
         const u2 a = byte_magic(w[0]), b = byte_magic(w[1]);
