@@ -280,6 +280,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane & 15, q4 = lane >> 4;
+    const int x32 = 4 * (lane ^ 32);  // byte index of lane ^ 32 for ds_bpermute
     const int G = a.gqa;
 
     const int64_t head_lin = (int64_t)b * a.k.n_kv_heads + kvh;
@@ -308,22 +309,21 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
         qv[0] = use ? x0.x : 0.f; qv[1] = use ? x0.y : 0.f; qv[2] = use ? x0.z : 0.f; qv[3] = use ? x0.w : 0.f;
         qv[4] = use ? x1.x : 0.f; qv[5] = use ? x1.y : 0.f; qv[6] = use ? x1.z : 0.f; qv[7] = use ? x1.w : 0.f;
     }
-    // the whole ring starts streaming once the query is in (queued behind
-    // the ring's DMAs the query would arrive late); the prologue below
-    // touches LDS only through hand-issued accesses, so it never waits for
-    // these DMAs
+    // the first slot starts streaming once the query is in (queued behind
+    // the DMAs the query would arrive late); the rest of the ring follows the
+    // prologue: a wave blocks while the memory queues are full, and the
+    // prologue should not wait behind that.  The prologue touches LDS only
+    // through hand-issued accesses, so it never waits for these DMAs.
     asm volatile("s_waitcnt vmcnt(0)" : "+v"(qv[0]), "+v"(qv[1]), "+v"(qv[2]), "+v"(qv[3]), "+v"(qv[4]),
                  "+v"(qv[5]), "+v"(qv[6]), "+v"(qv[7])::"memory");
-#pragma unroll
-    for (int s = 0; s < NS; ++s) dma_block<D, KC, VC>(st, wave + s * kWaves, myslots + s * C::SLOT, lane);
+    dma_block<D, KC, VC>(st, wave, myslots, lane);
 
     const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void *)smem;
     if (preps) {
         float m = 0.0f;
 #pragma unroll
         for (int s = 0; s < 8; ++s) m = fmaxf(m, fabsf(qv[s]));
-        m = fmaxf(m, shfl_xor(m, 16));
-        m = fmaxf(m, shfl_xor(m, 32));
+        m = quad_max(m, x32);
         if (q4 == 0) ds_wr(lds0 + (wave * 16 + h) * 4, __builtin_bit_cast(uint32_t, m), C::OFF_TMAX);
     }
     if (tid == 0) ds_wr(lds0, (uint32_t)(NS * kWaves), C::OFF_CNT);
@@ -354,8 +354,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
         }
         ds_wr(lds0 + wave * 2048 + lane * 16, __builtin_bit_cast(u4, hi8), C::OFF_QOP);
         ds_wr(lds0 + wave * 2048 + lane * 16, __builtin_bit_cast(u4, lo8), C::OFF_QOP + 1024);
-        cpart += shfl_xor(cpart, 16);
-        cpart += shfl_xor(cpart, 32);
+        cpart = quad_sum(cpart, x32);
         if (q4 == 0) ds_wr(lds0 + (wave * 16 + h) * 4, __builtin_bit_cast(uint32_t, cpart), C::OFF_CORR);
     }
     lds_barrier();
@@ -380,6 +379,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
         for (int i = 0; i < 2 * C::KSTEPS; ++i) ds_rd(*reinterpret_cast<u4 *>(&qreg[i]), lds0 + lane * 16, C::OFF_QOP + i * 1024);
         lds_wait<8 * C::KSTEPS>(reinterpret_cast<uint32_t *>(qreg));
     }
+
+#pragma unroll
+    for (int s = 1; s < NS; ++s) dma_block<D, KC, VC>(st, wave + s * kWaves, myslots + s * C::SLOT, lane);
 
     // LDS byte addresses for the hand-issued reads
     const uint32_t lds_slots = (uint32_t)(uintptr_t)(lds_void *)myslots;
@@ -456,10 +458,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
         const h2_alias *svb = reinterpret_cast<const h2_alias *>(vsw);
 
         // ---- online softmax (log2 domain)
-        float mx = fmaxf(fmaxf(fmaxf(S[0][0], S[0][1]), fmaxf(S[0][2], S[0][3])),
-                         fmaxf(fmaxf(S[1][0], S[1][1]), fmaxf(S[1][2], S[1][3])));
-        mx = fmaxf(mx, shfl_xor(mx, 16));
-        mx = fmaxf(mx, shfl_xor(mx, 32));
+        float mx = S[0][0];
+#pragma unroll
+        for (int i = 1; i < 8; ++i) mx = __builtin_elementwise_maximum(mx, S[i / 4][i % 4]);
+        mx = quad_max(mx, x32);
         const bool raise = mx > m_run + kRescaleThreshold;
         if (__any(raise)) {
             const float m_new = raise ? mx : m_run;
@@ -523,8 +525,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
 
     // ---- merge the waves through LDS (the compiler waits for any DMA still
     // in flight before these LDS accesses)
-    l_run += shfl_xor(l_run, 16);
-    l_run += shfl_xor(l_run, 32);
+    l_run = quad_sum(l_run, x32);
     __syncthreads();
     constexpr int DP = D + 4;                               // padded head stride
     float *so = reinterpret_cast<float *>(smem);           // [wave][G][DP]

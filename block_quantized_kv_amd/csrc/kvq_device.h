@@ -123,6 +123,25 @@ __device__ __forceinline__ h8 v_operand(const uint32_t *w, const h2_alias *dq2) 
 // ---- cross-lane ----------------------------------------------------------------
 __device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, 64); }
 
+// max / sum over the 4 lanes h, h+16, h+32, h+48 (every lane gets the result):
+// lane ^ 16 through a bit-mode swizzle (and 0x1F, xor 0x10: no index math),
+// lane ^ 32 through a permute whose byte index x32 = 4 * (lane ^ 32) the caller
+// computes once.
+__device__ __forceinline__ float xor16(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
+}
+__device__ __forceinline__ float xor32(float v, int x32) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(x32, __builtin_bit_cast(int, v)));
+}
+__device__ __forceinline__ float quad_max(float v, int x32) {
+    v = __builtin_elementwise_maximum(v, xor16(v));
+    return __builtin_elementwise_maximum(v, xor32(v, x32));
+}
+__device__ __forceinline__ float quad_sum(float v, int x32) {
+    v += xor16(v);
+    return v + xor32(v, x32);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 }  // namespace kvq
