@@ -45,7 +45,103 @@ def _args():
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run plain 256 MiB device copies (HBM counter calibration)")
+    p.add_argument("--write-traffic-summary", metavar="PMC_DIR",
+                   help="summarize rocprofv3 FETCH_SIZE/WRITE_SIZE runs (PMC_DIR/{fetch,write,cfetch,cwrite}) "
+                        "into " + os.path.relpath(TRAFFIC_FILE, ROOT) + " and exit")
     return p.parse_args()
+
+
+# ---- counter-backed HBM traffic of kvq_attend_decode ------------------------
+# rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) over this benchmark gives KiB
+# per dispatch of decode_kernel and combine_kernel; the same counters over
+# --calibrate-copy (exactly 256 MiB read and 256 MiB written per dispatch)
+# give the scale factors.  The summary records a hash of the decode sources
+# and is used only while they are unchanged.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode64k_q4g64_traffic.txt")
+DECODE_SOURCES = ["block_quantized_kv_amd/csrc/attn_decode.hip", "block_quantized_kv_amd/csrc/kvq_device.h",
+                  "block_quantized_kv_amd/csrc/kvq_layout.h", "block_quantized_kv_amd/csrc/kvq_internal.h"]
+
+
+def decode_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in DECODE_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _pmc_mean(path_glob: str, counter: str, name_pat: str):
+    import csv
+    import glob
+    vals = []
+    for f in glob.glob(path_glob):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] == counter and name_pat in r["Kernel_Name"]:
+                    vals.append(float(r["Counter_Value"]))
+    return (sum(vals) / len(vals), len(vals)) if vals else (None, 0)
+
+
+def write_traffic_summary(pmc_dir: str):
+    g = lambda sub: os.path.join(pmc_dir, sub, "*_counter_collection.csv")
+    f_dec, n1 = _pmc_mean(g("fetch"), "FETCH_SIZE", "decode_kernel")
+    f_cmb, _ = _pmc_mean(g("fetch"), "FETCH_SIZE", "combine_kernel")
+    w_dec, n2 = _pmc_mean(g("write"), "WRITE_SIZE", "decode_kernel")
+    w_cmb, _ = _pmc_mean(g("write"), "WRITE_SIZE", "combine_kernel")
+    f_cal, _ = _pmc_mean(g("cfetch"), "FETCH_SIZE", "copy")
+    w_cal, _ = _pmc_mean(g("cwrite"), "WRITE_SIZE", "copy")
+    if None in (f_dec, f_cmb, w_dec, w_cmb, f_cal, w_cal):
+        sys.exit("missing counter runs under " + pmc_dir)
+    kib256 = 256 * 1024  # KiB in 256 MiB
+    ff, fw = kib256 / f_cal, kib256 / w_cal
+    fetch_b = (f_dec + f_cmb) * ff * 1024
+    write_b = (w_dec + w_cmb) * fw * 1024
+    lines = [
+        "# HBM traffic of one kvq_attend_decode launch (decode_kernel + combine_kernel),",
+        "# 64K-context Q4_G64 decode (1 seq, 24/4 heads, head_dim 256), from rocprofv3 counters",
+        "#",
+        "# commands (GPU box, repo root; one counter per run):",
+        "#   rocprofv3 --pmc FETCH_SIZE --kernel-include-regex 'decode_kernel|combine_kernel' -d <dir>/fetch -o fetch "
+        "--output-format csv -- python -u bench.py --steps 32 --warmup 8 --no-cpu-baseline --no-prefill",
+        "#   rocprofv3 --pmc WRITE_SIZE (same, -d <dir>/write)",
+        "#   rocprofv3 --pmc FETCH_SIZE -d <dir>/cfetch -o cfetch --output-format csv -- python -u bench.py --calibrate-copy",
+        "#   rocprofv3 --pmc WRITE_SIZE -d <dir>/cwrite ... -- python -u bench.py --calibrate-copy",
+        "#   python bench.py --write-traffic-summary <dir>",
+        f"decode_source_hash: {decode_source_hash()}",
+        f"dispatches: {n1} {n2}",
+        f"fetch_kib_decode: {f_dec:.1f}",
+        f"fetch_kib_combine: {f_cmb:.1f}",
+        f"write_kib_decode: {w_dec:.1f}",
+        f"write_kib_combine: {w_cmb:.1f}",
+        f"copy_fetch_kib_per_256MiB: {f_cal:.1f}",
+        f"copy_write_kib_per_256MiB: {w_cal:.1f}",
+        f"fetch_scale: {ff:.4f}",
+        f"write_scale: {fw:.4f}",
+        f"traffic_bytes_per_launch: {fetch_b + write_b:.0f}",
+        f"fetch_bytes_per_launch: {fetch_b:.0f}",
+        f"write_bytes_per_launch: {write_b:.0f}",
+    ]
+    with open(TRAFFIC_FILE, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def read_traffic():
+    """Counter-backed bytes per kvq_attend_decode launch, or None when the
+    summary is missing or was taken on other decode sources."""
+    try:
+        kv = {}
+        with open(TRAFFIC_FILE) as fh:
+            for line in fh:
+                if ":" in line and not line.startswith("#"):
+                    k, v = line.split(":", 1)
+                    kv[k.strip()] = v.strip()
+        if kv.get("decode_source_hash") != decode_source_hash():
+            return None
+        return float(kv["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def calibrate_copy():
@@ -78,6 +174,9 @@ def main():
     args = _args()
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.write_traffic_summary:
+        write_traffic_summary(args.write_traffic_summary)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no "
@@ -194,6 +293,7 @@ def main():
     torch.cuda.synchronize()
     att_avg_ms = a0.elapsed_time(a1) / (reps * ROTATE)
     achieved = nb["attend_kernel"] / (att_avg_ms * 1e-3) / 1e9
+    traffic = read_traffic()
 
     result = {
         "metric": "decode-attention effective KV GB/s @64K ctx",
@@ -217,7 +317,7 @@ def main():
                    "wall_s_timed_region": round(wall, 4)},
         "roofline": {"bound": "hbm", "kernel": "kvq_attend_decode = decode_kernel<256,Q4_G64,Q4_G64> + combine_kernel<256>",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "bytes_per_launch": nb["attend_kernel"], "avg_launch_ms": round(att_avg_ms, 5)},
     }
 
