@@ -204,6 +204,7 @@ def main():
                    torch.zeros(b - a, dtype=torch.int32, device=dev),
                    torch.arange(a, b, dtype=torch.int64, device=dev))
     k_new, v_new = k[n - 1:n].contiguous(), v[n - 1:n].contiguous()
+    k_new2, v_new2 = k[n - 2:n].contiguous(), v[n - 2:n].contiguous()  # two drafted tokens
     host_kv = (k.cpu().numpy(), v.cpu().numpy()) if not args.no_cpu_baseline else None
     del k, v
     caches = [base] + [base.clone() for _ in range(ROTATE - 1)]
@@ -320,6 +321,36 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "bytes_per_launch": nb["attend_kernel"], "avg_launch_ms": round(att_avg_ms, 5)},
     }
+
+    # ---- the same step verifying two drafted tokens (multi-query decode):
+    # append rows n-2 and n-1, attend from both; the K/V bytes are read once
+    from block_quantized_kv_amd import decode_mq_workspace, kvq_attend_decode_mq
+    q2 = torch.randn(1, 2, cfg.n_q_heads, d, device=dev, generator=torch.Generator(device=dev).manual_seed(2))
+    out2 = torch.empty_like(q2)
+    ws2 = decode_mq_workspace(base, cfg.n_q_heads, 1, 2, n)
+    seq2 = torch.zeros(2, dtype=torch.int32, device=dev)
+    pos2 = torch.tensor([n - 2, n - 1], dtype=torch.int64, device=dev)
+
+    def step2(i):
+        L = caches[i % ROTATE]
+        kvq_append(L, k_new2, v_new2, seq2, pos2, stream=stream)
+        kvq_attend_decode_mq(L, q2, seq_len, n, cfg.scale, out=out2, workspace=ws2, stream=stream)
+
+    for i in range(args.warmup):
+        step2(i)
+    torch.cuda.synchronize()
+    m0, m1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    m0.record(stream)
+    for i in range(args.steps):
+        step2(i)
+    m1.record(stream)
+    torch.cuda.synchronize()
+    mq_ms = m0.elapsed_time(m1) / args.steps
+    mq_bytes = nb["kv"] + 2 * nb["q_out"] + 2 * nb["append"]
+    result["multi_query"] = {"q_len": 2, "ms_per_step": round(mq_ms, 5),
+                             "value": round(mq_bytes / (mq_ms * 1e-3) / 1e9, 2), "unit": "GB/s",
+                             "tokens_per_s": round(2 / (mq_ms * 1e-3), 1),
+                             "step": "kvq_append(2 tokens) + kvq_attend_decode_mq(q_len 2), eager"}
 
     if not args.no_prefill:
         result["prefill"] = run_prefill(torch, dev, args)

@@ -15,10 +15,13 @@ from ._binding import (  # noqa: F401
     Layer,
     kvq_append,
     kvq_attend_decode,
+    kvq_attend_decode_mq,
     kvq_attend_prefill,
     kvq_dequant,
     kvq_decode_workspace_bytes,
     decode_workspace,
+    decode_mq_workspace,
+    kvq_decode_mq_workspace_bytes,
     kvq_prefill_workspace_bytes,
     kvq_plane_bytes,
     kvq_row_code_bytes,

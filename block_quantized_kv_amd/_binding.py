@@ -61,6 +61,8 @@ def load_library():
         "kvq_append": (i32, [LY, P, P, P, P, i32, P, P]),
         "kvq_decode_workspace_bytes": (sz, [LY, i32, i32, i64]),
         "kvq_attend_decode": (i32, [LY, P, P, i32, i32, i64, f32, P, P, sz, P]),
+        "kvq_decode_mq_workspace_bytes": (sz, [LY, i32, i32, i32, i64]),
+        "kvq_attend_decode_mq": (i32, [LY, P, P, i32, i32, i32, i64, f32, P, P, sz, P]),
         "kvq_prefill_workspace_bytes": (sz, [LY, i32, i32]),
         "kvq_attend_prefill": (i32, [LY, P, i32, i64, i32, i32, f32, P, P, sz, P]),
         "kvq_dequant": (i32, [PL, i32, i64, i64, P, P]),
@@ -210,6 +212,38 @@ def kvq_attend_decode(layer: Layer, q, seq_len, max_len: int, softmax_scale: flo
     _check(load_library().kvq_attend_decode(ctypes.byref(L), _ptr(q), _ptr(seq_len), n_seqs, hq,
                                             max_len, softmax_scale, _ptr(out), _ptr(workspace),
                                             workspace.numel(), _stream(stream)))
+    return out
+
+
+def kvq_decode_mq_workspace_bytes(layer: Layer, n_q_heads: int, n_seqs: int, q_len: int, max_len: int) -> int:
+    L = layer.struct()
+    return int(load_library().kvq_decode_mq_workspace_bytes(ctypes.byref(L), n_q_heads, n_seqs, q_len, max_len))
+
+
+def decode_mq_workspace(layer: Layer, n_q_heads: int, n_seqs: int, q_len: int, max_len: int):
+    """A multi-query decode workspace (scratch for the split partials)."""
+    nbytes = max(kvq_decode_mq_workspace_bytes(layer, n_q_heads, n_seqs, q_len, max_len), 256)
+    return torch.zeros(nbytes, dtype=torch.uint8, device=layer.k.codes.device)
+
+
+def kvq_attend_decode_mq(layer: Layer, q, seq_len, max_len: int, softmax_scale: float, out=None,
+                         workspace=None, stream=None):
+    """q fp32 [n_seqs][q_len][n_q_heads][head_dim]; query i of sequence b sits at
+    row seq_len[b] - q_len + i (already appended) and attends rows up to it."""
+    n_seqs, q_len, hq, d = q.shape
+    _need(q, "q", torch.float32, (n_seqs, q_len, hq, layer.k.head_dim))
+    _need(seq_len, "seq_len", torch.int64, (n_seqs,))
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", torch.float32, (n_seqs, q_len, hq, layer.k.head_dim))
+    if workspace is None:
+        workspace = decode_mq_workspace(layer, hq, n_seqs, q_len, max_len)
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    L = layer.struct()
+    _check(load_library().kvq_attend_decode_mq(ctypes.byref(L), _ptr(q), _ptr(seq_len), n_seqs, q_len, hq,
+                                               max_len, softmax_scale, _ptr(out), _ptr(workspace),
+                                               workspace.numel(), _stream(stream)))
     return out
 
 

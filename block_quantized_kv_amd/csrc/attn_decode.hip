@@ -2,14 +2,17 @@
 // plus the log-sum-exp combine of the splits.  gfx950.
 //
 // What is computed (den_llama.cpp, "Results" / "What's in the fork":
-// FlashAttention reads the q8_0 / q4_0 / Q4_G64 K and V blocks directly):
-//   out[b][h] = sum_j softmax_j(scale * q[b][h] . k_hat_j) v_hat_j over the
-//   rows j < len_b of kv-head h / gqa.
+// FlashAttention reads the q8_0 / q4_0 / Q4_G64 K and V blocks directly;
+// "Ship command": up to two drafted tokens are verified per step): for each
+// of the q_len newest positions p_i = len_b - q_len + i,
+//   out[b][i][h] = sum_{j <= p_i} softmax_j(scale * q[b][i][h] . k_hat_j) v_hat_j
+// over kv-head h / gqa (q_len = 1 is plain decode).
 //
 // Design (one workgroup = 8 waves = one split of `split_rows` rows of one
 // (sequence, kv-head); the waves share the split's 32-row blocks):
-//  * The GQA group (<= 16 query heads) is the N side of 16x16x32 f16 matrix
-//    products, so every K/V byte is read once per kv-head:
+//  * The GQA group times the queries per sequence (<= 16 columns, each a
+//    (query, head) pair) is the N side of 16x16x32 f16 matrix products, so
+//    every K/V byte is read once per kv-head for all of them:
 //      S^T[row][head] = K[row][:] . Q'[:][head]   (A = K codes, B = query)
 //      O^T[ch][head] += V[ch][rows] . P^T[rows][head]
 //    The accumulator layout of S^T (lane = head + 16*q holds rows 4q..4q+3 of
@@ -268,8 +271,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     const int64_t r0 = (int64_t)sp * a.split_rows;
     if (r0 >= len) {  // whole workgroup: no barrier reached
         if (len == 0 && sp == 0) {  // an empty sequence attends nothing: output 0
-            float *dst = a.out + ((int64_t)b * a.n_q_heads + (int64_t)kvh * a.gqa) * D;
-            for (int i = threadIdx.x; i < a.gqa * D; i += kThreads) dst[i] = 0.0f;
+            for (int i = threadIdx.x; i < a.q_len * a.gqa * D; i += kThreads) {
+                const int col = i / D, qi = col / a.gqa, hh = col % a.gqa;
+                a.out[b * a.q_seq_stride + ((int64_t)qi * a.n_q_heads + (int64_t)kvh * a.gqa + hh) * D + i % D] = 0.0f;
+            }
         }
         return;
     }
@@ -282,6 +287,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     const int h = lane & 15, q4 = lane >> 4;
     const int x32 = 4 * (lane ^ 32);  // byte index of lane ^ 32 for ds_bpermute
     const int G = a.gqa;
+    const int NC = G * a.q_len;  // columns: (query, head) pairs, query-major
+    // this lane's column: query qi, head hh; it sees the rows of the split
+    // before nrows - cdelay (later rows are later queries' tokens)
+    const int qi = h < NC ? h / G : 0, hh = h < NC ? h % G : 0;
+    const int cdelay = a.q_tail + (a.q_len - 1 - qi);
+    const int maxdelay = a.q_tail + a.q_len - 1;
 
     const int64_t head_lin = (int64_t)b * a.k.n_kv_heads + kvh;
     Streams st;
@@ -298,10 +309,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     // ---- query prologue, part 1: wave w loads the slice of channel step w
     // (8 channels per lane)
     const bool preps = wave < C::KSTEPS;
-    const bool real = h < G;
+    const bool real = h < NC;
     float qv[8];
     {
-        const float *qp = a.q + ((int64_t)b * a.n_q_heads + (int64_t)kvh * G + (real ? h : 0)) * D +
+        const float *qp = a.q + b * a.q_seq_stride + ((int64_t)qi * a.n_q_heads + (int64_t)kvh * G + hh) * D +
                           32 * (preps ? wave : 0) + 8 * q4;
         const float4 x0 = *reinterpret_cast<const float4 *>(qp);
         const float4 x1 = *reinterpret_cast<const float4 *>(qp + 4);
@@ -396,7 +407,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
 
     // Computes block idx from its words.
     auto process = [&](Payload<D, KC, VC> &pl, int idx) {
-        const int rows_here = nrows - idx * kBlockRows;  // > 0
         // ---- scores S^T for the two 16-row tiles, channel steps in lockstep
         const f16_alias *ksc0 = reinterpret_cast<const f16_alias *>(pl.ks(0));
         const f16_alias *ksc1 = reinterpret_cast<const f16_alias *>(pl.ks(1));
@@ -434,13 +444,19 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) S[tau][r] *= c_h;
         uint32_t *vsw = pl.vs();
-        if (rows_here < kBlockRows) {
-            const int lim = rows_here - 4 * q4;  // row 16*tau + 4*q4 + r is valid iff 16*tau + r < lim
+        // rows from this block's start to the sequence end (capped: only
+        // whether it reaches past the block matters)
+        const int64_t rte64 = len - (r0 + (int64_t)idx * kBlockRows);
+        const int rend = rte64 < (1 << 20) ? (int)rte64 : (1 << 20);
+        if (rend - maxdelay < kBlockRows) {
+            // row 16*tau + 4*q4 + r is visible to this column iff 16*tau + r < lim
+            const int lim = rend - cdelay - 4 * q4;
 #pragma unroll
             for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     if (16 * tau + r >= lim) S[tau][r] = -INFINITY;
+            const int vlim = rend - 4 * q4;  // rows past the sequence end
             // rows past the end get a zero V scale, so that bytes that were
             // never written cannot turn 0 * V into NaN; word g*4+m holds the
             // scales of rows (m/2)*16 + 4*q4 + 2*(m%2) + {0, 1}
@@ -450,8 +466,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
                 for (int m = 0; m < 4; ++m) {
                     const int j0 = (m >> 1) * 16 + 2 * (m & 1);
                     uint32_t word = vsw[g * 4 + m];
-                    if (j0 >= lim) word &= 0xFFFF0000u;
-                    if (j0 + 1 >= lim) word &= 0x0000FFFFu;
+                    if (j0 >= vlim) word &= 0xFFFF0000u;
+                    if (j0 + 1 >= vlim) word &= 0x0000FFFFu;
                     vsw[g * 4 + m] = word;
                 }
         }
@@ -465,18 +481,23 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
         const bool raise = mx > m_run + kRescaleThreshold;
         if (__any(raise)) {
             const float m_new = raise ? mx : m_run;
-            const float alpha = fast_exp2(m_run - m_new);  // 0 on the first block
+            // 0 when raised from -inf; 1 for a lane that keeps its max (which
+            // may still be -inf: a column that sees no row yet)
+            const float alpha = raise ? fast_exp2(m_run - m_new) : 1.0f;
             l_run *= alpha;
 #pragma unroll
             for (int cb = 0; cb < C::CB; ++cb) O[cb] *= alpha;
             m_run = m_new;
         }
+        // a column that has seen no visible row yet keeps m_run = -inf; its
+        // scores here are all -inf too, and exp2(-inf - 0) = 0
+        const float mref = m_run > -INFINITY ? m_run : 0.0f;
         h8 P;
 #pragma unroll
         for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const float p = fast_exp2(S[tau][r] - m_run);
+                const float p = fast_exp2(S[tau][r] - mref);
                 l_run += p;
                 P[4 * tau + r] = (_Float16)p;
             }
@@ -528,37 +549,40 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     l_run = quad_sum(l_run, x32);
     __syncthreads();
     constexpr int DP = D + 4;                               // padded head stride
-    float *so = reinterpret_cast<float *>(smem);           // [wave][G][DP]
-    float *sm = so + kWaves * G * DP;                       // [wave][G]
-    float *sl = sm + kWaves * G;                            // [wave][G]
-    if (h < G) {
+    float *so = reinterpret_cast<float *>(smem);           // [wave][NC][DP]
+    float *sm = so + kWaves * NC * DP;                      // [wave][NC]
+    float *sl = sm + kWaves * NC;                           // [wave][NC]
+    if (h < NC) {
 #pragma unroll
         for (int cb = 0; cb < C::CB; ++cb)
-            *reinterpret_cast<f4 *>(&so[(wave * G + h) * DP + 16 * cb + 4 * q4]) = O[cb];
+            *reinterpret_cast<f4 *>(&so[(wave * NC + h) * DP + 16 * cb + 4 * q4]) = O[cb];
         if (q4 == 0) {
-            sm[wave * G + h] = m_run;
-            sl[wave * G + h] = l_run;
+            sm[wave * NC + h] = m_run;
+            sl[wave * NC + h] = l_run;
         }
     }
     __syncthreads();
     const int nsp = (int)((len + a.split_rows - 1) / a.split_rows);
-    for (int idx = tid; idx < G * D; idx += kThreads) {
-        const int hh = idx / D, c = idx % D;
+    for (int idx = tid; idx < NC * D; idx += kThreads) {
+        const int col = idx / D, c = idx % D;
         float M = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm[w * G + hh]);
+        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm[w * NC + col]);
+        const float Mref = M > -INFINITY ? M : 0.0f;  // -inf: no visible row in the split
         float o = 0.0f, L = 0.0f;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
-            const float e = fast_exp2(sm[w * G + hh] - M);  // 0 for waves without rows
-            o = fmaf(e, so[(w * G + hh) * DP + c], o);
-            L = fmaf(e, sl[w * G + hh], L);
+            const float e = fast_exp2(sm[w * NC + col] - Mref);  // 0 for waves without rows
+            o = fmaf(e, so[(w * NC + col) * DP + c], o);
+            L = fmaf(e, sl[w * NC + col], L);
         }
-        const int64_t qh = (int64_t)b * a.n_q_heads + (int64_t)kvh * G + hh;
+        const int cq = col / G, ch = col % G;
         if (nsp == 1) {
-            a.out[qh * D + c] = o / L;
+            a.out[b * a.q_seq_stride + ((int64_t)cq * a.n_q_heads + (int64_t)kvh * G + ch) * D + c] =
+                L > 0.0f ? o / L : 0.0f;
             continue;
         }
+        const int64_t qh = ((int64_t)b * a.q_len + cq) * a.n_q_heads + (int64_t)kvh * G + ch;
         const int64_t ph = qh * a.max_splits + sp;
         a.part_o[ph * D + c] = o;
         if (c == 0) {
@@ -568,19 +592,22 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     }
 }
 
-// Log-sum-exp merge of the splits of one (sequence, query head), 64 channels
+// Log-sum-exp merge of the splits of one (sequence, query, head), 64 channels
 // per workgroup: 4 thread groups take every 4th split; each thread issues the
 // loads of 16 splits at once and folds them into a running (max, sum, output)
-// triple, then the 4 groups merge through LDS.
+// triple, then the 4 groups merge through LDS.  A split in which the query
+// sees no row carries max -inf and sum 0; a query that sees no row at all
+// gets 0.
 template <int D>
 __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
     __shared__ float s_o[4][64], s_m[4][64], s_l[4][64];
-    const int hq = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+    const int hq = blockIdx.y, row = blockIdx.z, tid = threadIdx.x;
+    const int b = row / a.q_len, qi = row % a.q_len;
     int64_t len = a.seq_len[b];
     len = len < 0 ? 0 : (len > a.max_len ? a.max_len : len);
     const int nsp = (int)((len + a.split_rows - 1) / a.split_rows);
     if (nsp <= 1) return;  // the decode kernel wrote the output itself
-    const int64_t qh = (int64_t)b * a.n_q_heads + hq;
+    const int64_t qh = (int64_t)row * a.n_q_heads + hq;
     const int cl = tid & 63, sg = tid >> 6, c = blockIdx.x * 64 + cl;
     const float *ml = a.part_ml + 2 * qh * a.max_splits;
     const float *po = a.part_o + qh * a.max_splits * D + c;
@@ -598,13 +625,14 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
         }
         float mb = M;
 #pragma unroll
-        for (int u = 0; u < U; ++u) mb = fmaxf(mb, mv[u]);  // finite: split s0 exists
-        const float sc = fast_exp2(M - mb);                  // 0 on the first chunk
+        for (int u = 0; u < U; ++u) mb = fmaxf(mb, mv[u]);
+        const float mref = mb > -INFINITY ? mb : 0.0f;     // all -inf so far: nothing to scale
+        const float sc = fast_exp2(M - mref);              // 0 on the first chunk
         o *= sc;
         L *= sc;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const float e = fast_exp2(mv[u] - mb);
+            const float e = fast_exp2(mv[u] - mref);
             o = fmaf(e, ov[u], o);
             L = fmaf(e, lv[u], L);
         }
@@ -618,14 +646,15 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
         float Mt = s_m[0][cl];
 #pragma unroll
         for (int g = 1; g < 4; ++g) Mt = fmaxf(Mt, s_m[g][cl]);
+        const float Mref = Mt > -INFINITY ? Mt : 0.0f;
         float on = 0.0f, Ln = 0.0f;
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-            const float e = fast_exp2(s_m[g][cl] - Mt);  // 0 for a group without splits
+            const float e = fast_exp2(s_m[g][cl] - Mref);  // 0 for a group without splits
             on = fmaf(e, s_o[g][cl], on);
             Ln = fmaf(e, s_l[g][cl], Ln);
         }
-        a.out[qh * D + c] = on / Ln;
+        a.out[b * a.q_seq_stride + ((int64_t)qi * a.n_q_heads + hq) * D + c] = Ln > 0.0f ? on / Ln : 0.0f;
     }
 }
 
@@ -633,7 +662,7 @@ template <int D, int KC, int VC>
 hipError_t launch_typed(const DecodeArgs &a, hipStream_t s) {
     using C = Cfg<D, KC, VC>;
     const size_t stream_lds = (size_t)C::LDS_STREAM;
-    const size_t merge_lds = (size_t)kWaves * a.gqa * (D + 4 + 2) * sizeof(float);
+    const size_t merge_lds = (size_t)kWaves * a.gqa * a.q_len * (D + 4 + 2) * sizeof(float);
     const size_t lds = stream_lds > merge_lds ? stream_lds : merge_lds;
     const dim3 grid((unsigned)a.max_splits, (unsigned)a.k.n_kv_heads, (unsigned)a.n_seqs);
     if (lds > 65536) {
@@ -644,7 +673,7 @@ hipError_t launch_typed(const DecodeArgs &a, hipStream_t s) {
     decode_kernel<D, KC, VC><<<grid, dim3(kThreads), lds, s>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.max_splits <= 1) return e;
-    combine_kernel<D><<<dim3(D / 64, (unsigned)a.n_q_heads, (unsigned)a.n_seqs), dim3(256), 0, s>>>(a);
+    combine_kernel<D><<<dim3(D / 64, (unsigned)a.n_q_heads, (unsigned)(a.n_seqs * a.q_len)), dim3(256), 0, s>>>(a);
     return hipGetLastError();
 }
 
@@ -666,7 +695,8 @@ hipError_t launch_d(const DecodeArgs &a, hipStream_t s) {
 
 }  // namespace
 
-DecodePlan plan_decode(int head_dim, int n_kv_heads, int n_q_heads, int n_seqs, int64_t max_len) {
+DecodePlan plan_decode(int head_dim, int n_kv_heads, int n_q_heads, int n_seqs, int64_t max_len,
+                       int q_len) {
     // Enough rows per workgroup that the partials stay small next to the KV
     // bytes, few enough that ~one workgroup per compute unit (256) is busy;
     // long multi-sequence calls get more, shorter splits for load balance.
@@ -681,8 +711,8 @@ DecodePlan plan_decode(int head_dim, int n_kv_heads, int n_q_heads, int n_seqs, 
     p.max_splits = (int)((max_len + p.split_rows - 1) / p.split_rows);
     if (p.max_splits < 1) p.max_splits = 1;
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
-    p.part_ml_bytes = (size_t)n_seqs * n_q_heads * p.max_splits * 2 * sizeof(float);
-    p.part_o_bytes = (size_t)n_seqs * n_q_heads * p.max_splits * head_dim * sizeof(float);
+    p.part_ml_bytes = (size_t)n_seqs * q_len * n_q_heads * p.max_splits * 2 * sizeof(float);
+    p.part_o_bytes = (size_t)n_seqs * q_len * n_q_heads * p.max_splits * head_dim * sizeof(float);
     p.off_part_ml = 0;
     p.off_part_o = p.off_part_ml + up(p.part_ml_bytes);
     p.total_bytes = p.off_part_o + up(p.part_o_bytes);

@@ -321,7 +321,7 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
                 const bool raise = mx > m_run[nt] + kPRescaleThreshold;
                 if (__any(raise)) {
                     const float m_new = raise ? mx : m_run[nt];
-                    const float alpha = fast_exp2(m_run[nt] - m_new);
+                    const float alpha = raise ? fast_exp2(m_run[nt] - m_new) : 1.0f;
                     l_run[nt] *= alpha;
 #pragma unroll
                     for (int cb = 0; cb < C::CB; ++cb) O[nt][cb] *= alpha;

@@ -131,24 +131,38 @@ kvq_status kvq_append(const kvq_layer *L, const float *k_new, const float *v_new
     return hip_status(kvq::launch_append(a, static_cast<hipStream_t>(hip_stream)), "append launch");
 }
 
-size_t kvq_decode_workspace_bytes(const kvq_layer *L, int32_t n_q_heads, int32_t n_seqs,
-                                  int64_t max_len) {
-    if (!L || n_q_heads <= 0 || n_seqs <= 0 || max_len < 0) return 0;
-    const kvq::DecodePlan p =
-        kvq::plan_decode(L->k.head_dim, L->k.n_kv_heads, n_q_heads, n_seqs, max_len);
+namespace {
+
+// Queries per launch: the (query, head) columns of one kv-head fill at most
+// the 16 columns of a matrix-core tile.
+int queries_per_launch(int gqa, int q_len) {
+    const int per = KVQ_MAX_GQA / gqa;
+    return q_len < per ? q_len : per;
+}
+
+size_t decode_ws_bytes(const kvq_layer *L, int32_t n_q_heads, int32_t n_seqs, int32_t q_len,
+                       int64_t max_len) {
+    if (!L || n_q_heads <= 0 || n_seqs <= 0 || q_len <= 0 || max_len < 0 || L->k.n_kv_heads <= 0 ||
+        n_q_heads % L->k.n_kv_heads != 0)
+        return 0;
+    const int gqa = n_q_heads / L->k.n_kv_heads;
+    if (gqa > KVQ_MAX_GQA) return 0;
+    const kvq::DecodePlan p = kvq::plan_decode(L->k.head_dim, L->k.n_kv_heads, n_q_heads, n_seqs, max_len,
+                                               queries_per_launch(gqa, q_len));
     return p.total_bytes;
 }
 
-kvq_status kvq_attend_decode(const kvq_layer *L, const float *q, const int64_t *seq_len,
-                             int32_t n_seqs, int32_t n_q_heads, int64_t max_len,
-                             float softmax_scale, float *out, void *workspace, size_t ws_bytes,
-                             void *hip_stream) {
+kvq_status attend_decode(const kvq_layer *L, const float *q, const int64_t *seq_len, int32_t n_seqs,
+                         int32_t q_len, int32_t n_q_heads, int64_t max_len, float softmax_scale, float *out,
+                         void *workspace, size_t ws_bytes, void *hip_stream) {
     kvq_status st = check_layer(L);
     if (st != KVQ_OK) return st;
     if (!q || !seq_len || !out) return fail(KVQ_EINVAL, "null q/seq_len/out");
     if (!aligned(q, 16) || !aligned(out, 16)) return fail(KVQ_EINVAL, "q/out not 16-byte aligned");
     if (n_seqs <= 0 || n_seqs > L->k.n_seqs)
         return fail(KVQ_EINVAL, "n_seqs %d outside [1, %d]", n_seqs, L->k.n_seqs);
+    if (q_len <= 0 || q_len > KVQ_MAX_QUERIES)
+        return fail(KVQ_EINVAL, "q_len %d outside [1, %d]", q_len, KVQ_MAX_QUERIES);
     if (n_q_heads <= 0 || n_q_heads % L->k.n_kv_heads != 0)
         return fail(KVQ_EINVAL, "n_q_heads %d not a multiple of n_kv_heads %d", n_q_heads,
                     L->k.n_kv_heads);
@@ -161,22 +175,21 @@ kvq_status kvq_attend_decode(const kvq_layer *L, const float *q, const int64_t *
     if (!(softmax_scale == softmax_scale)) return fail(KVQ_EINVAL, "softmax_scale is NaN");
     if (!kvq::decode_supported(L->k.codec, L->v.codec, L->k.head_dim))
         return fail(KVQ_EUNSUPPORTED, "no decode kernel for this codec pair/head_dim");
-    const size_t need = kvq_decode_workspace_bytes(L, n_q_heads, n_seqs, max_len);
+    const size_t need = decode_ws_bytes(L, n_q_heads, n_seqs, q_len, max_len);
     if (!workspace || ws_bytes < need)
         return fail(KVQ_EWORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
     if (!aligned(workspace, 256)) return fail(KVQ_EINVAL, "workspace not 256-byte aligned");
 
+    const int per = queries_per_launch(gqa, q_len);
     const kvq::DecodePlan p =
-        kvq::plan_decode(L->k.head_dim, L->k.n_kv_heads, n_q_heads, n_seqs, max_len);
+        kvq::plan_decode(L->k.head_dim, L->k.n_kv_heads, n_q_heads, n_seqs, max_len, per);
     if (p.max_splits > 16384)
         return fail(KVQ_EUNSUPPORTED, "max_len %lld needs %d splits (limit 16384)",
                     (long long)max_len, p.max_splits);
     kvq::DecodeArgs a;
     a.k = view(L->k);
     a.v = view(L->v);
-    a.q = q;
     a.seq_len = seq_len;
-    a.out = out;
     char *ws = static_cast<char *>(workspace);
     a.part_ml = reinterpret_cast<float *>(ws + p.off_part_ml);
     a.part_o = reinterpret_cast<float *>(ws + p.off_part_o);
@@ -187,7 +200,47 @@ kvq_status kvq_attend_decode(const kvq_layer *L, const float *q, const int64_t *
     a.split_rows = p.split_rows;
     a.max_splits = p.max_splits;
     a.scale_log2 = softmax_scale * 1.4426950408889634f;
-    return hip_status(kvq::launch_decode(a, static_cast<hipStream_t>(hip_stream)), "decode launch");
+    const int64_t qstride = (int64_t)n_q_heads * L->k.head_dim;  // floats per query
+    a.q_seq_stride = (int64_t)q_len * qstride;
+    // launches of `per` queries each, in order on the stream (they share the
+    // workspace)
+    for (int first = 0; first < q_len; first += per) {
+        a.q_len = q_len - first < per ? q_len - first : per;
+        a.q_tail = q_len - first - a.q_len;
+        a.q = q + first * qstride;
+        a.out = out + first * qstride;
+        st = hip_status(kvq::launch_decode(a, static_cast<hipStream_t>(hip_stream)), "decode launch");
+        if (st != KVQ_OK) return st;
+    }
+    return KVQ_OK;
+}
+
+}  // namespace
+
+size_t kvq_decode_workspace_bytes(const kvq_layer *L, int32_t n_q_heads, int32_t n_seqs,
+                                  int64_t max_len) {
+    return decode_ws_bytes(L, n_q_heads, n_seqs, 1, max_len);
+}
+
+kvq_status kvq_attend_decode(const kvq_layer *L, const float *q, const int64_t *seq_len,
+                             int32_t n_seqs, int32_t n_q_heads, int64_t max_len,
+                             float softmax_scale, float *out, void *workspace, size_t ws_bytes,
+                             void *hip_stream) {
+    return attend_decode(L, q, seq_len, n_seqs, 1, n_q_heads, max_len, softmax_scale, out, workspace,
+                         ws_bytes, hip_stream);
+}
+
+size_t kvq_decode_mq_workspace_bytes(const kvq_layer *L, int32_t n_q_heads, int32_t n_seqs,
+                                     int32_t q_len, int64_t max_len) {
+    return decode_ws_bytes(L, n_q_heads, n_seqs, q_len, max_len);
+}
+
+kvq_status kvq_attend_decode_mq(const kvq_layer *L, const float *q, const int64_t *seq_len,
+                                int32_t n_seqs, int32_t q_len, int32_t n_q_heads, int64_t max_len,
+                                float softmax_scale, float *out, void *workspace, size_t ws_bytes,
+                                void *hip_stream) {
+    return attend_decode(L, q, seq_len, n_seqs, q_len, n_q_heads, max_len, softmax_scale, out, workspace,
+                         ws_bytes, hip_stream);
 }
 
 size_t kvq_prefill_workspace_bytes(const kvq_layer *L, int32_t n_q_heads, int32_t n_tokens) {

@@ -43,14 +43,20 @@ struct DequantArgs {
 
 struct DecodeArgs {
     PlaneView k, v;
-    const float *q;          // [n_seqs][Hq][D]
+    // q and out hold q_len consecutive queries per sequence ([q_len][Hq][D] at
+    // q + b * q_seq_stride); query i of sequence b sits at row
+    // len_b - 1 - q_tail - (q_len - 1 - i) and attends rows up to it.
+    const float *q;
     const int64_t *seq_len;  // [n_seqs]
-    float *out;              // [n_seqs][Hq][D]
-    float *part_o;           // [n_seqs][Hq][max_splits][D]
-    float *part_ml;          // [n_seqs][Hq][max_splits][2]  (max in log2 units, sum)
+    float *out;
+    float *part_o;           // [n_seqs][q_len][Hq][max_splits][D]
+    float *part_ml;          // [n_seqs][q_len][Hq][max_splits][2]  (max in log2 units, sum)
     int n_seqs;
     int n_q_heads;
     int gqa;                 // q-heads per kv-head
+    int q_len;               // queries per sequence in this launch (gqa * q_len <= 16)
+    int q_tail;              // later queries of the same sequences (other launches)
+    int64_t q_seq_stride;    // floats between sequences in q and out
     int64_t max_len;
     int split_rows;          // multiple of 256
     int max_splits;
@@ -78,7 +84,8 @@ struct DecodePlan {
     // byte offsets inside the workspace
     size_t off_part_ml, off_part_o, total_bytes;
 };
-DecodePlan plan_decode(int head_dim, int n_kv_heads, int n_q_heads, int n_seqs, int64_t max_len);
+DecodePlan plan_decode(int head_dim, int n_kv_heads, int n_q_heads, int n_seqs, int64_t max_len,
+                       int q_len);
 
 hipError_t launch_append(const AppendArgs &a, hipStream_t s);
 hipError_t launch_dequant(const DequantArgs &a, hipStream_t s);

@@ -60,6 +60,7 @@ extern "C" {
 
 #define KVQ_BLOCK_ROWS 32
 #define KVQ_MAX_GQA 16 /* q-heads per kv-head supported by the attention kernels */
+#define KVQ_MAX_QUERIES 64 /* queries per sequence in one kvq_attend_decode_mq call */
 
 typedef enum { KVQ_Q8_0 = 0, KVQ_Q4_0 = 1, KVQ_Q4_G64 = 2 } kvq_codec;
 
@@ -156,6 +157,31 @@ kvq_status kvq_attend_decode(const kvq_layer *L, const float *q, const int64_t *
                              int32_t n_seqs, int32_t n_q_heads, int64_t max_len,
                              float softmax_scale, float *out, void *workspace, size_t ws_bytes,
                              void *hip_stream);
+
+/* ---- multi-query decode (den_llama.cpp, "Ship command": the server drafts
+ * up to two tokens per step with multi-token prediction, so a verifying decode
+ * step attends from the newest q_len positions at once) ----------------------- */
+
+/* Workspace bytes kvq_attend_decode_mq needs for these sizes (host only). */
+size_t kvq_decode_mq_workspace_bytes(const kvq_layer *L, int32_t n_q_heads, int32_t n_seqs,
+                                     int32_t q_len, int64_t max_len);
+
+/* q_len queries per sequence, at the newest positions of the sequence: with
+ * len_b = min(seq_len[b], max_len), query i (0 <= i < q_len) sits at row
+ * p = len_b - q_len + i, whose K/V are already appended, and attends rows
+ * [0, p] (causal among the new tokens, itself included):
+ *   out[b][i][h] = sum_{j <= p} softmax_j(softmax_scale * q[b][i][h] . k_hat[b][g][j]) v_hat[b][g][j]
+ * A query with p < 0 attends nothing: its output is 0.
+ *   q   : fp32 [n_seqs][q_len][n_q_heads][head_dim], device
+ *   out : fp32 [n_seqs][q_len][n_q_heads][head_dim], device
+ *   q_len in [1, KVQ_MAX_QUERIES]; every other argument as for
+ *   kvq_attend_decode (which is this call with q_len = 1).
+ * Every K/V byte is read once per kv-head for up to 16 / (n_q_heads /
+ * n_kv_heads) queries at a time (one launch per such group of queries). */
+kvq_status kvq_attend_decode_mq(const kvq_layer *L, const float *q, const int64_t *seq_len,
+                                int32_t n_seqs, int32_t q_len, int32_t n_q_heads, int64_t max_len,
+                                float softmax_scale, float *out, void *workspace, size_t ws_bytes,
+                                void *hip_stream);
 
 /* ---- chunked-prefill attention (den_llama.cpp, "Results": prefill with the
  * quantized cache and 2048-token micro-batches; Llaminar, "GPU Graph

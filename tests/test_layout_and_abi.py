@@ -96,6 +96,24 @@ def test_validation_errors_return_before_launch():
     assert B.kvq_status_str(4).startswith("KVQ_EWORKSPACE")
 
 
+def test_multi_query_decode_validation():
+    lib = B.load_library()
+    good = B._Layer(_fake_plane(role=0), _fake_plane(codec="q4_0", role=1, codes=0x30000, scales=0x40000))
+
+    def call(q_len, hq=4, ws_bytes=1 << 30):
+        return lib.kvq_attend_decode_mq(ctypes.byref(good), 0x1000, 0x2000, 1, q_len, hq, 64, 0.1, 0x3000,
+                                        0x4000, ws_bytes, None)
+    assert call(0) == 1                 # no query
+    assert call(65) == 1                # above KVQ_MAX_QUERIES
+    assert call(2, hq=3) == 1           # not a multiple of Hkv
+    assert call(2, ws_bytes=16) == 4    # workspace too small
+    # the partials of one launch hold at most 16 / gqa queries: the workspace
+    # grows with q_len up to that and no further (gqa 2 -> 8 queries)
+    ws = [lib.kvq_decode_mq_workspace_bytes(ctypes.byref(good), 4, 1, n, 64) for n in (1, 2, 8, 9, 64)]
+    assert ws[0] == lib.kvq_decode_workspace_bytes(ctypes.byref(good), 4, 1, 64)
+    assert ws[0] < ws[1] < ws[2] == ws[3] == ws[4]
+
+
 def test_decode_workspace_grows_with_length():
     good = B._Layer(_fake_plane(cap=1 << 17), _fake_plane(role=1, cap=1 << 17, codes=0x30000, scales=0x40000))
     lib = B.load_library()
