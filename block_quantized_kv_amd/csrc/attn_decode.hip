@@ -270,7 +270,20 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     len = len < 0 ? 0 : (len > a.max_len ? a.max_len : len);
     const int64_t r0 = (int64_t)sp * a.split_rows;
     if (r0 >= len) {  // whole workgroup: no barrier reached
-        if (len == 0 && sp == 0) {  // an empty sequence attends nothing: output 0
+        if (a.max_splits > 1) {
+            // an empty split: its partials merge as nothing (max -inf, sum 0,
+            // o 0), so the combine needs no lengths
+            for (int i = threadIdx.x; i < a.q_len * a.gqa * D; i += kThreads) {
+                const int col = i / D, qi = col / a.gqa, hh = col % a.gqa;
+                const int64_t ph = (((int64_t)b * a.q_len + qi) * a.n_q_heads + (int64_t)kvh * a.gqa + hh) *
+                                       a.max_splits + sp;
+                a.part_o[ph * D + i % D] = 0.0f;
+                if (i % D == 0) {
+                    a.part_ml[2 * ph] = -INFINITY;
+                    a.part_ml[2 * ph + 1] = 0.0f;
+                }
+            }
+        } else {  // one split and an empty sequence: output 0
             for (int i = threadIdx.x; i < a.q_len * a.gqa * D; i += kThreads) {
                 const int col = i / D, qi = col / a.gqa, hh = col % a.gqa;
                 a.out[b * a.q_seq_stride + ((int64_t)qi * a.n_q_heads + (int64_t)kvh * a.gqa + hh) * D + i % D] = 0.0f;
@@ -562,7 +575,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
         }
     }
     __syncthreads();
-    const int nsp = (int)((len + a.split_rows - 1) / a.split_rows);
     for (int idx = tid; idx < NC * D; idx += kThreads) {
         const int col = idx / D, c = idx % D;
         float M = -INFINITY;
@@ -577,7 +589,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
             L = fmaf(e, sl[w * NC + col], L);
         }
         const int cq = col / G, ch = col % G;
-        if (nsp == 1) {
+        if (a.max_splits == 1) {  // the call has one split: write the output
             a.out[b * a.q_seq_stride + ((int64_t)cq * a.n_q_heads + (int64_t)kvh * G + ch) * D + c] =
                 L > 0.0f ? o / L : 0.0f;
             continue;
@@ -595,18 +607,15 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
 // Log-sum-exp merge of the splits of one (sequence, query, head), 64 channels
 // per workgroup: 4 thread groups take every 4th split; each thread issues the
 // loads of 16 splits at once and folds them into a running (max, sum, output)
-// triple, then the 4 groups merge through LDS.  A split in which the query
-// sees no row carries max -inf and sum 0; a query that sees no row at all
-// gets 0.
+// triple, then the 4 groups merge through LDS.  Every split of the call has
+// a partial (an empty or invisible one carries max -inf, sum 0, o 0), so no
+// length is read; a query that sees no row at all gets 0.
 template <int D>
 __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
     __shared__ float s_o[4][64], s_m[4][64], s_l[4][64];
     const int hq = blockIdx.y, row = blockIdx.z, tid = threadIdx.x;
     const int b = row / a.q_len, qi = row % a.q_len;
-    int64_t len = a.seq_len[b];
-    len = len < 0 ? 0 : (len > a.max_len ? a.max_len : len);
-    const int nsp = (int)((len + a.split_rows - 1) / a.split_rows);
-    if (nsp <= 1) return;  // the decode kernel wrote the output itself
+    const int nsp = a.max_splits;
     const int64_t qh = (int64_t)row * a.n_q_heads + hq;
     const int cl = tid & 63, sg = tid >> 6, c = blockIdx.x * 64 + cl;
     const float *ml = a.part_ml + 2 * qh * a.max_splits;
