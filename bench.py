@@ -42,6 +42,7 @@ def _args():
     p.add_argument("--warmup", type=int, default=50)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-prefill", action="store_true")
+    p.add_argument("--no-quality", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run plain 256 MiB device copies (HBM counter calibration)")
@@ -354,6 +355,8 @@ def main():
 
     if not args.no_prefill:
         result["prefill"] = run_prefill(torch, dev, args)
+    if not args.no_quality:
+        result["quality"] = run_quality(torch, dev, args)
 
     if host_kv is not None:
         result["cpu_baseline"] = cpu_baseline(cfg, host_kv, q.cpu().numpy(), nb, args.cpu_seconds)
@@ -399,6 +402,54 @@ def run_prefill(torch, dev, args):
                        "k_codec": kc, "v_codec": vc},
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": None}}
+
+
+def run_quality(torch, dev, args):
+    """Model-free quality of the codecs (the pages' KL-divergence runs need the
+    model): on the 32K (outlier channels) and 64K (per-channel scales)
+    decode distributions, the GPU decode output over each codec pair against
+    exact binary64 attention over the unquantized fp32 K/V, and the softmax KL
+    divergence between attention over the exact keys and over the keys as the
+    GPU dequantizes them (mean and max over query heads, nats)."""
+    import workloads
+    from block_quantized_kv_amd import Layer, kvq_append, kvq_attend_decode, kvq_dequant
+    res = {}
+    for cid in (2, 3):
+        cfg = workloads.CONFIGS[cid]
+        n, H, d, hq = cfg.ctx, cfg.n_kv_heads, cfg.head_dim, cfg.n_q_heads
+        G = hq // H
+        k = workloads.kv_rows(cfg, 0, 0, "k", 0, n, dev)
+        v = workloads.kv_rows(cfg, 0, 0, "v", 0, n, dev)
+        q = workloads.queries(cfg, 0, dev)
+        kd = k.double().cpu().permute(1, 0, 2)      # [H][n][d]
+        vd = v.double().cpu().permute(1, 0, 2)
+        qd = q[0].double().cpu().view(H, G, d)
+        s_exact = torch.einsum("hgd,hnd->hgn", qd, kd) * cfg.scale
+        p_exact = torch.softmax(s_exact, dim=-1)
+        ref = torch.einsum("hgn,hnd->hgd", p_exact, vd).reshape(hq, d)
+        logp_exact = torch.log_softmax(s_exact, dim=-1)
+        entry = {}
+        for kc, vc in (("q8_0", "q8_0"), ("q4_0", "q4_0"), ("q4_g64", "q4_g64"), ("q8_0", "q4_0")):
+            layer = Layer.create(kc, vc, d, H, 1, cfg.capacity, device=dev)
+            for a in range(0, n, 16384):
+                b = min(n, a + 16384)
+                kvq_append(layer, k[a:b].contiguous(), v[a:b].contiguous(),
+                           torch.zeros(b - a, dtype=torch.int32, device=dev),
+                           torch.arange(a, b, dtype=torch.int64, device=dev))
+            out = kvq_attend_decode(layer, q, torch.tensor([n], dtype=torch.int64, device=dev), n,
+                                    cfg.scale)[0].double().cpu()
+            khat = kvq_dequant(layer.k, 0, 0, n).double().cpu()
+            s_q = torch.einsum("hgd,hnd->hgn", qd, khat) * cfg.scale
+            kl = (p_exact * (logp_exact - torch.log_softmax(s_q, dim=-1))).sum(-1).reshape(-1)
+            err = (out - ref).abs()
+            entry[f"{kc}/{vc}"] = {
+                "out_max_rel_err": round(float(err.max() / ref.abs().max()), 6),
+                "out_rms_rel_err": round(float(err.pow(2).sum().sqrt() / ref.pow(2).sum().sqrt()), 6),
+                "softmax_kl_mean": float(f"{kl.mean().item():.4e}"),
+                "softmax_kl_max": float(f"{kl.max().item():.4e}")}
+            del layer
+        res[cfg.name] = entry
+    return res
 
 
 def cpu_baseline(cfg, host_kv, q, nb, seconds):
