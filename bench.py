@@ -43,6 +43,7 @@ def _args():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-quality", action="store_true")
+    p.add_argument("--no-baselines", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run plain 256 MiB device copies (HBM counter calibration)")
@@ -353,6 +354,14 @@ def main():
                              "tokens_per_s": round(2 / (mq_ms * 1e-3), 1),
                              "step": "kvq_append(2 tokens) + kvq_attend_decode_mq(q_len 2), eager"}
 
+    if not args.no_baselines:
+        bl = run_baselines(torch, dev, cfg, caches, q, seq_len, cfg.scale, max(8, min(args.steps, 64)))
+        bl["direct_quantized_attend_ms"] = round(att_avg_ms, 4)
+        bl["speedup_vs_f16_control"] = round(bl["f16_control"]["ms_per_attend"] / att_avg_ms, 2)
+        bl["speedup_vs_dequant_once"] = round(bl["dequant_once"]["ms_per_attend"] / att_avg_ms, 2)
+        # no f16 decode, however good, can move its 4x larger K/V faster than HBM peak
+        bl["f16_hbm_floor_ms"] = round(bl["f16_control"]["kv_bytes"] / (HBM_PEAK_GBS * 1e9) * 1e3, 4)
+        result["baselines"] = bl
     if not args.no_prefill:
         result["prefill"] = run_prefill(torch, dev, args)
     if not args.no_quality:
@@ -402,6 +411,61 @@ def run_prefill(torch, dev, args):
                        "k_codec": kc, "v_codec": vc},
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": None}}
+
+
+def run_baselines(torch, dev, cfg, caches, q, seq_len, scale, steps):
+    """What reading the quantized blocks directly saves, on the same 64K
+    decode: (1) an f16 control -- the K/V kept unquantized in binary16 and
+    attended with PyTorch's batched matrix products (rocBLAS/hipBLASLt) and
+    softmax; (2) dequant-once -- kvq_dequant of the quantized cache to fp32,
+    cast to binary16, then the same attention.  Both are vendor baselines,
+    not this library's kernels; K/V rotate over independent copies (>= 1 GB)."""
+    from block_quantized_kv_amd import kvq_dequant
+    n, H, d, hq = cfg.ctx, cfg.n_kv_heads, cfg.head_dim, cfg.n_q_heads
+    G = hq // H
+    qg = q[0].view(H, G, d).half().transpose(1, 2).contiguous()   # [H][d][G]
+
+    def attend_f16(kh, vh):
+        s = torch.bmm(kh, qg).float() * scale                       # [H][n][G]
+        p = torch.softmax(s, dim=1).half().transpose(1, 2).contiguous()  # [H][G][n]
+        return torch.bmm(p, vh)                                    # [H][G][d]
+
+    rot = 4  # 4 x 268 MB of f16 K/V
+    gen = torch.Generator(device=dev).manual_seed(11)
+    kv16 = [(torch.randn(H, n, d, device=dev, generator=gen).half(),
+             torch.randn(H, n, d, device=dev, generator=gen).half()) for _ in range(rot)]
+    for i in range(4):
+        attend_f16(*kv16[i % rot])
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        attend_f16(*kv16[i % rot])
+    e1.record()
+    torch.cuda.synchronize()
+    f16_ms = e0.elapsed_time(e1) / steps
+    del kv16
+
+    def dequant_once(L):
+        kh = kvq_dequant(L.k, 0, 0, n).half()
+        vh = kvq_dequant(L.v, 0, 0, n).half()
+        return attend_f16(kh, vh)
+
+    for i in range(2):
+        dequant_once(caches[i % len(caches)])
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(steps):
+        dequant_once(caches[i % len(caches)])
+    e1.record()
+    torch.cuda.synchronize()
+    dq_ms = e0.elapsed_time(e1) / steps
+    f16_bytes = 2 * H * n * d * 2
+    return {"f16_control": {"ms_per_attend": round(f16_ms, 4), "kv_bytes": f16_bytes,
+                            "gbs": round(f16_bytes / (f16_ms * 1e-3) / 1e9, 1),
+                            "how": "binary16 K/V, torch.bmm + softmax + torch.bmm"},
+            "dequant_once": {"ms_per_attend": round(dq_ms, 4),
+                             "how": "kvq_dequant (fp32) -> binary16 -> the f16 control's attention"}}
 
 
 def run_quality(torch, dev, args):
