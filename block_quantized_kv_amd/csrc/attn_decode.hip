@@ -34,9 +34,11 @@
 //  * Streaming: blocks travel HBM -> LDS by buffer-to-LDS DMA, which holds no
 //    registers while in flight.  Each wave owns a ring of NS block slots in
 //    LDS (byte layout = the cache's); it copies the oldest slot into
-//    registers, immediately refills that slot with the block NS*8 further on
-//    and computes from the registers, so NS blocks per wave are always on
-//    their way.  The compiler cannot see which LDS bytes a DMA writes (it
+//    registers, immediately refills that slot with the next block of the
+//    split (handed out by an LDS counter, so fast waves take more) and
+//    computes from the registers, so NS blocks per wave are always on their
+//    way.  NS keeps about 72 KB per workgroup in flight: deeper rings only
+//    lengthen the memory queues.  The compiler cannot see which LDS bytes a DMA writes (it
 //    would wait for every DMA before any LDS read), so the slot reads are
 //    hand-issued with an explicit wait for exactly the DMAs of that slot.
 //    Every DMA is issued unconditionally: one past the end of the split is
@@ -44,7 +46,8 @@
 //  * The query operand (hi/lo halves for every channel step) and the bias
 //    corrections are prepared once per workgroup, each wave taking one channel
 //    step, and shared through LDS.
-//  * The 8 waves merge through LDS; each workgroup writes one partial
+//  * The 8 waves merge through LDS (each rescales its own O to the common
+//    max, then the copies are summed); each workgroup writes one partial
 //    (unnormalized O, max, sum) per query head, or the final output when the
 //    sequence fits in one split; combine_kernel merges the splits
 //    (log-sum-exp) with many partial loads in flight at once.
@@ -61,6 +64,7 @@ constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kLdsBytes = 160 * 1024;  // per workgroup on gfx950
 constexpr float kRescaleThreshold = 8.0f;
+constexpr int kInflightBytes = 72 * 1024;  // target DMA bytes in flight per workgroup
 
 // number of DMA instructions that copy a region of B bytes (1 KB per dwordx4
 // DMA, 256 B per dword DMA, a lane-masked dword DMA for a shorter tail)
@@ -106,14 +110,26 @@ struct Cfg {
     static constexpr int OFF_TMAX = OFF_QOP + KSTEPS * 2 * 64 * 16;   // [KSTEPS][16] fp32
     static constexpr int OFF_CORR = OFF_TMAX + KSTEPS * 16 * 4;       // [KSTEPS][16] fp32
     static constexpr int OFF_CNT = OFF_CORR + KSTEPS * 16 * 4;        // block hand-out counter
-    static constexpr int OFF_SLOTS = OFF_CNT + 16;                    // [wave][NS] slots
+    static constexpr int OFF_ML = OFF_CNT + 16;                       // [wave][16] (max, sum)
+    static constexpr int OFF_FIN = OFF_ML + kWaves * 16 * 8;          // [16] merged (max, sum)
+    static constexpr int OFF_SLOTS = OFF_FIN + 16 * 8;                // [wave][NS] slots
+    // Ring depth: about 72 KB of blocks in flight per compute unit.  More
+    // only lengthens the memory queues (and the spread of completion times
+    // at the end of a split) without raising the streaming rate: at 64K
+    // context a one-block ring (70 KB) beats two (140 KB) by ~10%.
     static constexpr int NS_FIT = (kLdsBytes - OFF_SLOTS) / (kWaves * SLOT);
-    static constexpr int NS = NS_FIT > 3 ? 3 : NS_FIT;
+    static constexpr int NS_TGT = kInflightBytes / (kWaves * SLOT) < 1 ? 1 : kInflightBytes / (kWaves * SLOT);
+    static constexpr int NS = NS_TGT < NS_FIT ? (NS_TGT < 3 ? NS_TGT : 3) : NS_FIT;
     static_assert(NS >= 1, "one block slot per wave must fit in LDS");
     static_assert((NS - 1) * N_DMA <= 63, "DMAs in flight exceed the wait counter");
     static_assert(SL_V % 16 == 0 && SL_KS % 16 == 0 && SL_VS % 16 == 0 && SLOT % 16 == 0, "slot alignment");
     static_assert((NS - 1) * SLOT + SLOT <= 65535, "slot offsets fit the DS immediate");
     static constexpr int LDS_STREAM = OFF_SLOTS + kWaves * NS * SLOT;
+    // the final merge parks every wave's output columns, DP floats apart
+    // (D + 16: conflict-free 16-byte writes), from OFF_SLOTS on
+    static constexpr int DP = D + 16;
+    static constexpr int LDS_MERGE_MAX = OFF_SLOTS + kWaves * 16 * DP * 4;
+    static_assert(LDS_MERGE_MAX <= kLdsBytes, "the merge fits in LDS");
 };
 
 // Raw buffer descriptor (base in SGPRs, byte range checked by the hardware).
@@ -557,46 +573,63 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
         }(std::make_integer_sequence<int, NS>{});
     }
 
-    // ---- merge the waves through LDS (the compiler waits for any DMA still
-    // in flight before these LDS accesses)
+    // ---- merge the waves.  Each wave publishes its (max, sum) per column;
+    // after one barrier (which also waited for every wave's last DMAs, so
+    // the slots are idle) every wave rescales its O to the columns' common
+    // max and parks it in the slot area; after a second barrier the threads
+    // add up the 8 parked copies, 4 channels each.
     l_run = quad_sum(l_run, x32);
+    float *sml = reinterpret_cast<float *>(smem + C::OFF_ML);    // [wave][16][2]
+    float *sfin = reinterpret_cast<float *>(smem + C::OFF_FIN);  // [16][2]
+    if (h < NC && q4 == 0) {
+        sml[(wave * 16 + h) * 2] = m_run;
+        sml[(wave * 16 + h) * 2 + 1] = l_run;
+    }
     __syncthreads();
-    constexpr int DP = D + 4;                               // padded head stride
-    float *so = reinterpret_cast<float *>(smem);           // [wave][NC][DP]
-    float *sm = so + kWaves * NC * DP;                      // [wave][NC]
-    float *sl = sm + kWaves * NC;                           // [wave][NC]
     if (h < NC) {
+        float M = -INFINITY;
 #pragma unroll
-        for (int cb = 0; cb < C::CB; ++cb)
-            *reinterpret_cast<f4 *>(&so[(wave * NC + h) * DP + 16 * cb + 4 * q4]) = O[cb];
-        if (q4 == 0) {
-            sm[wave * NC + h] = m_run;
-            sl[wave * NC + h] = l_run;
+        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sml[(w * 16 + h) * 2]);
+        const float Mref = M > -INFINITY ? M : 0.0f;  // -inf: no visible row in the split
+        const float e = fast_exp2(m_run - Mref);      // 0 for a wave without visible rows
+        float *own = reinterpret_cast<float *>(smem + C::OFF_SLOTS) + (wave * NC + h) * C::DP + 4 * q4;
+#pragma unroll
+        for (int cb = 0; cb < C::CB; ++cb) {
+            const f4 x = O[cb];
+            *reinterpret_cast<f4 *>(own + 16 * cb) = f4{x[0] * e, x[1] * e, x[2] * e, x[3] * e};
+        }
+        if (wave == 0 && q4 == 0) {
+            float L = 0.0f;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w)
+                L = fmaf(fast_exp2(sml[(w * 16 + h) * 2] - Mref), sml[(w * 16 + h) * 2 + 1], L);
+            sfin[2 * h] = M;
+            sfin[2 * h + 1] = L;
         }
     }
     __syncthreads();
-    for (int idx = tid; idx < NC * D; idx += kThreads) {
-        const int col = idx / D, c = idx % D;
-        float M = -INFINITY;
+    constexpr int D4 = D / 4;
+    for (int idx = tid; idx < NC * D4; idx += kThreads) {
+        const int col = idx / D4, c = (idx % D4) * 4;
+        const float *src = reinterpret_cast<const float *>(smem + C::OFF_SLOTS) + col * C::DP + c;
+        f4 o = *reinterpret_cast<const f4 *>(src);
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm[w * NC + col]);
-        const float Mref = M > -INFINITY ? M : 0.0f;  // -inf: no visible row in the split
-        float o = 0.0f, L = 0.0f;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-            const float e = fast_exp2(sm[w * NC + col] - Mref);  // 0 for waves without rows
-            o = fmaf(e, so[(w * NC + col) * DP + c], o);
-            L = fmaf(e, sl[w * NC + col], L);
+        for (int w = 1; w < kWaves; ++w) {
+            const f4 x = *reinterpret_cast<const f4 *>(src + w * NC * C::DP);
+            o = f4{o[0] + x[0], o[1] + x[1], o[2] + x[2], o[3] + x[3]};
         }
+        const float M = sfin[2 * col], L = sfin[2 * col + 1];
         const int cq = col / G, ch = col % G;
         if (a.max_splits == 1) {  // the call has one split: write the output
-            a.out[b * a.q_seq_stride + ((int64_t)cq * a.n_q_heads + (int64_t)kvh * G + ch) * D + c] =
-                L > 0.0f ? o / L : 0.0f;
+            const float r = L > 0.0f ? 1.0f / L : 0.0f;
+            float *dst = a.out + b * a.q_seq_stride + ((int64_t)cq * a.n_q_heads + (int64_t)kvh * G + ch) * D + c;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dst[i] = o[i] * r;
             continue;
         }
         const int64_t qh = ((int64_t)b * a.q_len + cq) * a.n_q_heads + (int64_t)kvh * G + ch;
         const int64_t ph = qh * a.max_splits + sp;
-        a.part_o[ph * D + c] = o;
+        *reinterpret_cast<f4 *>(a.part_o + ph * D + c) = o;
         if (c == 0) {
             a.part_ml[2 * ph] = M;
             a.part_ml[2 * ph + 1] = L;
@@ -670,9 +703,8 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
 template <int D, int KC, int VC>
 hipError_t launch_typed(const DecodeArgs &a, hipStream_t s) {
     using C = Cfg<D, KC, VC>;
-    const size_t stream_lds = (size_t)C::LDS_STREAM;
-    const size_t merge_lds = (size_t)kWaves * a.gqa * a.q_len * (D + 4 + 2) * sizeof(float);
-    const size_t lds = stream_lds > merge_lds ? stream_lds : merge_lds;
+    const size_t merge_lds = (size_t)C::OFF_SLOTS + (size_t)kWaves * a.gqa * a.q_len * C::DP * sizeof(float);
+    const size_t lds = (size_t)C::LDS_STREAM > merge_lds ? (size_t)C::LDS_STREAM : merge_lds;
     const dim3 grid((unsigned)a.max_splits, (unsigned)a.k.n_kv_heads, (unsigned)a.n_seqs);
     if (lds > 65536) {
         hipError_t e = hipFuncSetAttribute((const void *)decode_kernel<D, KC, VC>,
