@@ -14,6 +14,8 @@ from ._binding import (  # noqa: F401
     Plane,
     Layer,
     kvq_append,
+    kvq_append_attend_decode,
+    kvq_append_attend_decode_mq,
     kvq_attend_decode,
     kvq_attend_decode_mq,
     kvq_attend_prefill,

@@ -63,6 +63,8 @@ def load_library():
         "kvq_attend_decode": (i32, [LY, P, P, i32, i32, i64, f32, P, P, sz, P]),
         "kvq_decode_mq_workspace_bytes": (sz, [LY, i32, i32, i32, i64]),
         "kvq_attend_decode_mq": (i32, [LY, P, P, i32, i32, i32, i64, f32, P, P, sz, P]),
+        "kvq_append_attend_decode": (i32, [LY, P, P, P, P, i32, i32, i64, f32, P, P, sz, P]),
+        "kvq_append_attend_decode_mq": (i32, [LY, P, P, P, P, i32, i32, i32, i64, f32, P, P, sz, P]),
         "kvq_prefill_workspace_bytes": (sz, [LY, i32, i32]),
         "kvq_attend_prefill": (i32, [LY, P, i32, i64, i32, i32, f32, P, P, sz, P]),
         "kvq_dequant": (i32, [PL, i32, i64, i64, P, P]),
@@ -244,6 +246,58 @@ def kvq_attend_decode_mq(layer: Layer, q, seq_len, max_len: int, softmax_scale: 
     _check(load_library().kvq_attend_decode_mq(ctypes.byref(L), _ptr(q), _ptr(seq_len), n_seqs, q_len, hq,
                                                max_len, softmax_scale, _ptr(out), _ptr(workspace),
                                                workspace.numel(), _stream(stream)))
+    return out
+
+
+def kvq_append_attend_decode(layer: Layer, k_new, v_new, q, seq_len, max_len: int, softmax_scale: float,
+                             out=None, workspace=None, stream=None):
+    """k_new, v_new fp32 [n_seqs][n_kv_heads][head_dim] become row seq_len[b] - 1
+    of sequence b; then q fp32 [n_seqs][n_q_heads][head_dim] attends as
+    kvq_attend_decode (one launch does both)."""
+    n_seqs, hq, d = q.shape
+    H = layer.k.n_kv_heads
+    _need(q, "q", torch.float32, (n_seqs, hq, layer.k.head_dim))
+    _need(k_new, "k_new", torch.float32, (n_seqs, H, layer.k.head_dim))
+    _need(v_new, "v_new", torch.float32, (n_seqs, H, layer.k.head_dim))
+    _need(seq_len, "seq_len", torch.int64, (n_seqs,))
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", torch.float32, (n_seqs, hq, layer.k.head_dim))
+    if workspace is None:
+        workspace = decode_workspace(layer, hq, n_seqs, max_len)
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    L = layer.struct()
+    _check(load_library().kvq_append_attend_decode(ctypes.byref(L), _ptr(k_new), _ptr(v_new), _ptr(q),
+                                                   _ptr(seq_len), n_seqs, hq, max_len, softmax_scale,
+                                                   _ptr(out), _ptr(workspace), workspace.numel(),
+                                                   _stream(stream)))
+    return out
+
+
+def kvq_append_attend_decode_mq(layer: Layer, k_new, v_new, q, seq_len, max_len: int, softmax_scale: float,
+                                out=None, workspace=None, stream=None):
+    """k_new, v_new fp32 [n_seqs][q_len][n_kv_heads][head_dim] become rows
+    seq_len[b] - q_len + i; then q fp32 [n_seqs][q_len][n_q_heads][head_dim]
+    attends as kvq_attend_decode_mq (the first launch appends)."""
+    n_seqs, q_len, hq, d = q.shape
+    H = layer.k.n_kv_heads
+    _need(q, "q", torch.float32, (n_seqs, q_len, hq, layer.k.head_dim))
+    _need(k_new, "k_new", torch.float32, (n_seqs, q_len, H, layer.k.head_dim))
+    _need(v_new, "v_new", torch.float32, (n_seqs, q_len, H, layer.k.head_dim))
+    _need(seq_len, "seq_len", torch.int64, (n_seqs,))
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", torch.float32, (n_seqs, q_len, hq, layer.k.head_dim))
+    if workspace is None:
+        workspace = decode_mq_workspace(layer, hq, n_seqs, q_len, max_len)
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    L = layer.struct()
+    _check(load_library().kvq_append_attend_decode_mq(ctypes.byref(L), _ptr(k_new), _ptr(v_new), _ptr(q),
+                                                      _ptr(seq_len), n_seqs, q_len, hq, max_len,
+                                                      softmax_scale, _ptr(out), _ptr(workspace),
+                                                      workspace.numel(), _stream(stream)))
     return out
 
 

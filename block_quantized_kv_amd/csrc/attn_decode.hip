@@ -55,6 +55,7 @@
 
 #include "kvq_device.h"
 #include "kvq_internal.h"
+#include "kvq_quant.h"
 
 namespace kvq {
 
@@ -275,6 +276,41 @@ __device__ __forceinline__ void read_slot(Payload<D, KC, VC> &pl, uint32_t a16, 
     lds_wait<Payload<D, KC, VC>::NW>(pl.w);
 }
 
+// Fused append, run by one wave: quantizes and stores rows [lo, hi) of kv-head
+// (b, kvh) in both planes; row p comes from entry p - first of the new rows
+// (app_k / app_v: [n_seqs][app_rows][n_kv_heads][D] fp32).
+template <int D, int KC, int VC>
+__device__ __forceinline__ void append_rows(const DecodeArgs &a, int b, int kvh, int64_t first, int64_t lo,
+                                            int64_t hi, int lane) {
+    constexpr int CH = D / 8;  // lanes per row (8 channels each)
+    const int items = (int)(hi - lo) * CH;
+    const int64_t head_lin = (int64_t)b * a.k.n_kv_heads + kvh;
+    for (int it = 0; it < items; it += 64) {
+        // a quantization group (G/8 lanes) never straddles rows or passes;
+        // the K and V rows load together
+        const int item = it + lane;
+        const bool live = item < items;
+        const int r = live ? item / CH : 0, chunk = item % CH;
+        const int64_t pos = lo + r;
+        float xk[8], xv[8];
+        if (live) {
+            const int64_t off = (((int64_t)b * a.app_rows + (pos - first)) * a.k.n_kv_heads + kvh) * D + 8 * chunk;
+            const float4 *pk = reinterpret_cast<const float4 *>(a.app_k + off);
+            const float4 *pv = reinterpret_cast<const float4 *>(a.app_v + off);
+            const float4 k0 = pk[0], k1 = pk[1], v0 = pv[0], v1 = pv[1];
+            xk[0] = k0.x; xk[1] = k0.y; xk[2] = k0.z; xk[3] = k0.w;
+            xk[4] = k1.x; xk[5] = k1.y; xk[6] = k1.z; xk[7] = k1.w;
+            xv[0] = v0.x; xv[1] = v0.y; xv[2] = v0.z; xv[3] = v0.w;
+            xv[4] = v1.x; xv[5] = v1.y; xv[6] = v1.z; xv[7] = v1.w;
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) xk[i] = xv[i] = 0.0f;
+        }
+        quantize_store<KC, ROLE_K>(a.k, head_lin, pos, chunk, xk, live);
+        quantize_store<VC, ROLE_V>(a.v, head_lin, pos, chunk, xv, live);
+    }
+}
+
 template <int D, int KC, int VC>
 __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     using C = Cfg<D, KC, VC>;
@@ -349,6 +385,25 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
         qv[0] = use ? x0.x : 0.f; qv[1] = use ? x0.y : 0.f; qv[2] = use ? x0.z : 0.f; qv[3] = use ? x0.w : 0.f;
         qv[4] = use ? x1.x : 0.f; qv[5] = use ? x1.y : 0.f; qv[6] = use ? x1.z : 0.f; qv[7] = use ? x1.w : 0.f;
     }
+    // ---- fused append (app_rows > 0): wave 0 quantizes and stores this
+    // split's share of the new rows [len - app_rows, len) and waits for its
+    // stores before the first barrier.  A DMA that could read those bytes
+    // (blocks from the new rows' first block minus one on: a line of scales
+    // can straddle two blocks) is issued only after that barrier.
+    int dma_late = nblk;  // local blocks >= dma_late wait for the first barrier
+    if (a.app_rows > 0) {
+        const int64_t first = len - a.app_rows;
+        const int64_t lo = first > r0 ? first : r0;
+        const int64_t hi = r0 + nrows;
+        if (lo < hi) {
+            const int nb0 = (int)((lo - r0) / kBlockRows);
+            dma_late = nb0 > 0 ? nb0 - 1 : 0;
+            if (wave == 0) {
+                append_rows<D, KC, VC>(a, b, kvh, first, lo, hi, lane);
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            }
+        }
+    }
     // the first slot starts streaming once the query is in (queued behind
     // the DMAs the query would arrive late); the rest of the ring follows the
     // prologue: a wave blocks while the memory queues are full, and the
@@ -356,7 +411,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     // through hand-issued accesses, so it never waits for these DMAs.
     asm volatile("s_waitcnt vmcnt(0)" : "+v"(qv[0]), "+v"(qv[1]), "+v"(qv[2]), "+v"(qv[3]), "+v"(qv[4]),
                  "+v"(qv[5]), "+v"(qv[6]), "+v"(qv[7])::"memory");
-    dma_block<D, KC, VC>(st, wave, myslots, lane);
+    if (wave < dma_late) dma_block<D, KC, VC>(st, wave, myslots, lane);
 
     const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void *)smem;
     if (preps) {
@@ -368,6 +423,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     }
     if (tid == 0) ds_wr(lds0, (uint32_t)(NS * kWaves), C::OFF_CNT);
     lds_barrier();
+    if (wave >= dma_late) dma_block<D, KC, VC>(st, wave, myslots, lane);
 
     // ---- part 2: power-of-two normalisation per head, hi + lo binary16
     // halves of channel step w, and that step's share of the bias correction

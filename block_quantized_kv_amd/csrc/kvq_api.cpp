@@ -152,13 +152,19 @@ size_t decode_ws_bytes(const kvq_layer *L, int32_t n_q_heads, int32_t n_seqs, in
     return p.total_bytes;
 }
 
-kvq_status attend_decode(const kvq_layer *L, const float *q, const int64_t *seq_len, int32_t n_seqs,
-                         int32_t q_len, int32_t n_q_heads, int64_t max_len, float softmax_scale, float *out,
-                         void *workspace, size_t ws_bytes, void *hip_stream) {
+// app_k / app_v (both null, or both set): fused append of q_len new rows per
+// sequence before the attention (the first launch writes them).
+kvq_status attend_decode(const kvq_layer *L, const float *app_k, const float *app_v, const float *q,
+                         const int64_t *seq_len, int32_t n_seqs, int32_t q_len, int32_t n_q_heads,
+                         int64_t max_len, float softmax_scale, float *out, void *workspace, size_t ws_bytes,
+                         void *hip_stream) {
     kvq_status st = check_layer(L);
     if (st != KVQ_OK) return st;
     if (!q || !seq_len || !out) return fail(KVQ_EINVAL, "null q/seq_len/out");
     if (!aligned(q, 16) || !aligned(out, 16)) return fail(KVQ_EINVAL, "q/out not 16-byte aligned");
+    if ((app_k == nullptr) != (app_v == nullptr)) return fail(KVQ_EINVAL, "k_new and v_new: both or neither");
+    if (app_k && (!aligned(app_k, 16) || !aligned(app_v, 16)))
+        return fail(KVQ_EINVAL, "k_new/v_new not 16-byte aligned");
     if (n_seqs <= 0 || n_seqs > L->k.n_seqs)
         return fail(KVQ_EINVAL, "n_seqs %d outside [1, %d]", n_seqs, L->k.n_seqs);
     if (q_len <= 0 || q_len > KVQ_MAX_QUERIES)
@@ -205,6 +211,11 @@ kvq_status attend_decode(const kvq_layer *L, const float *q, const int64_t *seq_
     // launches of `per` queries each, in order on the stream (they share the
     // workspace)
     for (int first = 0; first < q_len; first += per) {
+        // the first launch appends every new row (later launches' queries
+        // see them too)
+        a.app_k = first == 0 ? app_k : nullptr;
+        a.app_v = first == 0 ? app_v : nullptr;
+        a.app_rows = first == 0 && app_k ? q_len : 0;
         a.q_len = q_len - first < per ? q_len - first : per;
         a.q_tail = q_len - first - a.q_len;
         a.q = q + first * qstride;
@@ -226,8 +237,8 @@ kvq_status kvq_attend_decode(const kvq_layer *L, const float *q, const int64_t *
                              int32_t n_seqs, int32_t n_q_heads, int64_t max_len,
                              float softmax_scale, float *out, void *workspace, size_t ws_bytes,
                              void *hip_stream) {
-    return attend_decode(L, q, seq_len, n_seqs, 1, n_q_heads, max_len, softmax_scale, out, workspace,
-                         ws_bytes, hip_stream);
+    return attend_decode(L, nullptr, nullptr, q, seq_len, n_seqs, 1, n_q_heads, max_len, softmax_scale, out,
+                         workspace, ws_bytes, hip_stream);
 }
 
 size_t kvq_decode_mq_workspace_bytes(const kvq_layer *L, int32_t n_q_heads, int32_t n_seqs,
@@ -239,8 +250,26 @@ kvq_status kvq_attend_decode_mq(const kvq_layer *L, const float *q, const int64_
                                 int32_t n_seqs, int32_t q_len, int32_t n_q_heads, int64_t max_len,
                                 float softmax_scale, float *out, void *workspace, size_t ws_bytes,
                                 void *hip_stream) {
-    return attend_decode(L, q, seq_len, n_seqs, q_len, n_q_heads, max_len, softmax_scale, out, workspace,
-                         ws_bytes, hip_stream);
+    return attend_decode(L, nullptr, nullptr, q, seq_len, n_seqs, q_len, n_q_heads, max_len, softmax_scale, out,
+                         workspace, ws_bytes, hip_stream);
+}
+
+kvq_status kvq_append_attend_decode(const kvq_layer *L, const float *k_new, const float *v_new, const float *q,
+                                    const int64_t *seq_len, int32_t n_seqs, int32_t n_q_heads, int64_t max_len,
+                                    float softmax_scale, float *out, void *workspace, size_t ws_bytes,
+                                    void *hip_stream) {
+    if (!k_new || !v_new) return fail(KVQ_EINVAL, "null k_new/v_new");
+    return attend_decode(L, k_new, v_new, q, seq_len, n_seqs, 1, n_q_heads, max_len, softmax_scale, out,
+                         workspace, ws_bytes, hip_stream);
+}
+
+kvq_status kvq_append_attend_decode_mq(const kvq_layer *L, const float *k_new, const float *v_new,
+                                       const float *q, const int64_t *seq_len, int32_t n_seqs, int32_t q_len,
+                                       int32_t n_q_heads, int64_t max_len, float softmax_scale, float *out,
+                                       void *workspace, size_t ws_bytes, void *hip_stream) {
+    if (!k_new || !v_new) return fail(KVQ_EINVAL, "null k_new/v_new");
+    return attend_decode(L, k_new, v_new, q, seq_len, n_seqs, q_len, n_q_heads, max_len, softmax_scale, out,
+                         workspace, ws_bytes, hip_stream);
 }
 
 size_t kvq_prefill_workspace_bytes(const kvq_layer *L, int32_t n_q_heads, int32_t n_tokens) {

@@ -61,6 +61,12 @@ struct DecodeArgs {
     int split_rows;          // multiple of 256
     int max_splits;
     float scale_log2;        // softmax_scale * log2(e)
+    // fused append (app_rows = 0: none): rows len_b - app_rows .. len_b - 1
+    // (those at positions >= 0) of every kv-head are first quantized into the
+    // cache from app_k / app_v, fp32 [n_seqs][app_rows][n_kv_heads][D]
+    const float *app_k;
+    const float *app_v;
+    int app_rows;
 };
 
 struct PrefillArgs {

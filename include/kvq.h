@@ -183,6 +183,34 @@ kvq_status kvq_attend_decode_mq(const kvq_layer *L, const float *q, const int64_
                                 float softmax_scale, float *out, void *workspace, size_t ws_bytes,
                                 void *hip_stream);
 
+/* ---- fused append + decode (den_llama.cpp, "What's in the fork": the
+ * quantize-on-write path and the FlashAttention reader of the same codec,
+ * which the fork runs as two steps; here one launch does both) ------------ */
+
+/* Appends the step's new token and attends from it, in one launch:
+ * with len_b = min(seq_len[b], max_len), row len_b - 1 of every kv-head g of
+ * sequence b receives k_new[b][g] / v_new[b][g], quantized exactly as
+ * kvq_append stores it, and out is then what kvq_attend_decode returns on
+ * the updated cache.  A sequence with len_b <= 0 gets no row and out[b] = 0.
+ *   k_new, v_new : fp32 [n_seqs][n_kv_heads][head_dim], device, 16-B aligned
+ * Every other argument, the workspace size included, as for
+ * kvq_attend_decode.  The appended rows are the only cache bytes written. */
+kvq_status kvq_append_attend_decode(const kvq_layer *L, const float *k_new, const float *v_new,
+                                    const float *q, const int64_t *seq_len, int32_t n_seqs,
+                                    int32_t n_q_heads, int64_t max_len, float softmax_scale, float *out,
+                                    void *workspace, size_t ws_bytes, void *hip_stream);
+
+/* The same for q_len new tokens per sequence (a verifying multi-query step):
+ * rows len_b - q_len + i (those >= 0) receive k_new[b][i] / v_new[b][i], then
+ * the call returns what kvq_attend_decode_mq returns on the updated cache.
+ *   k_new, v_new : fp32 [n_seqs][q_len][n_kv_heads][head_dim], device
+ * Workspace size: kvq_decode_mq_workspace_bytes. */
+kvq_status kvq_append_attend_decode_mq(const kvq_layer *L, const float *k_new, const float *v_new,
+                                       const float *q, const int64_t *seq_len, int32_t n_seqs,
+                                       int32_t q_len, int32_t n_q_heads, int64_t max_len,
+                                       float softmax_scale, float *out, void *workspace, size_t ws_bytes,
+                                       void *hip_stream);
+
 /* ---- chunked-prefill attention (den_llama.cpp, "Results": prefill with the
  * quantized cache and 2048-token micro-batches; Llaminar, "GPU Graph
  * Capture": prefill runs in chunks) --------------------------------------- */

@@ -114,6 +114,29 @@ def test_multi_query_decode_validation():
     assert ws[0] < ws[1] < ws[2] == ws[3] == ws[4]
 
 
+def test_fused_append_decode_validation():
+    # every call here must fail in argument checking (the pointers are fake)
+    lib = B.load_library()
+    good = B._Layer(_fake_plane(role=0), _fake_plane(codec="q4_0", role=1, codes=0x30000, scales=0x40000))
+
+    def call(k, v, ws_bytes=1 << 30, q=0x1000):
+        return lib.kvq_append_attend_decode(ctypes.byref(good), k, v, q, 0x2000, 1, 4, 64, 0.1, 0x3000,
+                                            0x4000, ws_bytes, None)
+
+    def call_mq(k, v, q_len):
+        return lib.kvq_append_attend_decode_mq(ctypes.byref(good), k, v, 0x1000, 0x2000, 1, q_len, 4, 64, 0.1,
+                                               0x3000, 0x4000, 1 << 30, None)
+    assert call(None, 0x5000) == 1          # k_new missing
+    assert call(0x5000, None) == 1          # v_new missing
+    assert call(0x5004, 0x6000) == 1        # k_new not 16-byte aligned
+    assert call(0x5000, 0x6008) == 1        # v_new not 16-byte aligned
+    assert call(0x5000, 0x6000, q=0) == 1   # no query
+    assert call(0x5000, 0x6000, ws_bytes=16) == 4
+    assert call_mq(None, 0x6000, 2) == 1
+    assert call_mq(0x5000, 0x6000, 0) == 1
+    assert call_mq(0x5000, 0x6000, 65) == 1
+
+
 def test_decode_workspace_grows_with_length():
     good = B._Layer(_fake_plane(cap=1 << 17), _fake_plane(role=1, cap=1 << 17, codes=0x30000, scales=0x40000))
     lib = B.load_library()
