@@ -47,6 +47,9 @@ def _args():
     p.add_argument("--no-quality", action="store_true")
     p.add_argument("--no-baselines", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--step-only", action="store_true",
+                   help="time only the headline step (no two-call step, attention-only, multi-query, "
+                        "baseline, prefill, quality or CPU legs): the run that profiles and counters use")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run plain 256 MiB device copies (HBM counter calibration)")
     p.add_argument("--write-traffic-summary", metavar="PMC_DIR",
@@ -63,7 +66,8 @@ def _args():
 # and is used only while they are unchanged.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode64k_q4g64_traffic.txt")
 DECODE_SOURCES = ["block_quantized_kv_amd/csrc/attn_decode.hip", "block_quantized_kv_amd/csrc/kvq_device.h",
-                  "block_quantized_kv_amd/csrc/kvq_layout.h", "block_quantized_kv_amd/csrc/kvq_internal.h"]
+                  "block_quantized_kv_amd/csrc/kvq_layout.h", "block_quantized_kv_amd/csrc/kvq_internal.h",
+                  "block_quantized_kv_amd/csrc/kvq_quant.h"]
 
 
 def decode_source_hash() -> str:
@@ -102,12 +106,12 @@ def write_traffic_summary(pmc_dir: str):
     fetch_b = (f_dec + f_cmb) * ff * 1024
     write_b = (w_dec + w_cmb) * fw * 1024
     lines = [
-        "# HBM traffic of one kvq_attend_decode launch (decode_kernel + combine_kernel),",
+        "# HBM traffic of one decode step, kvq_append_attend_decode (decode_kernel + combine_kernel),",
         "# 64K-context Q4_G64 decode (1 seq, 24/4 heads, head_dim 256), from rocprofv3 counters",
         "#",
         "# commands (GPU box, repo root; one counter per run):",
         "#   rocprofv3 --pmc FETCH_SIZE --kernel-include-regex 'decode_kernel|combine_kernel' -d <dir>/fetch -o fetch "
-        "--output-format csv -- python -u bench.py --steps 32 --warmup 8 --no-cpu-baseline --no-prefill",
+        "--output-format csv -- python -u bench.py --steps 32 --warmup 8 --step-only",
         "#   rocprofv3 --pmc WRITE_SIZE (same, -d <dir>/write)",
         "#   rocprofv3 --pmc FETCH_SIZE -d <dir>/cfetch -o cfetch --output-format csv -- python -u bench.py --calibrate-copy",
         "#   rocprofv3 --pmc WRITE_SIZE -d <dir>/cwrite ... -- python -u bench.py --calibrate-copy",
@@ -190,6 +194,8 @@ def main():
     import numpy as np
     import torch
 
+    if args.step_only:
+        args.no_cpu_baseline = args.no_baselines = args.no_prefill = args.no_quality = True
     import workloads
     from block_quantized_kv_amd import (Layer, decode_workspace, kvq_append, kvq_append_attend_decode,
                                         kvq_attend_decode, load_library)
@@ -259,12 +265,13 @@ def main():
         with torch.cuda.graph(ring, stream=cap):
             for i in range(ROTATE):
                 step(i, cap)
-        with torch.cuda.graph(unfused_ring, stream=cap):
-            for i in range(ROTATE):
-                step_unfused(i, cap)
-        with torch.cuda.graph(attend_graph, stream=cap):
-            for i in range(ROTATE):
-                kvq_attend_decode(caches[i], q, seq_len, n, cfg.scale, out=out, workspace=ws, stream=cap)
+        if not args.step_only:
+            with torch.cuda.graph(unfused_ring, stream=cap):
+                for i in range(ROTATE):
+                    step_unfused(i, cap)
+            with torch.cuda.graph(attend_graph, stream=cap):
+                for i in range(ROTATE):
+                    kvq_attend_decode(caches[i], q, seq_len, n, cfg.scale, out=out, workspace=ws, stream=cap)
     torch.cuda.synchronize()
     for _ in range(max(1, args.warmup // ROTATE)):
         ring.replay()
@@ -308,21 +315,23 @@ def main():
     torch.cuda.synchronize()
     att_avg_ms = a0.elapsed_time(a1) / (reps * ROTATE)
     achieved = nb["fused_kernel"] / (att_avg_ms * 1e-3) / 1e9
-    # the same step as two calls (kvq_append, kvq_attend_decode)
-    u0, u1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    u0.record()
-    for _ in range(reps):
-        unfused_ring.replay()
-    u1.record()
-    torch.cuda.synchronize()
-    unfused_ms = u0.elapsed_time(u1) / (reps * ROTATE)
-    # attention alone (no append), for the baselines below
-    u0.record()
-    for _ in range(reps):
-        attend_graph.replay()
-    u1.record()
-    torch.cuda.synchronize()
-    attend_only_ms = u0.elapsed_time(u1) / (reps * ROTATE)
+    unfused_ms = attend_only_ms = None
+    if not args.step_only:
+        # the same step as two calls (kvq_append, kvq_attend_decode)
+        u0, u1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        u0.record()
+        for _ in range(reps):
+            unfused_ring.replay()
+        u1.record()
+        torch.cuda.synchronize()
+        unfused_ms = round(u0.elapsed_time(u1) / (reps * ROTATE), 5)
+        # attention alone (no append), for the baselines below
+        u0.record()
+        for _ in range(reps):
+            attend_graph.replay()
+        u1.record()
+        torch.cuda.synchronize()
+        attend_only_ms = round(u0.elapsed_time(u1) / (reps * ROTATE), 5)
     traffic = read_traffic()
 
     result = {
@@ -345,8 +354,8 @@ def main():
                    "bytes_per_step": nb["step"], "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
                    "timing": timing, "eager_ms_per_step": round(eager_ms, 5),
                    "graph_ms_per_step": round(graph_ms, 5),
-                   "unfused_graph_ms_per_step": round(unfused_ms, 5),
-                   "attend_only_graph_ms": round(attend_only_ms, 5),
+                   "unfused_graph_ms_per_step": unfused_ms,
+                   "attend_only_graph_ms": attend_only_ms,
                    "wall_s_timed_region": round(wall, 4)},
         "roofline": {"bound": "hbm",
                      "kernel": "kvq_append_attend_decode = decode_kernel<256,Q4_G64,Q4_G64> (append + attention)"
@@ -356,13 +365,34 @@ def main():
                      "bytes_per_launch": nb["fused_kernel"], "avg_launch_ms": round(att_avg_ms, 5)},
     }
 
+    if not args.step_only:
+        run_multi_query(torch, dev, cfg, caches, k_new2, v_new2, seq_len, nb, args, stream, result)
+    if not args.no_baselines:
+        bl = run_baselines(torch, dev, cfg, caches, q, seq_len, cfg.scale, max(8, min(args.steps, 64)))
+        bl["direct_quantized_attend_ms"] = round(attend_only_ms, 4)
+        bl["speedup_vs_f16_control"] = round(bl["f16_control"]["ms_per_attend"] / attend_only_ms, 2)
+        bl["speedup_vs_dequant_once"] = round(bl["dequant_once"]["ms_per_attend"] / attend_only_ms, 2)
+        # no f16 decode, however good, can move its 4x larger K/V faster than HBM peak
+        bl["f16_hbm_floor_ms"] = round(bl["f16_control"]["kv_bytes"] / (HBM_PEAK_GBS * 1e9) * 1e3, 4)
+        result["baselines"] = bl
+    if not args.no_prefill:
+        result["prefill"] = run_prefill(torch, dev, args)
+    if not args.no_quality:
+        result["quality"] = run_quality(torch, dev, args)
+
+    if host_kv is not None:
+        result["cpu_baseline"] = cpu_baseline(cfg, host_kv, q.cpu().numpy(), nb, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def run_multi_query(torch, dev, cfg, caches, k_new2, v_new2, seq_len, nb, args, stream, result):
     # ---- the same step verifying two drafted tokens (multi-query decode):
     # append rows n-2 and n-1, attend from both; the K/V bytes are read once
     from block_quantized_kv_amd import decode_mq_workspace, kvq_append_attend_decode_mq
+    n, d = cfg.ctx, cfg.head_dim
     q2 = torch.randn(1, 2, cfg.n_q_heads, d, device=dev, generator=torch.Generator(device=dev).manual_seed(2))
     out2 = torch.empty_like(q2)
-    ws2 = decode_mq_workspace(base, cfg.n_q_heads, 1, 2, n)
-
+    ws2 = decode_mq_workspace(caches[0], cfg.n_q_heads, 1, 2, n)
     k_new2, v_new2 = k_new2[None], v_new2[None]  # [n_seqs][q_len][H][d]
 
     def step2(i):
@@ -384,23 +414,6 @@ def main():
                              "value": round(mq_bytes / (mq_ms * 1e-3) / 1e9, 2), "unit": "GB/s",
                              "tokens_per_s": round(2 / (mq_ms * 1e-3), 1),
                              "step": "kvq_append_attend_decode_mq (append 2 tokens + attend from both), eager"}
-
-    if not args.no_baselines:
-        bl = run_baselines(torch, dev, cfg, caches, q, seq_len, cfg.scale, max(8, min(args.steps, 64)))
-        bl["direct_quantized_attend_ms"] = round(attend_only_ms, 4)
-        bl["speedup_vs_f16_control"] = round(bl["f16_control"]["ms_per_attend"] / attend_only_ms, 2)
-        bl["speedup_vs_dequant_once"] = round(bl["dequant_once"]["ms_per_attend"] / attend_only_ms, 2)
-        # no f16 decode, however good, can move its 4x larger K/V faster than HBM peak
-        bl["f16_hbm_floor_ms"] = round(bl["f16_control"]["kv_bytes"] / (HBM_PEAK_GBS * 1e9) * 1e3, 4)
-        result["baselines"] = bl
-    if not args.no_prefill:
-        result["prefill"] = run_prefill(torch, dev, args)
-    if not args.no_quality:
-        result["quality"] = run_quality(torch, dev, args)
-
-    if host_kv is not None:
-        result["cpu_baseline"] = cpu_baseline(cfg, host_kv, q.cpu().numpy(), nb, args.cpu_seconds)
-    print(json.dumps(result), flush=True)
 
 
 def run_prefill(torch, dev, args):
