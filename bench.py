@@ -333,6 +333,16 @@ def main():
         torch.cuda.synchronize()
         attend_only_ms = round(u0.elapsed_time(u1) / (reps * ROTATE), 5)
     traffic = read_traffic()
+    # the graph timing repeated 5 times (medians are steadier than one run)
+    reps5 = []
+    for _ in range(5):
+        a0.record()
+        run_graph_steps(max(ROTATE, (args.steps // 5) // ROTATE * ROTATE))
+        a1.record()
+        torch.cuda.synchronize()
+        reps5.append(a0.elapsed_time(a1) / max(ROTATE, (args.steps // 5) // ROTATE * ROTATE))
+    reps5.sort()
+    speak = stream_peak(torch, dev) if not args.step_only else None
 
     result = {
         "metric": "decode-attention effective KV GB/s @64K ctx",
@@ -354,6 +364,7 @@ def main():
                    "bytes_per_step": nb["step"], "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
                    "timing": timing, "eager_ms_per_step": round(eager_ms, 5),
                    "graph_ms_per_step": round(graph_ms, 5),
+                   "graph_ms_per_step_median_of_5": round(reps5[2], 5),
                    "unfused_graph_ms_per_step": unfused_ms,
                    "attend_only_graph_ms": attend_only_ms,
                    "wall_s_timed_region": round(wall, 4)},
@@ -362,11 +373,15 @@ def main():
                                " + combine_kernel<256>",
                      "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "bytes_per_launch": nb["fused_kernel"], "avg_launch_ms": round(att_avg_ms, 5)},
+                     "bytes_per_launch": nb["fused_kernel"], "avg_launch_ms": round(att_avg_ms, 5),
+                     "stream_read_peak_gbs": speak["gbs"] if speak else None,
+                     "frac_of_stream_read_peak": round(achieved / speak["gbs"], 4) if speak else None},
     }
 
     if not args.step_only:
         run_multi_query(torch, dev, cfg, caches, k_new2, v_new2, seq_len, nb, args, stream, result)
+    if speak is not None:
+        result["stream_read_peak"] = speak
     if not args.no_baselines:
         bl = run_baselines(torch, dev, cfg, caches, q, seq_len, cfg.scale, max(8, min(args.steps, 64)))
         bl["direct_quantized_attend_ms"] = round(attend_only_ms, 4)
@@ -383,6 +398,31 @@ def main():
     if host_kv is not None:
         result["cpu_baseline"] = cpu_baseline(cfg, host_kv, q.cpu().numpy(), nb, args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def stream_peak(torch, dev, reps: int = 48) -> dict:
+    """On-box streaming-read rate: kvq_probe_stream_read over 64 MiB windows
+    rotating through 1 GiB (so the 256 MB last-level cache cannot serve them),
+    for 256, 512 and 1024 workgroups of 8 waves; the best is the practical
+    ceiling the decode roofline is also quoted against."""
+    from block_quantized_kv_amd import kvq_probe_stream_read
+    win, total = 64 << 20, 1 << 30
+    buf = torch.ones(total, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    by = {}
+    for nwg in (256, 512, 1024):
+        for i in range(4):
+            kvq_probe_stream_read(buf[i * win:(i + 1) * win], nwg, sink)
+        e0.record()
+        for i in range(reps):
+            j = i % (total // win)
+            kvq_probe_stream_read(buf[j * win:(j + 1) * win], nwg, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        by[str(nwg)] = round(win * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+    del buf
+    return {"gbs": max(by.values()), "by_workgroups_of_8_waves": by, "bytes_per_launch": win}
 
 
 def run_multi_query(torch, dev, cfg, caches, k_new2, v_new2, seq_len, nb, args, stream, result):

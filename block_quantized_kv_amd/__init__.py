@@ -25,6 +25,7 @@ from ._binding import (  # noqa: F401
     decode_mq_workspace,
     kvq_decode_mq_workspace_bytes,
     kvq_prefill_workspace_bytes,
+    kvq_probe_stream_read,
     kvq_plane_bytes,
     kvq_row_code_bytes,
     kvq_status_str,

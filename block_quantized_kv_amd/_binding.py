@@ -68,6 +68,7 @@ def load_library():
         "kvq_prefill_workspace_bytes": (sz, [LY, i32, i32]),
         "kvq_attend_prefill": (i32, [LY, P, i32, i64, i32, i32, f32, P, P, sz, P]),
         "kvq_dequant": (i32, [PL, i32, i64, i64, P, P]),
+        "kvq_probe_stream_read": (i32, [P, sz, i32, P, P]),
         "kvq_status_str": (ctypes.c_char_p, [i32]),
         "kvq_last_error": (ctypes.c_char_p, []),
     }
@@ -335,3 +336,13 @@ def kvq_dequant(plane: Plane, seq: int, row0: int, n_rows: int, out=None, stream
     P = plane.struct()
     _check(load_library().kvq_dequant(ctypes.byref(P), seq, row0, n_rows, _ptr(out), _stream(stream)))
     return out
+
+
+def kvq_probe_stream_read(buf, n_workgroups: int, sink, stream=None) -> None:
+    """Streaming read of the whole contiguous device tensor `buf` (measurement
+    helper, not part of the attention path); sink: int32 [1] device."""
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous device tensor")
+    _need(sink, "sink", torch.int32, (1,))
+    _check(load_library().kvq_probe_stream_read(_ptr(buf), buf.numel() * buf.element_size(), n_workgroups,
+                                                _ptr(sink), _stream(stream)))

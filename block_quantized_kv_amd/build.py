@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkvq.so")
-SOURCES = ["kvq_api.cpp", "kv_append.hip", "attn_decode.hip", "attn_prefill.hip"]
+SOURCES = ["kvq_api.cpp", "kv_append.hip", "attn_decode.hip", "attn_prefill.hip", "stream_probe.hip"]
 ARCH = "gfx950"
 PER_SOURCE_FLAGS: dict = {}
 

@@ -3,6 +3,7 @@ exports every symbol include/kvq.h declares, host-only sizing, argument
 validation (which returns before anything touches a GPU), and the in-block
 permutation used by the planes."""
 import ctypes
+import glob
 import os
 import re
 
@@ -13,19 +14,22 @@ from block_quantized_kv_amd import _binding as B
 from block_quantized_kv_amd import layout
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "kvq.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 
 def _declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(kvq_[a-z_]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(kvq_[a-z_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_symbol():
     lib = B.load_library()
     names = _declared_functions()
-    assert {"kvq_append", "kvq_attend_decode", "kvq_attend_prefill", "kvq_dequant"} <= set(names)
+    assert {"kvq_append", "kvq_attend_decode", "kvq_attend_prefill", "kvq_dequant",
+            "kvq_append_attend_decode", "kvq_probe_stream_read"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -135,6 +139,15 @@ def test_fused_append_decode_validation():
     assert call_mq(None, 0x6000, 2) == 1
     assert call_mq(0x5000, 0x6000, 0) == 1
     assert call_mq(0x5000, 0x6000, 65) == 1
+
+
+def test_stream_probe_validation():
+    # sizes that do not split into whole 8 KiB stripes per wave are refused
+    lib = B.load_library()
+    assert lib.kvq_probe_stream_read(None, 1 << 20, 8, 0x1000, None) == 1
+    assert lib.kvq_probe_stream_read(0x10000, (1 << 20) + 4096, 8, 0x1000, None) == 1
+    assert lib.kvq_probe_stream_read(0x10000, 1 << 20, 0, 0x1000, None) == 1
+    assert lib.kvq_probe_stream_read(0x10000, 1 << 31, 8, 0x1000, None) == 1
 
 
 def test_decode_workspace_grows_with_length():
