@@ -380,6 +380,7 @@ def main():
 
     if not args.step_only:
         run_multi_query(torch, dev, cfg, caches, k_new2, v_new2, seq_len, nb, args, stream, result)
+        result["paged"] = run_paged(torch, dev, cfg, base, k_new, v_new, q, seq_len, nb, args)
     if speak is not None:
         result["stream_read_peak"] = speak
     if not args.no_baselines:
@@ -423,6 +424,53 @@ def stream_peak(torch, dev, reps: int = 48) -> dict:
         by[str(nwg)] = round(win * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
     del buf
     return {"gbs": max(by.values()), "by_workgroups_of_8_waves": by, "bytes_per_launch": win}
+
+
+def run_paged(torch, dev, cfg, base, k_new, v_new, q, seq_len, nb, args) -> dict:
+    """The same step over paged planes: each rotated cache is a pool of
+    256-row pages in shuffled order, reached through a block table."""
+    import numpy as np
+    from block_quantized_kv_amd import Layer, PagedLayer, kvq_paged_append_attend_decode_mq, paged_decode_workspace
+    n, d, H = cfg.ctx, cfg.head_dim, cfg.n_kv_heads
+    R, npg = 256, cfg.ctx // 256
+    pools = []
+    for r in range(ROTATE):
+        perm = np.random.default_rng(100 + r).permutation(npg).astype(np.int32)
+        pool = Layer.create(base.k.codec, base.v.codec, d, H, npg, R, device=dev, zero=False)
+        # page perm[i] holds rows [i*R, (i+1)*R) of the contiguous cache
+        for src, dst in ((base.k, pool.k), (base.v, pool.v)):
+            for t_src, t_dst in ((src.codes, dst.codes), (src.scales, dst.scales)):
+                per = t_src.numel() // (H * npg)
+                view_src = t_src.view(H, npg, per)
+                view_dst = t_dst.view(npg, H, per)
+                view_dst[torch.from_numpy(perm).to(dev).long()] = view_src.transpose(0, 1)
+        pools.append(PagedLayer(pool, torch.from_numpy(perm[None]).to(dev)))
+    kn, vn, q1 = k_new[None].contiguous(), v_new[None].contiguous(), q[:, None].contiguous()
+    out = torch.empty_like(q1)
+    ws = paged_decode_workspace(pools[0], cfg.n_q_heads, 1, 1, n)
+    cap = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cap):
+        for i in range(ROTATE):  # warm the kernels before capture
+            kvq_paged_append_attend_decode_mq(pools[i], kn, vn, q1, seq_len, n, cfg.scale, out=out, workspace=ws,
+                                              stream=cap)
+        with torch.cuda.graph(g, stream=cap):
+            for i in range(ROTATE):
+                kvq_paged_append_attend_decode_mq(pools[i], kn, vn, q1, seq_len, n, cfg.scale, out=out,
+                                                  workspace=ws, stream=cap)
+    torch.cuda.synchronize()
+    reps = max(4, args.steps // ROTATE)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / (reps * ROTATE)
+    del pools
+    return {"ms_per_step": round(ms, 5), "value": round(nb["step"] / (ms * 1e-3) / 1e9, 2), "unit": "GB/s",
+            "page_rows": R, "pages": npg, "order": "shuffled",
+            "step": "kvq_paged_append_attend_decode_mq (q_len 1), HIP-graph replay"}
 
 
 def run_multi_query(torch, dev, cfg, caches, k_new2, v_new2, seq_len, nb, args, stream, result):

@@ -13,6 +13,7 @@ from ._binding import (  # noqa: F401
     KvqError,
     Plane,
     Layer,
+    PagedLayer,
     kvq_append,
     kvq_append_attend_decode,
     kvq_append_attend_decode_mq,
@@ -26,6 +27,11 @@ from ._binding import (  # noqa: F401
     kvq_decode_mq_workspace_bytes,
     kvq_prefill_workspace_bytes,
     kvq_probe_stream_read,
+    kvq_paged_append,
+    kvq_paged_attend_decode_mq,
+    kvq_paged_append_attend_decode_mq,
+    kvq_paged_decode_workspace_bytes,
+    paged_decode_workspace,
     kvq_plane_bytes,
     kvq_row_code_bytes,
     kvq_status_str,

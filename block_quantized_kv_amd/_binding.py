@@ -36,6 +36,11 @@ class _Layer(ctypes.Structure):
     _fields_ = [("k", _Plane), ("v", _Plane)]
 
 
+class _PagedLayer(ctypes.Structure):
+    _fields_ = [("pool", _Layer), ("block_table", ctypes.c_void_p), ("n_seqs", ctypes.c_int32),
+                ("max_pages", ctypes.c_int32)]
+
+
 _lib = None
 
 
@@ -54,7 +59,7 @@ def load_library():
                           "(there is no CPU or PyTorch fallback)")
     lib = ctypes.CDLL(path)
     P, i32, i64, sz, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
-    PL, LY = ctypes.POINTER(_Plane), ctypes.POINTER(_Layer)
+    PL, LY, PG = ctypes.POINTER(_Plane), ctypes.POINTER(_Layer), ctypes.POINTER(_PagedLayer)
     sig = {
         "kvq_row_code_bytes": (sz, [i32, i32]),
         "kvq_plane_bytes": (i32, [i32, i32, i32, i32, i64, ctypes.POINTER(sz), ctypes.POINTER(sz)]),
@@ -69,6 +74,10 @@ def load_library():
         "kvq_attend_prefill": (i32, [LY, P, i32, i64, i32, i32, f32, P, P, sz, P]),
         "kvq_dequant": (i32, [PL, i32, i64, i64, P, P]),
         "kvq_probe_stream_read": (i32, [P, sz, i32, P, P]),
+        "kvq_paged_append": (i32, [PG, P, P, P, P, i32, P, P]),
+        "kvq_paged_decode_workspace_bytes": (sz, [PG, i32, i32, i32, i64]),
+        "kvq_paged_attend_decode_mq": (i32, [PG, P, P, i32, i32, i32, i64, f32, P, P, sz, P]),
+        "kvq_paged_append_attend_decode_mq": (i32, [PG, P, P, P, P, i32, i32, i32, i64, f32, P, P, sz, P]),
         "kvq_status_str": (ctypes.c_char_p, [i32]),
         "kvq_last_error": (ctypes.c_char_p, []),
     }
@@ -346,3 +355,88 @@ def kvq_probe_stream_read(buf, n_workgroups: int, sink, stream=None) -> None:
     _need(sink, "sink", torch.int32, (1,))
     _check(load_library().kvq_probe_stream_read(_ptr(buf), buf.numel() * buf.element_size(), n_workgroups,
                                                 _ptr(sink), _stream(stream)))
+
+
+class PagedLayer:
+    """A page pool (a Layer whose "sequences" are pages and whose capacity is
+    the rows per page) plus a block table int32 [n_seqs][max_pages] (device):
+    entry [b][i] is the page holding rows [i * page_rows, (i + 1) * page_rows)
+    of sequence b."""
+
+    def __init__(self, pool: Layer, block_table):
+        if block_table.dtype != torch.int32 or block_table.dim() != 2 or not block_table.is_cuda \
+                or not block_table.is_contiguous():
+            raise ValueError("block_table: expected a contiguous device int32 [n_seqs][max_pages] tensor")
+        self.pool, self.block_table = pool, block_table
+        self.n_seqs, self.max_pages = block_table.shape
+        self.page_rows = pool.k.capacity
+
+    def struct(self) -> _PagedLayer:
+        return _PagedLayer(self.pool.struct(), self.block_table.data_ptr(), self.n_seqs, self.max_pages)
+
+
+def kvq_paged_append(pl: PagedLayer, k_new, v_new, seq_idx, pos, dev_status=None, stream=None) -> None:
+    """kvq_append through the block table (pos is the row within the sequence)."""
+    n = int(seq_idx.numel())
+    _need(seq_idx, "seq_idx", torch.int32, (n,))
+    _need(pos, "pos", torch.int64, (n,))
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        if t is not None:
+            _need(t, name, torch.float32, (n, pl.pool.k.n_kv_heads, pl.pool.k.head_dim))
+    if dev_status is not None:
+        _need(dev_status, "dev_status", torch.int32, (1,))
+    P = pl.struct()
+    _check(load_library().kvq_paged_append(ctypes.byref(P), _ptr(k_new), _ptr(v_new), _ptr(seq_idx), _ptr(pos), n,
+                                           _ptr(dev_status), _stream(stream)))
+
+
+def kvq_paged_decode_workspace_bytes(pl: PagedLayer, n_q_heads: int, n_seqs: int, q_len: int, max_len: int) -> int:
+    P = pl.struct()
+    return int(load_library().kvq_paged_decode_workspace_bytes(ctypes.byref(P), n_q_heads, n_seqs, q_len, max_len))
+
+
+def paged_decode_workspace(pl: PagedLayer, n_q_heads: int, n_seqs: int, q_len: int, max_len: int):
+    nbytes = max(kvq_paged_decode_workspace_bytes(pl, n_q_heads, n_seqs, q_len, max_len), 256)
+    return torch.zeros(nbytes, dtype=torch.uint8, device=pl.pool.k.codes.device)
+
+
+def _paged_decode(pl: PagedLayer, k_new, v_new, q, seq_len, max_len, softmax_scale, out, workspace, stream):
+    n_seqs, q_len, hq, d = q.shape
+    H, D = pl.pool.k.n_kv_heads, pl.pool.k.head_dim
+    _need(q, "q", torch.float32, (n_seqs, q_len, hq, D))
+    _need(seq_len, "seq_len", torch.int64, (n_seqs,))
+    if k_new is not None:
+        _need(k_new, "k_new", torch.float32, (n_seqs, q_len, H, D))
+        _need(v_new, "v_new", torch.float32, (n_seqs, q_len, H, D))
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", torch.float32, (n_seqs, q_len, hq, D))
+    if workspace is None:
+        workspace = paged_decode_workspace(pl, hq, n_seqs, q_len, max_len)
+    if not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    P = pl.struct()
+    lib = load_library()
+    if k_new is None:
+        st = lib.kvq_paged_attend_decode_mq(ctypes.byref(P), _ptr(q), _ptr(seq_len), n_seqs, q_len, hq, max_len,
+                                            softmax_scale, _ptr(out), _ptr(workspace), workspace.numel(),
+                                            _stream(stream))
+    else:
+        st = lib.kvq_paged_append_attend_decode_mq(ctypes.byref(P), _ptr(k_new), _ptr(v_new), _ptr(q),
+                                                   _ptr(seq_len), n_seqs, q_len, hq, max_len, softmax_scale,
+                                                   _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(st)
+    return out
+
+
+def kvq_paged_attend_decode_mq(pl: PagedLayer, q, seq_len, max_len: int, softmax_scale: float, out=None,
+                               workspace=None, stream=None):
+    """q fp32 [n_seqs][q_len][n_q_heads][head_dim]: kvq_attend_decode_mq over paged planes."""
+    return _paged_decode(pl, None, None, q, seq_len, max_len, softmax_scale, out, workspace, stream)
+
+
+def kvq_paged_append_attend_decode_mq(pl: PagedLayer, k_new, v_new, q, seq_len, max_len: int,
+                                      softmax_scale: float, out=None, workspace=None, stream=None):
+    """kvq_append_attend_decode_mq over paged planes (k_new, v_new fp32
+    [n_seqs][q_len][n_kv_heads][head_dim])."""
+    return _paged_decode(pl, k_new, v_new, q, seq_len, max_len, softmax_scale, out, workspace, stream)

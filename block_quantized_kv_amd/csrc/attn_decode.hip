@@ -251,6 +251,25 @@ __device__ __forceinline__ void vm_wait() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"i"(N) : "memory");
 }
 
+// Buffer descriptors of one block of a paged plane pair: block `within` of
+// page `page` (records 0, so every access is cut off, for page < 0).
+template <int D, int KC, int VC>
+__device__ __forceinline__ Streams page_block_streams(const DecodeArgs &a, int page, int kvh, int within) {
+    using C = Cfg<D, KC, VC>;
+    const bool ok = page >= 0 && page < a.k.n_seqs;
+    const int64_t hl = ok ? (int64_t)page * a.k.n_kv_heads + kvh : 0;
+    Streams st;
+    st.kc = make_rsrc(a.k.codes + hl * a.k.head_code_stride + (int64_t)within * C::K_BLOCK_BYTES,
+                      ok ? C::K_BLOCK_BYTES : 0);
+    st.vc = make_rsrc(a.v.codes + hl * a.v.head_code_stride + (int64_t)within * C::V_BLOCK_BYTES,
+                      ok ? C::V_BLOCK_BYTES : 0);
+    st.ks = make_rsrc(a.k.scales + hl * a.k.head_scale_stride + (int64_t)within * C::K_BLOCK_SCALES,
+                      ok ? C::K_BLOCK_SCALES * 2 : 0);
+    st.vs = make_rsrc(a.v.scales + hl * a.v.head_scale_stride + (int64_t)within * C::V_BLOCK_SCALES,
+                      ok ? C::V_BLOCK_SCALES * 2 : 0);
+    return st;
+}
+
 // One block's words for one lane, copied out of its LDS slot.
 template <int D, int KC, int VC>
 struct Payload {
@@ -284,7 +303,6 @@ __device__ __forceinline__ void append_rows(const DecodeArgs &a, int b, int kvh,
                                             int64_t hi, int lane) {
     constexpr int CH = D / 8;  // lanes per row (8 channels each)
     const int items = (int)(hi - lo) * CH;
-    const int64_t head_lin = (int64_t)b * a.k.n_kv_heads + kvh;
     for (int it = 0; it < items; it += 64) {
         // a quantization group (G/8 lanes) never straddles rows or passes;
         // the K and V rows load together
@@ -293,7 +311,10 @@ __device__ __forceinline__ void append_rows(const DecodeArgs &a, int b, int kvh,
         const int r = live ? item / CH : 0, chunk = item % CH;
         const int64_t pos = lo + r;
         float xk[8], xv[8];
+        int64_t head_lin = 0, row = 0;
+        bool ok = live;
         if (live) {
+            ok = phys_row(a.k, a.pt, b, kvh, pos, head_lin, row);  // K and V pages share the table
             const int64_t off = (((int64_t)b * a.app_rows + (pos - first)) * a.k.n_kv_heads + kvh) * D + 8 * chunk;
             const float4 *pk = reinterpret_cast<const float4 *>(a.app_k + off);
             const float4 *pv = reinterpret_cast<const float4 *>(a.app_v + off);
@@ -306,12 +327,13 @@ __device__ __forceinline__ void append_rows(const DecodeArgs &a, int b, int kvh,
 #pragma unroll
             for (int i = 0; i < 8; ++i) xk[i] = xv[i] = 0.0f;
         }
-        quantize_store<KC, ROLE_K>(a.k, head_lin, pos, chunk, xk, live);
-        quantize_store<VC, ROLE_V>(a.v, head_lin, pos, chunk, xv, live);
+        quantize_store<KC, ROLE_K>(a.k, head_lin, row, chunk, xk, ok);
+        quantize_store<VC, ROLE_V>(a.v, head_lin, row, chunk, xv, ok);
     }
 }
 
-template <int D, int KC, int VC>
+// PAGED: the planes are a page pool addressed through a.pt (else contiguous).
+template <int D, int KC, int VC, bool PAGED>
 __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     using C = Cfg<D, KC, VC>;
     constexpr int NS = C::NS;
@@ -370,6 +392,33 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     st.vs = make_rsrc(a.v.scales + head_lin * a.v.head_scale_stride + blk0 * C::V_BLOCK_SCALES,
                       (uint32_t)nblk * C::V_BLOCK_SCALES * 2);
     unsigned char *myslots = smem + C::OFF_SLOTS + wave * NS * C::SLOT;
+    // paged planes: the split's page numbers, entry j in lane j % 64 of
+    // pages[j / 64] (a split spans at most 128 blocks, so at most 128 pages)
+    constexpr bool paged = PAGED;
+    const int pblk = paged ? a.pt.page_rows / kBlockRows : 1;
+    const int64_t pg0 = blk0 / pblk;
+    int pages[2] = {-1, -1};
+    if constexpr (paged) {
+        const int64_t npg = (blk0 + nblk - 1) / pblk - pg0 + 1;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            if (lane + 64 * j < npg) pages[j] = a.pt.table[(int64_t)b * a.pt.table_stride + pg0 + lane + 64 * j];
+    }
+    // issues the DMAs of local block idx into `slot` (past the split: cut off)
+    auto issue = [&](int idx, unsigned char *slot) {
+        if constexpr (!paged) {
+            dma_block<D, KC, VC>(st, idx, slot, lane);
+        } else {
+            int page = -1, within = 0;
+            if (idx < nblk) {
+                const int64_t gb = blk0 + idx;
+                const int j = (int)(gb / pblk - pg0);
+                page = __builtin_amdgcn_readlane(j < 64 ? pages[0] : pages[1], j & 63);
+                within = (int)(gb % pblk);
+            }
+            dma_block<D, KC, VC>(page_block_streams<D, KC, VC>(a, page, kvh, within), 0, slot, lane);
+        }
+    };
 
     // ---- query prologue, part 1: wave w loads the slice of channel step w
     // (8 channels per lane)
@@ -397,7 +446,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
         const int64_t hi = r0 + nrows;
         if (lo < hi) {
             const int nb0 = (int)((lo - r0) / kBlockRows);
-            dma_late = nb0 > 0 ? nb0 - 1 : 0;
+            // paged: any block of the split may sit next to the new rows' one
+            dma_late = paged ? 0 : (nb0 > 0 ? nb0 - 1 : 0);
             if (wave == 0) {
                 append_rows<D, KC, VC>(a, b, kvh, first, lo, hi, lane);
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -411,7 +461,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     // through hand-issued accesses, so it never waits for these DMAs.
     asm volatile("s_waitcnt vmcnt(0)" : "+v"(qv[0]), "+v"(qv[1]), "+v"(qv[2]), "+v"(qv[3]), "+v"(qv[4]),
                  "+v"(qv[5]), "+v"(qv[6]), "+v"(qv[7])::"memory");
-    if (wave < dma_late) dma_block<D, KC, VC>(st, wave, myslots, lane);
+    if (wave < dma_late) issue(wave, myslots);
 
     const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void *)smem;
     if (preps) {
@@ -423,7 +473,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     }
     if (tid == 0) ds_wr(lds0, (uint32_t)(NS * kWaves), C::OFF_CNT);
     lds_barrier();
-    if (wave >= dma_late) dma_block<D, KC, VC>(st, wave, myslots, lane);
+    if (wave >= dma_late) issue(wave, myslots);
 
     // ---- part 2: power-of-two normalisation per head, hi + lo binary16
     // halves of channel step w, and that step's share of the bias correction
@@ -477,7 +527,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     }
 
 #pragma unroll
-    for (int s = 1; s < NS; ++s) dma_block<D, KC, VC>(st, wave + s * kWaves, myslots + s * C::SLOT, lane);
+    for (int s = 1; s < NS; ++s) issue(wave + s * kWaves, myslots + s * C::SLOT);
 
     // LDS byte addresses for the hand-issued reads
     const uint32_t lds_slots = (uint32_t)(uintptr_t)(lds_void *)myslots;
@@ -622,7 +672,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
                  read_slot<D, KC, VC>(pl, a16, a8, a4, aks, avs, S * C::SLOT);
                  const int nxt = grab();
                  sidx[S] = nxt;
-                 dma_block<D, KC, VC>(st, nxt, myslots + S * C::SLOT, lane);
+                 issue(nxt, myslots + S * C::SLOT);
                  process(pl, idx);
              }()),
              ...);
@@ -762,12 +812,16 @@ hipError_t launch_typed(const DecodeArgs &a, hipStream_t s) {
     const size_t merge_lds = (size_t)C::OFF_SLOTS + (size_t)kWaves * a.gqa * a.q_len * C::DP * sizeof(float);
     const size_t lds = (size_t)C::LDS_STREAM > merge_lds ? (size_t)C::LDS_STREAM : merge_lds;
     const dim3 grid((unsigned)a.max_splits, (unsigned)a.k.n_kv_heads, (unsigned)a.n_seqs);
+    const void *fn = a.pt.table ? (const void *)decode_kernel<D, KC, VC, true>
+                                : (const void *)decode_kernel<D, KC, VC, false>;
     if (lds > 65536) {
-        hipError_t e = hipFuncSetAttribute((const void *)decode_kernel<D, KC, VC>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
-    decode_kernel<D, KC, VC><<<grid, dim3(kThreads), lds, s>>>(a);
+    if (a.pt.table)
+        decode_kernel<D, KC, VC, true><<<grid, dim3(kThreads), lds, s>>>(a);
+    else
+        decode_kernel<D, KC, VC, false><<<grid, dim3(kThreads), lds, s>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.max_splits <= 1) return e;
     combine_kernel<D><<<dim3(D / 64, (unsigned)a.n_q_heads, (unsigned)(a.n_seqs * a.q_len)), dim3(256), 0, s>>>(a);

@@ -17,7 +17,7 @@ namespace {
 
 // Quantizes and stores this thread's 8 channels of one row of one plane.
 template <int CODEC, int ROLE>
-__device__ __forceinline__ void append_plane(const PlaneView &pl, const float *xsrc,
+__device__ __forceinline__ void append_plane(const PlaneView &pl, const PageTable &pt, const float *xsrc,
                                              const int32_t *seq_idx, const int64_t *pos_arr,
                                              int n_tokens, int32_t *dev_status, int64_t tid) {
     const int d = pl.head_dim;
@@ -43,9 +43,13 @@ __device__ __forceinline__ void append_plane(const PlaneView &pl, const float *x
     } else {
         for (int s = 0; s < 8; ++s) x[s] = 0.0f;
     }
-    const bool in_range = sq >= 0 && sq < pl.n_seqs && pos >= 0 && pos < pl.capacity;
+    const int n_seqs = pt.table ? pt.n_seqs : pl.n_seqs;
+    const int64_t cap = pt.table ? (int64_t)pt.table_stride * pt.page_rows : pl.capacity;
+    bool in_range = sq >= 0 && sq < n_seqs && pos >= 0 && pos < cap;
+    int64_t head_lin = 0, prow = 0;
+    if (live && in_range) in_range = phys_row(pl, pt, sq, head, pos, head_lin, prow);
     if (live && !in_range && dev_status) *dev_status = 3;  // KVQ_ERANGE
-    quantize_store<CODEC, ROLE>(pl, (int64_t)sq * pl.n_kv_heads + head, pos, chunk, x, live && in_range);
+    quantize_store<CODEC, ROLE>(pl, head_lin, prow, chunk, x, live && in_range);
 }
 
 // grid.y = 0: K plane, 1: V plane (one launch appends both).
@@ -53,10 +57,10 @@ template <int KC, int VC>
 __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
     const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (blockIdx.y == 0) {
-        if (a.x[0]) append_plane<KC, ROLE_K>(a.plane[0], a.x[0], a.seq_idx, a.pos, a.n_tokens,
+        if (a.x[0]) append_plane<KC, ROLE_K>(a.plane[0], a.pt, a.x[0], a.seq_idx, a.pos, a.n_tokens,
                                              a.dev_status, tid);
     } else {
-        if (a.x[1]) append_plane<VC, ROLE_V>(a.plane[1], a.x[1], a.seq_idx, a.pos, a.n_tokens,
+        if (a.x[1]) append_plane<VC, ROLE_V>(a.plane[1], a.pt, a.x[1], a.seq_idx, a.pos, a.n_tokens,
                                              a.dev_status, tid);
     }
 }

@@ -108,11 +108,36 @@ kvq_status kvq_plane_bytes(int32_t codec, int32_t head_dim, int32_t n_kv_heads, 
     return ok();
 }
 
-kvq_status kvq_append(const kvq_layer *L, const float *k_new, const float *v_new,
-                      const int32_t *seq_idx, const int64_t *pos, int32_t n_tokens,
-                      int32_t *dev_status, void *hip_stream) {
-    kvq_status st = check_layer(L);
+namespace {
+
+// The page table of a paged layer (table null: contiguous planes).
+kvq::PageTable no_pages() {
+    kvq::PageTable t;
+    t.table = nullptr;
+    t.table_stride = 0;
+    t.page_rows = 0;
+    t.n_seqs = 0;
+    return t;
+}
+
+kvq_status check_paged(const kvq_paged_layer *P, kvq::PageTable *pt) {
+    if (!P) return fail(KVQ_EINVAL, "null paged layer");
+    kvq_status st = check_layer(&P->pool);
     if (st != KVQ_OK) return st;
+    if (!P->block_table || !aligned(P->block_table, 4)) return fail(KVQ_EINVAL, "null or misaligned block_table");
+    if (P->n_seqs <= 0 || P->max_pages <= 0)
+        return fail(KVQ_EINVAL, "paged layer: n_seqs=%d max_pages=%d", P->n_seqs, P->max_pages);
+    if (P->pool.k.capacity > INT32_MAX) return fail(KVQ_EUNSUPPORTED, "page of 2^31 rows or more");
+    pt->table = P->block_table;
+    pt->table_stride = P->max_pages;
+    pt->page_rows = (int)P->pool.k.capacity;
+    pt->n_seqs = P->n_seqs;
+    return KVQ_OK;
+}
+
+kvq_status append_impl(const kvq_layer *L, const kvq::PageTable &pt, const float *k_new, const float *v_new,
+                       const int32_t *seq_idx, const int64_t *pos, int32_t n_tokens, int32_t *dev_status,
+                       void *hip_stream) {
     if (n_tokens < 0) return fail(KVQ_EINVAL, "n_tokens %d < 0", n_tokens);
     if (!k_new && !v_new) return fail(KVQ_EINVAL, "both k_new and v_new are null");
     if (n_tokens > 0 && (!seq_idx || !pos)) return fail(KVQ_EINVAL, "null seq_idx/pos");
@@ -122,6 +147,7 @@ kvq_status kvq_append(const kvq_layer *L, const float *k_new, const float *v_new
     kvq::AppendArgs a;
     a.plane[0] = view(L->k);
     a.plane[1] = view(L->v);
+    a.pt = pt;
     a.x[0] = k_new;
     a.x[1] = v_new;
     a.seq_idx = seq_idx;
@@ -129,6 +155,25 @@ kvq_status kvq_append(const kvq_layer *L, const float *k_new, const float *v_new
     a.n_tokens = n_tokens;
     a.dev_status = dev_status;
     return hip_status(kvq::launch_append(a, static_cast<hipStream_t>(hip_stream)), "append launch");
+}
+
+}  // namespace
+
+kvq_status kvq_append(const kvq_layer *L, const float *k_new, const float *v_new,
+                      const int32_t *seq_idx, const int64_t *pos, int32_t n_tokens,
+                      int32_t *dev_status, void *hip_stream) {
+    kvq_status st = check_layer(L);
+    if (st != KVQ_OK) return st;
+    return append_impl(L, no_pages(), k_new, v_new, seq_idx, pos, n_tokens, dev_status, hip_stream);
+}
+
+kvq_status kvq_paged_append(const kvq_paged_layer *P, const float *k_new, const float *v_new,
+                            const int32_t *seq_idx, const int64_t *pos, int32_t n_tokens, int32_t *dev_status,
+                            void *hip_stream) {
+    kvq::PageTable pt;
+    kvq_status st = check_paged(P, &pt);
+    if (st != KVQ_OK) return st;
+    return append_impl(&P->pool, pt, k_new, v_new, seq_idx, pos, n_tokens, dev_status, hip_stream);
 }
 
 namespace {
@@ -154,19 +199,22 @@ size_t decode_ws_bytes(const kvq_layer *L, int32_t n_q_heads, int32_t n_seqs, in
 
 // app_k / app_v (both null, or both set): fused append of q_len new rows per
 // sequence before the attention (the first launch writes them).
-kvq_status attend_decode(const kvq_layer *L, const float *app_k, const float *app_v, const float *q,
-                         const int64_t *seq_len, int32_t n_seqs, int32_t q_len, int32_t n_q_heads,
+// pt: the page table of a paged layer (table null: contiguous planes; the
+// caller has checked L).
+kvq_status attend_decode(const kvq_layer *L, const kvq::PageTable &pt, const float *app_k, const float *app_v,
+                         const float *q, const int64_t *seq_len, int32_t n_seqs, int32_t q_len, int32_t n_q_heads,
                          int64_t max_len, float softmax_scale, float *out, void *workspace, size_t ws_bytes,
                          void *hip_stream) {
-    kvq_status st = check_layer(L);
-    if (st != KVQ_OK) return st;
+    kvq_status st = KVQ_OK;
+    const int32_t seq_limit = pt.table ? pt.n_seqs : L->k.n_seqs;
+    const int64_t cap = pt.table ? (int64_t)pt.table_stride * pt.page_rows : L->k.capacity;
     if (!q || !seq_len || !out) return fail(KVQ_EINVAL, "null q/seq_len/out");
     if (!aligned(q, 16) || !aligned(out, 16)) return fail(KVQ_EINVAL, "q/out not 16-byte aligned");
     if ((app_k == nullptr) != (app_v == nullptr)) return fail(KVQ_EINVAL, "k_new and v_new: both or neither");
     if (app_k && (!aligned(app_k, 16) || !aligned(app_v, 16)))
         return fail(KVQ_EINVAL, "k_new/v_new not 16-byte aligned");
-    if (n_seqs <= 0 || n_seqs > L->k.n_seqs)
-        return fail(KVQ_EINVAL, "n_seqs %d outside [1, %d]", n_seqs, L->k.n_seqs);
+    if (n_seqs <= 0 || n_seqs > seq_limit)
+        return fail(KVQ_EINVAL, "n_seqs %d outside [1, %d]", n_seqs, seq_limit);
     if (q_len <= 0 || q_len > KVQ_MAX_QUERIES)
         return fail(KVQ_EINVAL, "q_len %d outside [1, %d]", q_len, KVQ_MAX_QUERIES);
     if (n_q_heads <= 0 || n_q_heads % L->k.n_kv_heads != 0)
@@ -175,9 +223,8 @@ kvq_status attend_decode(const kvq_layer *L, const float *app_k, const float *ap
     const int gqa = n_q_heads / L->k.n_kv_heads;
     if (gqa > KVQ_MAX_GQA)
         return fail(KVQ_EUNSUPPORTED, "%d q-heads per kv-head exceeds %d", gqa, KVQ_MAX_GQA);
-    if (max_len < 0 || max_len > L->k.capacity)
-        return fail(KVQ_ERANGE, "max_len %lld outside [0, capacity %lld]", (long long)max_len,
-                    (long long)L->k.capacity);
+    if (max_len < 0 || max_len > cap)
+        return fail(KVQ_ERANGE, "max_len %lld outside [0, capacity %lld]", (long long)max_len, (long long)cap);
     if (!(softmax_scale == softmax_scale)) return fail(KVQ_EINVAL, "softmax_scale is NaN");
     if (!kvq::decode_supported(L->k.codec, L->v.codec, L->k.head_dim))
         return fail(KVQ_EUNSUPPORTED, "no decode kernel for this codec pair/head_dim");
@@ -195,6 +242,7 @@ kvq_status attend_decode(const kvq_layer *L, const float *app_k, const float *ap
     kvq::DecodeArgs a;
     a.k = view(L->k);
     a.v = view(L->v);
+    a.pt = pt;
     a.seq_len = seq_len;
     char *ws = static_cast<char *>(workspace);
     a.part_ml = reinterpret_cast<float *>(ws + p.off_part_ml);
@@ -237,8 +285,10 @@ kvq_status kvq_attend_decode(const kvq_layer *L, const float *q, const int64_t *
                              int32_t n_seqs, int32_t n_q_heads, int64_t max_len,
                              float softmax_scale, float *out, void *workspace, size_t ws_bytes,
                              void *hip_stream) {
-    return attend_decode(L, nullptr, nullptr, q, seq_len, n_seqs, 1, n_q_heads, max_len, softmax_scale, out,
-                         workspace, ws_bytes, hip_stream);
+    kvq_status st = check_layer(L);
+    if (st != KVQ_OK) return st;
+    return attend_decode(L, no_pages(), nullptr, nullptr, q, seq_len, n_seqs, 1, n_q_heads, max_len, softmax_scale,
+                         out, workspace, ws_bytes, hip_stream);
 }
 
 size_t kvq_decode_mq_workspace_bytes(const kvq_layer *L, int32_t n_q_heads, int32_t n_seqs,
@@ -250,8 +300,10 @@ kvq_status kvq_attend_decode_mq(const kvq_layer *L, const float *q, const int64_
                                 int32_t n_seqs, int32_t q_len, int32_t n_q_heads, int64_t max_len,
                                 float softmax_scale, float *out, void *workspace, size_t ws_bytes,
                                 void *hip_stream) {
-    return attend_decode(L, nullptr, nullptr, q, seq_len, n_seqs, q_len, n_q_heads, max_len, softmax_scale, out,
-                         workspace, ws_bytes, hip_stream);
+    kvq_status st = check_layer(L);
+    if (st != KVQ_OK) return st;
+    return attend_decode(L, no_pages(), nullptr, nullptr, q, seq_len, n_seqs, q_len, n_q_heads, max_len,
+                         softmax_scale, out, workspace, ws_bytes, hip_stream);
 }
 
 kvq_status kvq_append_attend_decode(const kvq_layer *L, const float *k_new, const float *v_new, const float *q,
@@ -259,8 +311,10 @@ kvq_status kvq_append_attend_decode(const kvq_layer *L, const float *k_new, cons
                                     float softmax_scale, float *out, void *workspace, size_t ws_bytes,
                                     void *hip_stream) {
     if (!k_new || !v_new) return fail(KVQ_EINVAL, "null k_new/v_new");
-    return attend_decode(L, k_new, v_new, q, seq_len, n_seqs, 1, n_q_heads, max_len, softmax_scale, out,
-                         workspace, ws_bytes, hip_stream);
+    kvq_status st = check_layer(L);
+    if (st != KVQ_OK) return st;
+    return attend_decode(L, no_pages(), k_new, v_new, q, seq_len, n_seqs, 1, n_q_heads, max_len, softmax_scale,
+                         out, workspace, ws_bytes, hip_stream);
 }
 
 kvq_status kvq_append_attend_decode_mq(const kvq_layer *L, const float *k_new, const float *v_new,
@@ -268,8 +322,38 @@ kvq_status kvq_append_attend_decode_mq(const kvq_layer *L, const float *k_new, c
                                        int32_t n_q_heads, int64_t max_len, float softmax_scale, float *out,
                                        void *workspace, size_t ws_bytes, void *hip_stream) {
     if (!k_new || !v_new) return fail(KVQ_EINVAL, "null k_new/v_new");
-    return attend_decode(L, k_new, v_new, q, seq_len, n_seqs, q_len, n_q_heads, max_len, softmax_scale, out,
-                         workspace, ws_bytes, hip_stream);
+    kvq_status st = check_layer(L);
+    if (st != KVQ_OK) return st;
+    return attend_decode(L, no_pages(), k_new, v_new, q, seq_len, n_seqs, q_len, n_q_heads, max_len,
+                         softmax_scale, out, workspace, ws_bytes, hip_stream);
+}
+
+size_t kvq_paged_decode_workspace_bytes(const kvq_paged_layer *P, int32_t n_q_heads, int32_t n_seqs,
+                                        int32_t q_len, int64_t max_len) {
+    return P ? decode_ws_bytes(&P->pool, n_q_heads, n_seqs, q_len, max_len) : 0;
+}
+
+kvq_status kvq_paged_attend_decode_mq(const kvq_paged_layer *P, const float *q, const int64_t *seq_len,
+                                      int32_t n_seqs, int32_t q_len, int32_t n_q_heads, int64_t max_len,
+                                      float softmax_scale, float *out, void *workspace, size_t ws_bytes,
+                                      void *hip_stream) {
+    kvq::PageTable pt;
+    kvq_status st = check_paged(P, &pt);
+    if (st != KVQ_OK) return st;
+    return attend_decode(&P->pool, pt, nullptr, nullptr, q, seq_len, n_seqs, q_len, n_q_heads, max_len,
+                         softmax_scale, out, workspace, ws_bytes, hip_stream);
+}
+
+kvq_status kvq_paged_append_attend_decode_mq(const kvq_paged_layer *P, const float *k_new, const float *v_new,
+                                             const float *q, const int64_t *seq_len, int32_t n_seqs, int32_t q_len,
+                                             int32_t n_q_heads, int64_t max_len, float softmax_scale, float *out,
+                                             void *workspace, size_t ws_bytes, void *hip_stream) {
+    if (!k_new || !v_new) return fail(KVQ_EINVAL, "null k_new/v_new");
+    kvq::PageTable pt;
+    kvq_status st = check_paged(P, &pt);
+    if (st != KVQ_OK) return st;
+    return attend_decode(&P->pool, pt, k_new, v_new, q, seq_len, n_seqs, q_len, n_q_heads, max_len,
+                         softmax_scale, out, workspace, ws_bytes, hip_stream);
 }
 
 size_t kvq_prefill_workspace_bytes(const kvq_layer *L, int32_t n_q_heads, int32_t n_tokens) {

@@ -22,9 +22,21 @@ struct PlaneView {
     int64_t head_scale_stride;  // binary16 per (seq, head) = capacity/32 * block_scales
 };
 
+// Paged planes: the planes are a pool of pages (PlaneView.n_seqs = pages,
+// capacity = rows per page); row r of sequence b lives in page
+// table[b * table_stride + r / page_rows] at row r % page_rows.
+// table == nullptr: contiguous planes (sequence b is "page" b).
+struct PageTable {
+    const int32_t *table;
+    int table_stride;        // entries per sequence
+    int page_rows;           // multiple of 32
+    int n_seqs;              // sequences (rows of the table)
+};
+
 // Both planes of a layer are appended by one launch (grid.y = plane).
 struct AppendArgs {
     PlaneView plane[2];      // K, V
+    PageTable pt;
     const float *x[2];       // [n_tokens][n_kv_heads][head_dim]; null = skip that plane
     const int32_t *seq_idx;  // [n_tokens]
     const int64_t *pos;      // [n_tokens]
@@ -43,6 +55,7 @@ struct DequantArgs {
 
 struct DecodeArgs {
     PlaneView k, v;
+    PageTable pt;
     // q and out hold q_len consecutive queries per sequence ([q_len][Hq][D] at
     // q + b * q_seq_stride); query i of sequence b sits at row
     // len_b - 1 - q_tail - (q_len - 1 - i) and attends rows up to it.

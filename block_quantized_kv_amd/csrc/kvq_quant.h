@@ -91,4 +91,21 @@ __device__ __forceinline__ void quantize_store(const PlaneView &pl, int64_t head
     }
 }
 
+// Where row `pos` of sequence `seq`, kv-head `head` lives: head_lin indexes
+// the planes' (sequence-or-page, kv-head) ranges, row the row inside it.
+// Paged planes look the page up in the table (one load); false if the table
+// sends the row outside the pool (nothing may be stored then).
+__device__ __forceinline__ bool phys_row(const PlaneView &pl, const PageTable &pt, int64_t seq, int head, int64_t pos,
+                                         int64_t &head_lin, int64_t &row) {
+    if (!pt.table) {
+        head_lin = seq * pl.n_kv_heads + head;
+        row = pos;
+        return true;
+    }
+    const int32_t page = pt.table[seq * pt.table_stride + pos / pt.page_rows];
+    head_lin = (int64_t)page * pl.n_kv_heads + head;
+    row = pos % pt.page_rows;
+    return page >= 0 && page < pl.n_seqs;
+}
+
 }  // namespace kvq

@@ -211,6 +211,56 @@ kvq_status kvq_append_attend_decode_mq(const kvq_layer *L, const float *k_new, c
                                        float softmax_scale, float *out, void *workspace, size_t ws_bytes,
                                        void *hip_stream);
 
+/* ---- paged planes (den_llama.cpp, "Adaptive KV streaming (contributed)": a
+ * bounded device pool of resident KV pages; here the pool itself, addressed
+ * through a per-sequence block table, without the host tier) ------------- */
+
+/* A page pool plus the table that maps each sequence's rows to pages.
+ *   pool        : k and v planes laid out exactly as contiguous planes whose
+ *                 n_seqs is the number of pages and whose capacity is the
+ *                 rows per page (a multiple of 32); each page holds those
+ *                 rows for every kv-head.
+ *   block_table : device int32 [n_seqs][max_pages]; entry [b][i] is the page
+ *                 that holds rows [i * page_rows, (i + 1) * page_rows) of
+ *                 sequence b.  A sequence's capacity is max_pages * page_rows.
+ * Pages need not be distinct across sequences only if the rows they hold are
+ * never written through both.  An entry outside [0, pages) makes the
+ * attention read zeros for those rows and the append skip them (no memory
+ * outside the pool is touched; kvq_paged_append reports KVQ_ERANGE through
+ * dev_status). */
+typedef struct {
+    kvq_layer pool;
+    const int32_t *block_table;
+    int32_t n_seqs;
+    int32_t max_pages;
+} kvq_paged_layer;
+
+/* kvq_append through the table: seq_idx in [0, n_seqs), pos in
+ * [0, max_pages * page_rows). */
+kvq_status kvq_paged_append(const kvq_paged_layer *P, const float *k_new, const float *v_new,
+                            const int32_t *seq_idx, const int64_t *pos, int32_t n_tokens, int32_t *dev_status,
+                            void *hip_stream);
+
+/* Workspace bytes of the two calls below (host only). */
+size_t kvq_paged_decode_workspace_bytes(const kvq_paged_layer *P, int32_t n_q_heads, int32_t n_seqs,
+                                        int32_t q_len, int64_t max_len);
+
+/* kvq_attend_decode_mq (q_len = 1: kvq_attend_decode) over paged planes:
+ * the same result as on contiguous planes holding the same rows; max_len
+ * <= max_pages * page_rows. */
+kvq_status kvq_paged_attend_decode_mq(const kvq_paged_layer *P, const float *q, const int64_t *seq_len,
+                                      int32_t n_seqs, int32_t q_len, int32_t n_q_heads, int64_t max_len,
+                                      float softmax_scale, float *out, void *workspace, size_t ws_bytes,
+                                      void *hip_stream);
+
+/* kvq_append_attend_decode_mq over paged planes (the new rows go through
+ * the table too). */
+kvq_status kvq_paged_append_attend_decode_mq(const kvq_paged_layer *P, const float *k_new, const float *v_new,
+                                             const float *q, const int64_t *seq_len, int32_t n_seqs,
+                                             int32_t q_len, int32_t n_q_heads, int64_t max_len,
+                                             float softmax_scale, float *out, void *workspace, size_t ws_bytes,
+                                             void *hip_stream);
+
 /* ---- chunked-prefill attention (den_llama.cpp, "Results": prefill with the
  * quantized cache and 2048-token micro-batches; Llaminar, "GPU Graph
  * Capture": prefill runs in chunks) --------------------------------------- */
