@@ -121,11 +121,16 @@ struct Cfg {
     static constexpr int NS_FIT = (kLdsBytes - OFF_SLOTS) / (kWaves * SLOT);
     static constexpr int NS_TGT = kInflightBytes / (kWaves * SLOT) < 1 ? 1 : kInflightBytes / (kWaves * SLOT);
     static constexpr int NS = NS_TGT < NS_FIT ? (NS_TGT < 3 ? NS_TGT : 3) : NS_FIT;
+    // A one-block ring starts with two blocks per wave when LDS allows: the
+    // wave then has its second block on the way while it computes its first,
+    // instead of requesting it only once the first has arrived.
+    static constexpr bool HEAD2 = NS == 1 && NS_FIT >= 2;
+    static constexpr int NSLOT = NS + (HEAD2 ? 1 : 0);  // slots per wave
     static_assert(NS >= 1, "one block slot per wave must fit in LDS");
     static_assert((NS - 1) * N_DMA <= 63, "DMAs in flight exceed the wait counter");
     static_assert(SL_V % 16 == 0 && SL_KS % 16 == 0 && SL_VS % 16 == 0 && SLOT % 16 == 0, "slot alignment");
-    static_assert((NS - 1) * SLOT + SLOT <= 65535, "slot offsets fit the DS immediate");
-    static constexpr int LDS_STREAM = OFF_SLOTS + kWaves * NS * SLOT;
+    static_assert(NSLOT * SLOT <= 65535, "slot offsets fit the DS immediate");
+    static constexpr int LDS_STREAM = OFF_SLOTS + kWaves * NSLOT * SLOT;
     // the final merge parks every wave's output columns, DP floats apart
     // (D + 16: conflict-free 16-byte writes), from OFF_SLOTS on
     static constexpr int DP = D + 16;
@@ -391,7 +396,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
                       (uint32_t)nblk * C::K_BLOCK_SCALES * 2);
     st.vs = make_rsrc(a.v.scales + head_lin * a.v.head_scale_stride + blk0 * C::V_BLOCK_SCALES,
                       (uint32_t)nblk * C::V_BLOCK_SCALES * 2);
-    unsigned char *myslots = smem + C::OFF_SLOTS + wave * NS * C::SLOT;
+    unsigned char *myslots = smem + C::OFF_SLOTS + wave * C::NSLOT * C::SLOT;
     // paged planes: the split's page numbers, entry j in lane j % 64 of
     // pages[j / 64] (a split spans at most 128 blocks, so at most 128 pages)
     constexpr bool paged = PAGED;
@@ -471,7 +476,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
         m = quad_max(m, x32);
         if (q4 == 0) ds_wr(lds0 + (wave * 16 + h) * 4, __builtin_bit_cast(uint32_t, m), C::OFF_TMAX);
     }
-    if (tid == 0) ds_wr(lds0, (uint32_t)(NS * kWaves), C::OFF_CNT);
+    if (tid == 0) ds_wr(lds0, (uint32_t)(C::NSLOT * kWaves), C::OFF_CNT);
     lds_barrier();
     if (wave >= dma_late) issue(wave, myslots);
 
@@ -528,6 +533,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
 
 #pragma unroll
     for (int s = 1; s < NS; ++s) issue(wave + s * kWaves, myslots + s * C::SLOT);
+    if constexpr (C::HEAD2) issue(wave + kWaves, myslots + C::SLOT);
 
     // LDS byte addresses for the hand-issued reads
     const uint32_t lds_slots = (uint32_t)(uintptr_t)(lds_void *)myslots;
@@ -660,6 +666,27 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     int sidx[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) sidx[s] = wave + s * kWaves;
+    if constexpr (C::HEAD2) {
+        // slot 0 holds block `wave`, slot 1 block `wave + 8`: the first is
+        // consumed without a refill, the second refills slot 0, where the
+        // one-block ring then continues
+        if (wave < nblk) {
+            vm_wait<C::N_DMA>();
+            Payload<D, KC, VC> pl;
+            read_slot<D, KC, VC>(pl, a16, a8, a4, aks, avs, 0);
+            process(pl, wave);
+        }
+        sidx[0] = nblk;
+        if (wave + kWaves < nblk) {
+            vm_wait<0>();
+            Payload<D, KC, VC> pl;
+            read_slot<D, KC, VC>(pl, a16, a8, a4, aks, avs, C::SLOT);
+            const int nxt = grab();
+            sidx[0] = nxt;
+            issue(nxt, myslots);
+            process(pl, wave + kWaves);
+        }
+    }
     bool live = true;
     while (live) {
         [&]<int... S>(std::integer_sequence<int, S...>) {
