@@ -97,8 +97,9 @@ struct Cfg {
     static constexpr int SL_KS = SL_V + V_BLOCK_BYTES;
     static constexpr int SL_VS = SL_KS + 2 * K_BLOCK_SCALES;
     static constexpr int SLOT = SL_VS + 2 * V_BLOCK_SCALES;
-    static constexpr int N_DMA = dma_count(K_BLOCK_BYTES) + dma_count(V_BLOCK_BYTES) +
-                                 dma_count(2 * K_BLOCK_SCALES) + dma_count(2 * V_BLOCK_SCALES);
+    static constexpr int N_DMA_K = dma_count(K_BLOCK_BYTES) + dma_count(2 * K_BLOCK_SCALES);
+    static constexpr int N_DMA_V = dma_count(V_BLOCK_BYTES) + dma_count(2 * V_BLOCK_SCALES);
+    static constexpr int N_DMA = N_DMA_K + N_DMA_V;
     // per-lane scale words of one block: K (4 rows x KNG groups per tile),
     // V (8 rows x VNG groups)
     static constexpr int KS_LANE_BYTES = 8 * KNG;   // per tile
@@ -121,10 +122,17 @@ struct Cfg {
     static constexpr int NS_FIT = (kLdsBytes - OFF_SLOTS) / (kWaves * SLOT);
     static constexpr int NS_TGT = kInflightBytes / (kWaves * SLOT) < 1 ? 1 : kInflightBytes / (kWaves * SLOT);
     static constexpr int NS = NS_TGT < NS_FIT ? (NS_TGT < 3 ? NS_TGT : 3) : NS_FIT;
+    // Blocks whose one-lane share is 80 words or more at head_dim 256 (8-bit
+    // codes, or q4_0 K with its 8 scale groups) are read in two halves: the K
+    // half is copied, refilled and scored before the V half is copied, so
+    // both are never held in registers at once (the single copy spills)
+    static constexpr int NWK = 2 * K_WORDS + KS_LANE_BYTES / 2;
+    static constexpr int NWV = V_WORDS + VS_LANE_BYTES / 4;
+    static constexpr bool TWO_PHASE = NS == 1 && NWK + NWV >= 80 && D == 256;
     // A one-block ring starts with two blocks per wave when LDS allows: the
     // wave then has its second block on the way while it computes its first,
     // instead of requesting it only once the first has arrived.
-    static constexpr bool HEAD2 = NS == 1 && NS_FIT >= 2;
+    static constexpr bool HEAD2 = NS == 1 && NS_FIT >= 2 && !TWO_PHASE;
     static constexpr int NSLOT = NS + (HEAD2 ? 1 : 0);  // slots per wave
     static_assert(NS >= 1, "one block slot per wave must fit in LDS");
     static_assert((NS - 1) * N_DMA <= 63, "DMAs in flight exceed the wait counter");
@@ -171,13 +179,25 @@ __device__ __forceinline__ void dma_region(__amdgpu_buffer_rsrc_t r, uint32_t go
     }
 }
 
+// The K half (codes, scales) or the V half of block idx, as one DMA group.
+template <int D, int KC, int VC>
+__device__ __forceinline__ void dma_half(const Streams &st, int idx, unsigned char *slot, int lane, bool k_half) {
+    using C = Cfg<D, KC, VC>;
+    if (k_half) {
+        dma_region<C::K_BLOCK_BYTES>(st.kc, (uint32_t)idx * C::K_BLOCK_BYTES, slot + C::SL_K, lane);
+        dma_region<2 * C::K_BLOCK_SCALES>(st.ks, (uint32_t)idx * C::K_BLOCK_SCALES * 2, slot + C::SL_KS, lane);
+    } else {
+        dma_region<C::V_BLOCK_BYTES>(st.vc, (uint32_t)idx * C::V_BLOCK_BYTES, slot + C::SL_V, lane);
+        dma_region<2 * C::V_BLOCK_SCALES>(st.vs, (uint32_t)idx * C::V_BLOCK_SCALES * 2, slot + C::SL_VS, lane);
+    }
+}
+
+// Both halves, K first.
 template <int D, int KC, int VC>
 __device__ __forceinline__ void dma_block(const Streams &st, int idx, unsigned char *slot, int lane) {
     using C = Cfg<D, KC, VC>;
-    dma_region<C::K_BLOCK_BYTES>(st.kc, (uint32_t)idx * C::K_BLOCK_BYTES, slot + C::SL_K, lane);
-    dma_region<C::V_BLOCK_BYTES>(st.vc, (uint32_t)idx * C::V_BLOCK_BYTES, slot + C::SL_V, lane);
-    dma_region<2 * C::K_BLOCK_SCALES>(st.ks, (uint32_t)idx * C::K_BLOCK_SCALES * 2, slot + C::SL_KS, lane);
-    dma_region<2 * C::V_BLOCK_SCALES>(st.vs, (uint32_t)idx * C::V_BLOCK_SCALES * 2, slot + C::SL_VS, lane);
+    dma_half<D, KC, VC>(st, idx, slot, lane, true);
+    dma_half<D, KC, VC>(st, idx, slot, lane, false);
 }
 
 // ---- hand-issued LDS reads (no wait; see lds_wait).  `off` must fold to a
@@ -279,12 +299,12 @@ __device__ __forceinline__ Streams page_block_streams(const DecodeArgs &a, int p
 template <int D, int KC, int VC>
 struct Payload {
     using C = Cfg<D, KC, VC>;
-    static constexpr int NW = 2 * C::K_WORDS + C::V_WORDS + C::KS_LANE_BYTES / 2 + C::VS_LANE_BYTES / 4;
+    static constexpr int NW = C::NWK + C::NWV;  // [K tiles][K scales] [V][V scales]
     uint32_t w[NW];
     __device__ __forceinline__ uint32_t *k(int tau) { return w + tau * C::K_WORDS; }
-    __device__ __forceinline__ uint32_t *v() { return w + 2 * C::K_WORDS; }
-    __device__ __forceinline__ uint32_t *ks(int tau) { return w + 2 * C::K_WORDS + C::V_WORDS + tau * (C::KS_LANE_BYTES / 4); }
-    __device__ __forceinline__ uint32_t *vs() { return w + 2 * C::K_WORDS + C::V_WORDS + C::KS_LANE_BYTES / 2; }
+    __device__ __forceinline__ uint32_t *ks(int tau) { return w + 2 * C::K_WORDS + tau * (C::KS_LANE_BYTES / 4); }
+    __device__ __forceinline__ uint32_t *v() { return w + C::NWK; }
+    __device__ __forceinline__ uint32_t *vs() { return w + C::NWK + C::V_WORDS; }
 };
 
 template <int D, int KC, int VC>
@@ -298,6 +318,26 @@ __device__ __forceinline__ void read_slot(Payload<D, KC, VC> &pl, uint32_t a16, 
     ds_rd_span<C::KS_LANE_BYTES>(pl.ks(1), aks, soff + C::SL_KS + 32 * C::KNG);
     ds_rd_span<C::VS_LANE_BYTES>(pl.vs(), avs, soff + C::SL_VS);
     lds_wait<Payload<D, KC, VC>::NW>(pl.w);
+}
+// The K half alone (codes of both tiles and their scales) ...
+template <int D, int KC, int VC>
+__device__ __forceinline__ void read_slot_k(Payload<D, KC, VC> &pl, uint32_t a16, uint32_t a8, uint32_t a4,
+                                            uint32_t aks, int soff) {
+    using C = Cfg<D, KC, VC>;
+    ds_rd_lane<C::K_LB>(pl.k(0), a16, a8, a4, soff + C::SL_K);
+    ds_rd_lane<C::K_LB>(pl.k(1), a16, a8, a4, soff + C::SL_K + C::K_TILE_BYTES);
+    ds_rd_span<C::KS_LANE_BYTES>(pl.ks(0), aks, soff + C::SL_KS);
+    ds_rd_span<C::KS_LANE_BYTES>(pl.ks(1), aks, soff + C::SL_KS + 32 * C::KNG);
+    lds_wait<C::NWK>(pl.w);
+}
+// ... and the V half.
+template <int D, int KC, int VC>
+__device__ __forceinline__ void read_slot_v(Payload<D, KC, VC> &pl, uint32_t a16, uint32_t a8, uint32_t a4,
+                                            uint32_t avs, int soff) {
+    using C = Cfg<D, KC, VC>;
+    ds_rd_lane<C::V_LB>(pl.v(), a16, a8, a4, soff + C::SL_V);
+    ds_rd_span<C::VS_LANE_BYTES>(pl.vs(), avs, soff + C::SL_VS);
+    lds_wait<C::NWV>(pl.v());
 }
 
 // Fused append, run by one wave: quantizes and stores rows [lo, hi) of kv-head
@@ -409,11 +449,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
         for (int j = 0; j < 2; ++j)
             if (lane + 64 * j < npg) pages[j] = a.pt.table[(int64_t)b * a.pt.table_stride + pg0 + lane + 64 * j];
     }
-    // issues the DMAs of local block idx into `slot` (past the split: cut off)
-    auto issue = [&](int idx, unsigned char *slot) {
-        if constexpr (!paged) {
-            dma_block<D, KC, VC>(st, idx, slot, lane);
-        } else {
+    // issues the DMAs of local block idx into `slot` (past the split: cut
+    // off): part 0 the whole block, 1 its K half, 2 its V half
+    auto issue_part = [&](int idx, unsigned char *slot, int part) {
+        Streams bs = st;
+        int bidx = idx;
+        if constexpr (paged) {
             int page = -1, within = 0;
             if (idx < nblk) {
                 const int64_t gb = blk0 + idx;
@@ -421,9 +462,15 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
                 page = __builtin_amdgcn_readlane(j < 64 ? pages[0] : pages[1], j & 63);
                 within = (int)(gb % pblk);
             }
-            dma_block<D, KC, VC>(page_block_streams<D, KC, VC>(a, page, kvh, within), 0, slot, lane);
+            bs = page_block_streams<D, KC, VC>(a, page, kvh, within);
+            bidx = 0;
         }
+        if (part == 0)
+            dma_block<D, KC, VC>(bs, bidx, slot, lane);
+        else
+            dma_half<D, KC, VC>(bs, bidx, slot, lane, part == 1);
     };
+    auto issue = [&](int idx, unsigned char *slot) { issue_part(idx, slot, 0); };
 
     // ---- query prologue, part 1: wave w loads the slice of channel step w
     // (8 channels per lane)
@@ -547,7 +594,15 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     float m_run = -INFINITY, l_run = 0.0f;
 
     // Computes block idx from its words.
-    auto process = [&](Payload<D, KC, VC> &pl, int idx) {
+    // rows from block idx's start to the sequence end (capped: only whether
+    // it reaches past the block matters)
+    auto rows_to_end = [&](int idx) -> int {
+        const int64_t rte64 = len - (r0 + (int64_t)idx * kBlockRows);
+        return rte64 < (1 << 20) ? (int)rte64 : (1 << 20);
+    };
+    // Scores, masking and the softmax update of block idx from its K half;
+    // returns the probabilities (the P^T operand).
+    auto process_s = [&](Payload<D, KC, VC> &pl, int idx) -> h8 {
         // ---- scores S^T for the two 16-row tiles, channel steps in lockstep
         const f16_alias *ksc0 = reinterpret_cast<const f16_alias *>(pl.ks(0));
         const f16_alias *ksc1 = reinterpret_cast<const f16_alias *>(pl.ks(1));
@@ -584,11 +639,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
         for (int tau = 0; tau < 2; ++tau)
 #pragma unroll
             for (int r = 0; r < 4; ++r) S[tau][r] *= c_h;
-        uint32_t *vsw = pl.vs();
-        // rows from this block's start to the sequence end (capped: only
-        // whether it reaches past the block matters)
-        const int64_t rte64 = len - (r0 + (int64_t)idx * kBlockRows);
-        const int rend = rte64 < (1 << 20) ? (int)rte64 : (1 << 20);
+        const int rend = rows_to_end(idx);
         if (rend - maxdelay < kBlockRows) {
             // row 16*tau + 4*q4 + r is visible to this column iff 16*tau + r < lim
             const int lim = rend - cdelay - 4 * q4;
@@ -597,22 +648,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
                     if (16 * tau + r >= lim) S[tau][r] = -INFINITY;
-            const int vlim = rend - 4 * q4;  // rows past the sequence end
-            // rows past the end get a zero V scale, so that bytes that were
-            // never written cannot turn 0 * V into NaN; word g*4+m holds the
-            // scales of rows (m/2)*16 + 4*q4 + 2*(m%2) + {0, 1}
-#pragma unroll
-            for (int g = 0; g < C::VNG; ++g)
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    const int j0 = (m >> 1) * 16 + 2 * (m & 1);
-                    uint32_t word = vsw[g * 4 + m];
-                    if (j0 >= vlim) word &= 0xFFFF0000u;
-                    if (j0 + 1 >= vlim) word &= 0x0000FFFFu;
-                    vsw[g * 4 + m] = word;
-                }
         }
-        const h2_alias *svb = reinterpret_cast<const h2_alias *>(vsw);
 
         // ---- online softmax (log2 domain)
         float mx = S[0][0];
@@ -642,6 +678,29 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
                 l_run += p;
                 P[4 * tau + r] = (_Float16)p;
             }
+        return P;
+    };
+    // O^T += V^T P^T for block idx from its V half.
+    auto process_v = [&](Payload<D, KC, VC> &pl, int idx, const h8 &P) {
+        uint32_t *vsw = pl.vs();
+        const int rend = rows_to_end(idx);
+        if (rend < kBlockRows) {
+            const int vlim = rend - 4 * q4;  // rows past the sequence end
+            // rows past the end get a zero V scale, so that bytes that were
+            // never written cannot turn 0 * V into NaN; word g*4+m holds the
+            // scales of rows (m/2)*16 + 4*q4 + 2*(m%2) + {0, 1}
+#pragma unroll
+            for (int g = 0; g < C::VNG; ++g)
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const int j0 = (m >> 1) * 16 + 2 * (m & 1);
+                    uint32_t word = vsw[g * 4 + m];
+                    if (j0 >= vlim) word &= 0xFFFF0000u;
+                    if (j0 + 1 >= vlim) word &= 0x0000FFFFu;
+                    vsw[g * 4 + m] = word;
+                }
+        }
+        const h2_alias *svb = reinterpret_cast<const h2_alias *>(vsw);
 
         // ---- O^T += V^T P^T, one 16-channel block at a time
 #pragma unroll
@@ -650,6 +709,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
             const h8 vop = v_operand<VC>(&pl.v()[is8(VC) ? 2 * cb : cb], svb + gv * 4);
             O[cb] = mfma16x16x32(vop, P, O[cb]);
         }
+    };
+    auto process = [&](Payload<D, KC, VC> &pl, int idx) {
+        const h8 P = process_s(pl, idx);
+        process_v(pl, idx, P);
     };
 
     // ---- the ring.  Slot s starts with block w + 8 s; each refill takes the
@@ -686,6 +749,28 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
             issue(nxt, myslots);
             process(pl, wave + kWaves);
         }
+    }
+    if constexpr (C::TWO_PHASE) {
+        // one slot, refilled half by half: the K half of the next block is
+        // requested once this block's K half is copied, its V half once this
+        // block's V half is copied.  DMA order K(n), V(n), K(n+1), V(n+1):
+        // K(n) has landed when at most the V(n) DMAs remain, V(n) when at
+        // most the K(n+1) DMAs remain.
+        int cur = wave;
+        while (cur < nblk) {
+            Payload<D, KC, VC> pl;
+            vm_wait<C::N_DMA_V>();
+            read_slot_k<D, KC, VC>(pl, a16, a8, a4, aks, 0);
+            const int nxt = grab();
+            issue_part(nxt, myslots, 1);
+            const h8 P = process_s(pl, cur);
+            vm_wait<C::N_DMA_K>();
+            read_slot_v<D, KC, VC>(pl, a16, a8, a4, avs, 0);
+            issue_part(nxt, myslots, 2);
+            process_v(pl, cur, P);
+            cur = nxt;
+        }
+        sidx[0] = nblk;  // the ring below has nothing left
     }
     bool live = true;
     while (live) {
