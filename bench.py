@@ -381,6 +381,7 @@ def main():
     if not args.step_only:
         run_multi_query(torch, dev, cfg, caches, k_new2, v_new2, seq_len, nb, args, stream, result)
         result["paged"] = run_paged(torch, dev, cfg, base, k_new, v_new, q, seq_len, nb, args)
+        result["long_context"] = run_long_context(torch, dev, args)
     if speak is not None:
         result["stream_read_peak"] = speak
     if not args.no_baselines:
@@ -424,6 +425,57 @@ def stream_peak(torch, dev, reps: int = 48) -> dict:
         by[str(nwg)] = round(win * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
     del buf
     return {"gbs": max(by.values()), "by_workgroups_of_8_waves": by, "bytes_per_launch": win}
+
+
+def run_long_context(torch, dev, args) -> dict:
+    """The 196K-context split-KV configuration: four layers (layer 0 q8_0 K/V,
+    layers 1-3 Q4_G64), one kvq_attend_decode per layer per step, timed as
+    HIP-graph replays of the four calls (1.07 GB of K/V per step, so no
+    rotation is needed)."""
+    import workloads
+    from block_quantized_kv_amd import Layer, decode_workspace, kvq_append, kvq_attend_decode
+    cfg = workloads.CONFIGS[4]
+    n, H, d = cfg.ctx, cfg.n_kv_heads, cfg.head_dim
+    layers, qs, outs, kv_bytes = [], [], [], []
+    for li, (kc, vc) in enumerate(cfg.layers):
+        L = Layer.create(kc, vc, d, H, 1, cfg.capacity, device=dev)
+        for a in range(0, n, 32768):
+            b = min(n, a + 32768)
+            k = workloads.kv_rows(cfg, li, 0, "k", a, b - a, dev)
+            v = workloads.kv_rows(cfg, li, 0, "v", a, b - a, dev)
+            kvq_append(L, k, v, torch.zeros(b - a, dtype=torch.int32, device=dev),
+                       torch.arange(a, b, dtype=torch.int64, device=dev))
+            del k, v
+        layers.append(L)
+        qs.append(workloads.queries(cfg, li, dev))
+        outs.append(torch.empty_like(qs[-1]))
+        kv_bytes.append(L.k.nbytes + L.v.nbytes)
+    ws = decode_workspace(layers[0], cfg.n_q_heads, 1, n)
+    lens = torch.tensor([n], dtype=torch.int64, device=dev)
+    cap = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cap):
+        for li, L in enumerate(layers):
+            kvq_attend_decode(L, qs[li], lens, n, cfg.scale, out=outs[li], workspace=ws, stream=cap)
+        with torch.cuda.graph(g, stream=cap):
+            for li, L in enumerate(layers):
+                kvq_attend_decode(L, qs[li], lens, n, cfg.scale, out=outs[li], workspace=ws, stream=cap)
+    torch.cuda.synchronize()
+    reps = max(8, args.steps // 16)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g.replay()
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    total = sum(kv_bytes)
+    del layers
+    return {"workload": cfg.name, "context": n, "layers": [f"{kc}/{vc}" for kc, vc in cfg.layers],
+            "ms_per_step": round(ms, 5), "kv_bytes_per_step": total,
+            "value": round(total / (ms * 1e-3) / 1e9, 2), "unit": "GB/s",
+            "step": "4 x kvq_attend_decode (one per layer), HIP-graph replay"}
 
 
 def run_paged(torch, dev, cfg, base, k_new, v_new, q, seq_len, nb, args) -> dict:
