@@ -24,7 +24,9 @@
 //  * Causal mask only on tiles that cross a column's diagonal; rows past the
 //    needed range get a zero V so never-written bytes cannot leak NaN.
 //  * The two LDS tile buffers alternate, so the dequant of tile k+1 overlaps
-//    the products of tile k.
+//    the products of tile k; tile k+2's codes are loaded into registers and
+//    its scales staged in LDS during iteration k, so the dequant never waits
+//    for memory.
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -66,6 +68,14 @@ struct PCfg {
     static constexpr int K_TILE_ELEMS = kTileRows * KS;
     static constexpr int V_TILE_ELEMS = D * VS;
     static constexpr int BUF_ELEMS = K_TILE_ELEMS + V_TILE_ELEMS;
+    // dequant units per thread, and a tile's scales (both blocks, K then V)
+    static constexpr int UK = (K_UNITS + kPThreads - 1) / kPThreads;
+    static constexpr int UV = (V_UNITS + kPThreads - 1) / kPThreads;
+    static constexpr int KSC_BYTES = 2 * 2 * K_BLOCK_SCALES;
+    static constexpr int VSC_BYTES = 2 * 2 * V_BLOCK_SCALES;
+    static constexpr int SC_BYTES = KSC_BYTES + VSC_BYTES;
+    static_assert(KSC_BYTES % 16 == 0 && VSC_BYTES % 16 == 0, "scale spans are whole 16-byte pieces");
+    static_assert(SC_BYTES / 16 <= kPThreads, "one 16-byte scale piece per thread");
 };
 
 __device__ __forceinline__ bfbits to_bf16(float x) {
@@ -79,33 +89,52 @@ __device__ __forceinline__ int nibble_code(uint32_t w, int p) {
     else return ((int)(w << (28 - 4 * p))) >> 28;  // sign-extend the two's complement nibble
 }
 
-// Dequantize one K lane chunk (W bytes of lane L in tile tau of block blk)
-// into K_hat rows.  rows_valid: rows of the tile (0..63) that may be read.
+// Byte offset, within the tile's two K blocks, of K dequant unit u (lane L's
+// W-byte chunk c of tile tau of block blk).
 template <int D, int KC, int VC>
-__device__ __forceinline__ void deq_k_unit(int u, const uint8_t *kblk0, const uint16_t *ksc0,
-                                           bfbits *khat) {
+__device__ __forceinline__ int k_unit_offset(int u) {
+    using C = PCfg<D, KC, VC>;
+    constexpr int CH = C::K_LB / C::K_W;
+    const int L = u & 63, c = (u >> 6) % CH, tau = (u >> 6) / CH % 2, blk = (u >> 6) / CH / 2;
+    return blk * C::K_BLOCK_BYTES + tau * C::K_TILE_BYTES + c * 64 * C::K_W + L * C::K_W;
+}
+template <int D, int KC, int VC>
+__device__ __forceinline__ int v_unit_offset(int u) {
+    using C = PCfg<D, KC, VC>;
+    constexpr int CH = C::V_LB / C::V_W;
+    const int L = u & 63, c = (u >> 6) % CH, blk = (u >> 6) / CH;
+    return blk * C::V_BLOCK_BYTES + c * 64 * C::V_W + L * C::V_W;
+}
+
+// Loads the W bytes at src into words (W = 4, 8 or 16).
+template <int W>
+__device__ __forceinline__ void load_chunk(uint32_t (&w)[W / 4], const uint8_t *src) {
+    if constexpr (W == 16) {
+        const u4 v = *reinterpret_cast<const u4 *>(src);
+        w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
+    } else if constexpr (W == 8) {
+        const u2 v = *reinterpret_cast<const u2 *>(src);
+        w[0] = v.x; w[1] = v.y;
+    } else {
+        w[0] = *reinterpret_cast<const uint32_t *>(src);
+    }
+}
+
+// Dequantize K unit u from its code words w into K_hat rows; ksc: the tile's
+// K scales (both blocks) in LDS.
+template <int D, int KC, int VC>
+__device__ __forceinline__ void deq_k_unit(int u, const uint32_t (&w)[PCfg<D, KC, VC>::K_W / 4],
+                                           const uint16_t *ksc0, bfbits *khat) {
     using C = PCfg<D, KC, VC>;
     constexpr int CH = C::K_LB / C::K_W;
     const int L = u & 63;
     const int c = (u >> 6) % CH;
     const int tau = (u >> 6) / CH % 2;
     const int blk = (u >> 6) / CH / 2;
-    const uint8_t *src = kblk0 + (int64_t)blk * C::K_BLOCK_BYTES + tau * C::K_TILE_BYTES +
-                         c * 64 * C::K_W + L * C::K_W;
-    const uint16_t *ksc = ksc0 + (int64_t)blk * C::K_BLOCK_SCALES;
+    const uint16_t *ksc = ksc0 + blk * C::K_BLOCK_SCALES;
     const int i = L & 15, kq = L >> 4;
     const int j = tau * 16 + i;        // row in block
     const int row = blk * 32 + j;      // row in tile
-    uint32_t w[C::K_W / 4];
-    if constexpr (C::K_W == 16) {
-        const u4 v = *reinterpret_cast<const u4 *>(src);
-        w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
-    } else if constexpr (C::K_W == 8) {
-        const u2 v = *reinterpret_cast<const u2 *>(src);
-        w[0] = v.x; w[1] = v.y;
-    } else {
-        w[0] = *reinterpret_cast<const uint32_t *>(src);
-    }
     constexpr int STEPS = is8(KC) ? C::K_W / 8 : C::K_W / 4;  // k-steps in this chunk
 #pragma unroll
     for (int st = 0; st < STEPS; ++st) {
@@ -129,27 +158,19 @@ __device__ __forceinline__ void deq_k_unit(int u, const uint8_t *kblk0, const ui
     }
 }
 
-// Dequantize one V lane chunk into V_hat^T [channel][row]; rows at or past
-// `vrows` (tile-relative) are written as zero.
+// Dequantize V unit u from its code words into V_hat^T [channel][row]; vsc0:
+// the tile's V scales (both blocks) in LDS; rows at or past `vrows`
+// (tile-relative) are written as zero.
 template <int D, int KC, int VC>
-__device__ __forceinline__ void deq_v_unit(int u, const uint8_t *vblk0, const uint16_t *vsc0,
-                                           bfbits *vhat, int vrows) {
+__device__ __forceinline__ void deq_v_unit(int u, const uint32_t (&w)[PCfg<D, KC, VC>::V_W / 4],
+                                           const uint16_t *vsc0, bfbits *vhat, int vrows) {
     using C = PCfg<D, KC, VC>;
     constexpr int CH = C::V_LB / C::V_W;
     const int L = u & 63;
     const int c = (u >> 6) % CH;
     const int blk = (u >> 6) / CH;
-    const uint8_t *src = vblk0 + (int64_t)blk * C::V_BLOCK_BYTES + c * 64 * C::V_W + L * C::V_W;
-    const uint16_t *vsc = vsc0 + (int64_t)blk * C::V_BLOCK_SCALES;
+    const uint16_t *vsc = vsc0 + blk * C::V_BLOCK_SCALES;
     const int c16 = L & 15, kq = L >> 4;
-    uint32_t w[C::V_W / 4];
-    if constexpr (C::V_W == 16) {
-        const u4 v = *reinterpret_cast<const u4 *>(src);
-        w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
-    } else {
-        const u2 v = *reinterpret_cast<const u2 *>(src);
-        w[0] = v.x; w[1] = v.y;
-    }
     constexpr int CBS = is8(VC) ? C::V_W / 8 : C::V_W / 4;  // channel blocks in this chunk
 #pragma unroll
     for (int k = 0; k < CBS; ++k) {
@@ -215,17 +236,62 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
     const uint16_t *vscales = a.v.scales + head_lin * a.v.head_scale_stride;
     const int64_t nblocks_plane = a.k.capacity / kBlockRows;
 
-    auto dequant_tile = [&](int tile, bfbits *buf) {
+    // The tile pipeline: a tile's codes are loaded into registers and its
+    // scales staged in LDS one iteration before it is dequantized, which is
+    // one iteration before its products, so neither the global loads nor the
+    // dequant wait in line with the matrix products.
+    uint32_t rk[C::UK][C::K_W / 4], rv[C::UV][C::V_W / 4];
+    u4 rsc = u4{0u, 0u, 0u, 0u};
+    uint16_t *sc_lds = reinterpret_cast<uint16_t *>(lds + 2 * C::BUF_ELEMS);  // [2][SC_BYTES / 2]
+    auto load_tile = [&](int tile) {
         const int64_t b0 = (int64_t)tile * 2;  // first block of the tile
-        const int vrows = (int)min((int64_t)kTileRows, nrows - (int64_t)tile * kTileRows);
         const bool two = b0 + 1 < nblocks_plane;  // the second block exists
+        const uint8_t *kb = kcodes + b0 * C::K_BLOCK_BYTES;
+        const uint8_t *vb = vcodes + b0 * C::V_BLOCK_BYTES;
+#pragma unroll
+        for (int i = 0; i < C::UK; ++i) {
+            const int u = tid + i * kPThreads;
+            if (u < C::K_UNITS && (two || u < C::K_UNITS / 2)) load_chunk<C::K_W>(rk[i], kb + k_unit_offset<D, KC, VC>(u));
+        }
+#pragma unroll
+        for (int i = 0; i < C::UV; ++i) {
+            const int u = tid + i * kPThreads;
+            if (u < C::V_UNITS && (two || u < C::V_UNITS / 2)) load_chunk<C::V_W>(rv[i], vb + v_unit_offset<D, KC, VC>(u));
+        }
+        // the tile's scales, 16 bytes per thread: K (both blocks) then V
+        const int o = tid * 16;
+        if (o < C::KSC_BYTES) {
+            if (two || o < C::KSC_BYTES / 2)
+                rsc = *reinterpret_cast<const u4 *>(reinterpret_cast<const uint8_t *>(kscales + b0 * C::K_BLOCK_SCALES) + o);
+        } else if (o < C::SC_BYTES) {
+            const int ov = o - C::KSC_BYTES;
+            if (two || ov < C::VSC_BYTES / 2)
+                rsc = *reinterpret_cast<const u4 *>(reinterpret_cast<const uint8_t *>(vscales + b0 * C::V_BLOCK_SCALES) + ov);
+        }
+    };
+    auto stage_scales = [&](int tile) {
+        if (tid * 16 < C::SC_BYTES)
+            *reinterpret_cast<u4 *>(reinterpret_cast<uint8_t *>(sc_lds + (tile & 1) * (C::SC_BYTES / 2)) + tid * 16) = rsc;
+    };
+    // dequantizes the tile whose codes are in rk/rv and whose scales are staged
+    auto dequant_tile = [&](int tile, bfbits *buf) {
+        const int64_t b0 = (int64_t)tile * 2;
+        const int vrows = (int)min((int64_t)kTileRows, nrows - (int64_t)tile * kTileRows);
+        const bool two = b0 + 1 < nblocks_plane;
+        const uint16_t *ksc = sc_lds + (tile & 1) * (C::SC_BYTES / 2);
+        const uint16_t *vsc = ksc + C::KSC_BYTES / 2;
         bfbits *khat = buf;
         bfbits *vhat = buf + C::K_TILE_ELEMS;
-        for (int u = tid; u < C::K_UNITS; u += kPThreads) {
-            if (!two && u >= C::K_UNITS / 2) continue;  // block 1 absent: its rows stay unused
-            deq_k_unit<D, KC, VC>(u, kcodes + b0 * C::K_BLOCK_BYTES, kscales + b0 * C::K_BLOCK_SCALES, khat);
+#pragma unroll
+        for (int i = 0; i < C::UK; ++i) {
+            const int u = tid + i * kPThreads;
+            if (u >= C::K_UNITS || (!two && u >= C::K_UNITS / 2)) continue;  // block 1 absent: rows unused
+            deq_k_unit<D, KC, VC>(u, rk[i], ksc, khat);
         }
-        for (int u = tid; u < C::V_UNITS; u += kPThreads) {
+#pragma unroll
+        for (int i = 0; i < C::UV; ++i) {
+            const int u = tid + i * kPThreads;
+            if (u >= C::V_UNITS) continue;
             if (!two && u >= C::V_UNITS / 2) {
                 // absent block: zero its V columns so masked products stay 0
                 const int L = u & 63, c16 = L & 15, kq = L >> 4;
@@ -240,8 +306,7 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
                 }
                 continue;
             }
-            deq_v_unit<D, KC, VC>(u, vcodes + b0 * C::V_BLOCK_BYTES, vscales + b0 * C::V_BLOCK_SCALES,
-                                  vhat, vrows);
+            deq_v_unit<D, KC, VC>(u, rv[i], vsc, vhat, vrows);
         }
     };
 
@@ -275,11 +340,20 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
         wave_max_diag = v;  // -1 when the wave has no valid column
     }
 
+    // prologue: tile 0 dequantized, tile 1 loaded and its scales staged
+    load_tile(0);
+    stage_scales(0);
+    __syncthreads();
     dequant_tile(0, lds);
+    if (1 < ntiles) {
+        load_tile(1);
+        stage_scales(1);
+    }
     __syncthreads();
     for (int tile = 0; tile < ntiles; ++tile) {
         bfbits *cur = lds + (tile & 1) * C::BUF_ELEMS;
         if (tile + 1 < ntiles) dequant_tile(tile + 1, lds + ((tile + 1) & 1) * C::BUF_ELEMS);
+        if (tile + 2 < ntiles) load_tile(tile + 2);
         const int row0 = tile * kTileRows;
         if (row0 <= wave_max_diag) {  // some column of this wave sees rows of this tile
             const bfbits *khat = cur;
@@ -301,6 +375,8 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
                 }
             }
             const bool diag_tile = row0 + kTileRows - 1 > wave_min_diag;
+            // P^T operands: k-step ks covers row tiles 2ks, 2ks+1
+            bf8 P[C::NT][2];
 #pragma unroll
             for (int nt = 0; nt < C::NT; ++nt) {
                 if (diag_tile) {
@@ -327,31 +403,34 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
                     for (int cb = 0; cb < C::CB; ++cb) O[nt][cb] *= alpha;
                     m_run[nt] = m_new;
                 }
-                // P^T operands: k-step ks covers row tiles 2ks, 2ks+1
-                bf8 P[2];
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const float p = fast_exp2(S[nt][mt][r] - m_run[nt]);  // 0 when masked
                         l_run[nt] += p;
-                        P[mt >> 1][4 * (mt & 1) + r] = (__bf16)p;
+                        P[nt][mt >> 1][4 * (mt & 1) + r] = (__bf16)p;
                     }
-                // ---- O^T += V_hat^T P^T
+            }
+            // ---- O^T += V_hat^T P^T; each V_hat operand read serves every
+            // column tile of the wave
 #pragma unroll
-                for (int cb = 0; cb < C::CB; ++cb) {
+            for (int cb = 0; cb < C::CB; ++cb) {
 #pragma unroll
-                    for (int ks = 0; ks < 2; ++ks) {
-                        const bfbits *vp = vhat + (16 * cb + h16) * C::VS + 32 * ks + 4 * q4;
-                        const u2 lo = *reinterpret_cast<const u2 *>(vp);
-                        const u2 hi = *reinterpret_cast<const u2 *>(vp + 16);
-                        const u4 vv = {lo.x, lo.y, hi.x, hi.y};
-                        O[nt][cb] = mfma16x16x32_bf16(__builtin_bit_cast(bf8, vv), P[ks], O[nt][cb]);
-                    }
+                for (int ks = 0; ks < 2; ++ks) {
+                    const bfbits *vp = vhat + (16 * cb + h16) * C::VS + 32 * ks + 4 * q4;
+                    const u2 lo = *reinterpret_cast<const u2 *>(vp);
+                    const u2 hi = *reinterpret_cast<const u2 *>(vp + 16);
+                    const bf8 vop = __builtin_bit_cast(bf8, u4{lo.x, lo.y, hi.x, hi.y});
+#pragma unroll
+                    for (int nt = 0; nt < C::NT; ++nt) O[nt][cb] = mfma16x16x32_bf16(vop, P[nt][ks], O[nt][cb]);
                 }
             }
         }
-        __syncthreads();  // next tile's dequant done; this tile's reads done
+        // tile + 2's scales go where tile's were (read by its dequant, one
+        // iteration ago)
+        if (tile + 2 < ntiles) stage_scales(tile + 2);
+        __syncthreads();  // next tile's dequant and staging done; this tile's reads done
     }
 
     // ---- normalize and store: lane (column h16, q4) holds channels 16cb+4q4..+3
@@ -374,7 +453,7 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
 template <int D, int KC, int VC>
 hipError_t launch_ptyped(const PrefillArgs &a, hipStream_t s) {
     using C = PCfg<D, KC, VC>;
-    const size_t lds = 2 * (size_t)C::BUF_ELEMS * sizeof(bfbits);
+    const size_t lds = 2 * (size_t)C::BUF_ELEMS * sizeof(bfbits) + 2 * (size_t)C::SC_BYTES;
     if (lds > 65536) {
         hipError_t e = hipFuncSetAttribute((const void *)prefill_kernel<D, KC, VC>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
