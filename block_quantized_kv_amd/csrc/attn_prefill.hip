@@ -62,9 +62,12 @@ struct PCfg {
     static constexpr int K_UNITS = 2 * 2 * (K_LB / K_W) * 64;
     static constexpr int V_UNITS = 2 * (V_LB / V_W) * 64;
     // LDS tiles (bf16): K_hat [64][KS], V_hat^T [D][VS]; the pads keep the
-    // 16-lane groups of the operand reads on distinct banks
+    // 16-lane groups of the operand reads on distinct banks.  V_hat^T rows are
+    // read and written 8 bytes per lane: a row stride of 34 dwords (2 mod 4)
+    // measured fastest (a 36-dword stride costs 5 %, 40 dwords 25 %, an
+    // unpadded 32 three times the kernel time)
     static constexpr int KS = D + 8;
-    static constexpr int VS = kTileRows + 8;
+    static constexpr int VS = kTileRows + 4;
     static constexpr int K_TILE_ELEMS = kTileRows * KS;
     static constexpr int V_TILE_ELEMS = D * VS;
     static constexpr int BUF_ELEMS = K_TILE_ELEMS + V_TILE_ELEMS;
