@@ -50,6 +50,9 @@ def _args():
     p.add_argument("--step-only", action="store_true",
                    help="time only the headline step (no two-call step, attention-only, multi-query, "
                         "baseline, prefill, quality or CPU legs): the run that profiles and counters use")
+    p.add_argument("--prefill-only", action="store_true",
+                   help="run only the prefill leg (2048-token chunk over a 32768-row prefix) and print its JSON: "
+                        "the run that the prefill kernel's profile uses")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run plain 256 MiB device copies (HBM counter calibration)")
     p.add_argument("--write-traffic-summary", metavar="PMC_DIR",
@@ -186,6 +189,12 @@ def main():
         return
     if args.write_traffic_summary:
         write_traffic_summary(args.write_traffic_summary)
+        return
+    if args.prefill_only:
+        import torch
+        from block_quantized_kv_amd import load_library
+        load_library()
+        print(json.dumps(run_prefill(torch, torch.device("cuda:0"), args)), flush=True)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no "
