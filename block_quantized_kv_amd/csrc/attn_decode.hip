@@ -875,13 +875,23 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
     float M = -INFINITY, o = 0.0f, L = 0.0f;
     for (int s0 = sg; s0 < nsp; s0 += 4 * U) {
         float mv[U], lv[U], ov[U];
+        // every load is issued (a split past the end re-reads the last one),
+        // so all of them are in flight together behind a single wait; the
+        // surplus values are dropped afterwards
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int s2 = s0 + 4 * u;
-            const bool ok = s2 < nsp;
-            mv[u] = ok ? ml[2 * s2] : -INFINITY;
-            lv[u] = ok ? ml[2 * s2 + 1] : 0.0f;
-            ov[u] = ok ? po[(int64_t)s2 * D] : 0.0f;
+            const int s2 = s0 + 4 * u < nsp ? s0 + 4 * u : nsp - 1;
+            const float2 x = *reinterpret_cast<const float2 *>(ml + 2 * s2);
+            mv[u] = x.x;
+            lv[u] = x.y;
+            ov[u] = po[(int64_t)s2 * D];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const bool ok = s0 + 4 * u < nsp;
+            mv[u] = ok ? mv[u] : -INFINITY;
+            lv[u] = ok ? lv[u] : 0.0f;
+            ov[u] = ok ? ov[u] : 0.0f;
         }
         float mb = M;
 #pragma unroll

@@ -1,5 +1,5 @@
 // attn_prefill.hip -- chunked-prefill attention over the block-quantized cache
-// on bf16 matrix cores.  gfx950.
+// on binary16 matrix cores.  gfx950.
 //
 // What is computed (den_llama.cpp, "Results": prefill with 2048-token
 // micro-batches over a q8_0 K / q4_0 V cache; Llaminar, "Graphs and Compute
@@ -12,15 +12,24 @@
 //    token-major.  A workgroup of 8 waves owns 256 consecutive columns (16*NT
 //    per wave) of one kv-head, so every K/V tile it dequantizes serves all of
 //    them; tiles are 64 rows (two cache blocks).
-//  * Per tile, the workgroup dequantizes K and V into LDS as bf16 (code *
+//  * Per tile, the workgroup dequantizes K and V into LDS as binary16 (code *
 //    scale, rounded to nearest even once): K_hat row-major, V_hat transposed
-//    [channel][row].  The V-role block layout hands each thread the eight rows
-//    of one channel, so the transposed writes are two 8-byte runs.
-//  * Each wave computes S^T = K_hat Q^T (A = K_hat rows from LDS, B = its bf16
+//    [channel][row].  Codes become exact binary16 pairs by bit operations
+//    (1024 + n), so a pair of values costs one packed subtract and one packed
+//    multiply; the work is cut into units so that every thread dequantizes
+//    the same number of values.  The V-role block layout hands each thread
+//    the eight rows of one channel, so the transposed writes are two 8-byte
+//    runs.
+//  * The bf16 query is widened and scaled by a power of two per (token,
+//    head) column so that its largest value lies in [1, 2), then rounded to
+//    binary16 (exact for every value within 2^-14 of that maximum); the power
+//    of two is folded into the column's score scale.
+//  * Each wave computes S^T = K_hat Q^T (A = K_hat rows from LDS, B = its
 //    query columns held in registers) and O^T += V_hat^T P^T on
-//    v_mfma_f32_16x16x32_bf16.  The S^T accumulator layout is the P^T operand
+//    v_mfma_f32_16x16x32_f16.  The S^T accumulator layout is the P^T operand
 //    layout, as in the decode kernel.  Online softmax in log2 units with fp32
-//    statistics; the running max is raised only when exceeded by more than 8.
+//    statistics; the running max is raised only when exceeded by more than 8
+//    (so probabilities stay <= 256 in binary16).
 //  * Causal mask only on tiles that cross a column's diagonal; rows past the
 //    needed range get a zero V so never-written bytes cannot leak NaN.
 //  * The two LDS tile buffers alternate, so the dequant of tile k+1 overlaps
@@ -39,7 +48,9 @@ constexpr int kPThreads = 64 * kPWaves;
 constexpr int kTileRows = 64;
 constexpr float kPRescaleThreshold = 8.0f;
 
-typedef uint16_t bfbits;
+typedef uint16_t f16bits;
+
+constexpr int clamp_width(int w, int lo, int hi) { return w < lo ? lo : (w > hi ? hi : w); }
 
 template <int D, int KC, int VC>
 struct PCfg {
@@ -49,19 +60,28 @@ struct PCfg {
     static constexpr int COLS = kPWaves * 16 * NT;
     static constexpr int KG = group_size(KC);
     static constexpr int VG = group_size(VC);
+    static constexpr int VNG = D / VG;
     static constexpr int K_LB = k_lane_bytes(KC, D);
     static constexpr int V_LB = v_lane_bytes(VC, D);
-    static constexpr int K_W = chunk_width(K_LB);
-    static constexpr int V_W = chunk_width(V_LB);
+    // the cache's chunk widths, and the dequant unit widths: a unit is UW
+    // bytes of one lane's chunk, sized so that a 64-row tile has one unit per
+    // thread where the codec allows (a unit holds at least one k-step /
+    // channel block)
+    static constexpr int K_CW = chunk_width(K_LB);
+    static constexpr int V_CW = chunk_width(V_LB);
+    static constexpr int K_BPS = is8(KC) ? 8 : 4;  // code bytes per k-step per lane
+    static constexpr int V_BPC = is8(VC) ? 8 : 4;  // code bytes per channel block per lane
+    static constexpr int K_UW = clamp_width(K_LB / 2, K_BPS, K_CW);
+    static constexpr int V_UW = clamp_width(V_LB / 4, V_BPC, V_CW);
     static constexpr int K_TILE_BYTES = 16 * row_bytes(KC, D);
     static constexpr int K_BLOCK_BYTES = block_code_bytes(KC, D);
     static constexpr int V_BLOCK_BYTES = block_code_bytes(VC, D);
     static constexpr int K_BLOCK_SCALES = block_scales(KC, D);
     static constexpr int V_BLOCK_SCALES = block_scales(VC, D);
-    // dequant work units per 64-row tile (one unit = one lane chunk of W bytes)
-    static constexpr int K_UNITS = 2 * 2 * (K_LB / K_W) * 64;
-    static constexpr int V_UNITS = 2 * (V_LB / V_W) * 64;
-    // LDS tiles (bf16): K_hat [64][KS], V_hat^T [D][VS]; the pads keep the
+    // dequant units per 64-row tile
+    static constexpr int K_UNITS = 2 * 2 * (K_LB / K_UW) * 64;
+    static constexpr int V_UNITS = 2 * (V_LB / V_UW) * 64;
+    // LDS tiles (binary16): K_hat [64][KS], V_hat^T [D][VS]; the pads keep the
     // 16-lane groups of the operand reads on distinct banks.  V_hat^T rows are
     // read and written 8 bytes per lane: a row stride of 34 dwords (2 mod 4)
     // measured fastest (a 36-dword stride costs 5 %, 40 dwords 25 %, an
@@ -70,7 +90,17 @@ struct PCfg {
     static constexpr int VS = kTileRows + 4;
     static constexpr int K_TILE_ELEMS = kTileRows * KS;
     static constexpr int V_TILE_ELEMS = D * VS;
-    static constexpr int BUF_ELEMS = K_TILE_ELEMS + V_TILE_ELEMS;
+    static constexpr int KSC_BYTES_ = 2 * 2 * K_BLOCK_SCALES;
+    static constexpr int SC_BYTES_ = KSC_BYTES_ + 2 * 2 * V_BLOCK_SCALES;
+    // Two K_hat buffers; three V_hat buffers where LDS allows, so that a
+    // tile's V_hat outlives the next tile's K_hat (the two wave groups below
+    // run half a tile apart), else two
+    static constexpr int NVB =
+        (2 * K_TILE_ELEMS + 3 * V_TILE_ELEMS) * 2 + 2 * SC_BYTES_ <= 160 * 1024 ? 3 : 2;
+    static constexpr bool PINGPONG = NVB == 3;
+    static constexpr int OFF_V = 2 * K_TILE_ELEMS;               // elements
+    static constexpr int OFF_SC = OFF_V + NVB * V_TILE_ELEMS;    // elements
+    static constexpr int LDS_BYTES = OFF_SC * 2 + 2 * SC_BYTES_;
     // dequant units per thread, and a tile's scales (both blocks, K then V)
     static constexpr int UK = (K_UNITS + kPThreads - 1) / kPThreads;
     static constexpr int UV = (V_UNITS + kPThreads - 1) / kPThreads;
@@ -79,34 +109,43 @@ struct PCfg {
     static constexpr int SC_BYTES = KSC_BYTES + VSC_BYTES;
     static_assert(KSC_BYTES % 16 == 0 && VSC_BYTES % 16 == 0, "scale spans are whole 16-byte pieces");
     static_assert(SC_BYTES / 16 <= kPThreads, "one 16-byte scale piece per thread");
+    static_assert(K_UW % K_BPS == 0 && V_UW % V_BPC == 0, "units hold whole k-steps / channel blocks");
 };
 
-__device__ __forceinline__ bfbits to_bf16(float x) {
-    return __builtin_bit_cast(bfbits, (__bf16)x);  // round to nearest even
+// Unit u of a tile's K codes: lane L, chunk c, sub-unit `sub` of tile tau of
+// block blk.
+struct KUnit {
+    int L, sub, c, tau, blk;
+};
+template <int D, int KC, int VC>
+__device__ __forceinline__ KUnit k_unit(int u) {
+    using C = PCfg<D, KC, VC>;
+    constexpr int SUB = C::K_CW / C::K_UW, CH = C::K_LB / C::K_CW;
+    const int x = u >> 6;
+    return KUnit{u & 63, x % SUB, x / SUB % CH, x / SUB / CH % 2, x / SUB / CH / 2};
 }
-
-// Signed code of the element in nibble position p of a 4-bit word.
-template <int CODEC>
-__device__ __forceinline__ int nibble_code(uint32_t w, int p) {
-    if constexpr (CODEC == Q4_0) return (int)((w >> (4 * p)) & 0xFu) - 8;
-    else return ((int)(w << (28 - 4 * p))) >> 28;  // sign-extend the two's complement nibble
-}
-
-// Byte offset, within the tile's two K blocks, of K dequant unit u (lane L's
-// W-byte chunk c of tile tau of block blk).
+// Byte offset of K unit u within the tile's two K blocks.
 template <int D, int KC, int VC>
 __device__ __forceinline__ int k_unit_offset(int u) {
     using C = PCfg<D, KC, VC>;
-    constexpr int CH = C::K_LB / C::K_W;
-    const int L = u & 63, c = (u >> 6) % CH, tau = (u >> 6) / CH % 2, blk = (u >> 6) / CH / 2;
-    return blk * C::K_BLOCK_BYTES + tau * C::K_TILE_BYTES + c * 64 * C::K_W + L * C::K_W;
+    const KUnit k = k_unit<D, KC, VC>(u);
+    return k.blk * C::K_BLOCK_BYTES + k.tau * C::K_TILE_BYTES + k.c * 64 * C::K_CW + k.L * C::K_CW + k.sub * C::K_UW;
+}
+struct VUnit {
+    int L, sub, c, blk;
+};
+template <int D, int KC, int VC>
+__device__ __forceinline__ VUnit v_unit(int u) {
+    using C = PCfg<D, KC, VC>;
+    constexpr int SUB = C::V_CW / C::V_UW, CH = C::V_LB / C::V_CW;
+    const int x = u >> 6;
+    return VUnit{u & 63, x % SUB, x / SUB % CH, x / SUB / CH};
 }
 template <int D, int KC, int VC>
 __device__ __forceinline__ int v_unit_offset(int u) {
     using C = PCfg<D, KC, VC>;
-    constexpr int CH = C::V_LB / C::V_W;
-    const int L = u & 63, c = (u >> 6) % CH, blk = (u >> 6) / CH;
-    return blk * C::V_BLOCK_BYTES + c * 64 * C::V_W + L * C::V_W;
+    const VUnit v = v_unit<D, KC, VC>(u);
+    return v.blk * C::V_BLOCK_BYTES + v.c * 64 * C::V_CW + v.L * C::V_CW + v.sub * C::V_UW;
 }
 
 // Loads the W bytes at src into words (W = 4, 8 or 16).
@@ -123,77 +162,67 @@ __device__ __forceinline__ void load_chunk(uint32_t (&w)[W / 4], const uint8_t *
     }
 }
 
-// Dequantize K unit u from its code words w into K_hat rows; ksc: the tile's
-// K scales (both blocks) in LDS.
+// Dequantize K unit u from its code words w into K_hat rows; ksc0: the tile's
+// K scales (both blocks) in LDS.  Every slot of a k-step shares one scale.
 template <int D, int KC, int VC>
-__device__ __forceinline__ void deq_k_unit(int u, const uint32_t (&w)[PCfg<D, KC, VC>::K_W / 4],
-                                           const uint16_t *ksc0, bfbits *khat) {
+__device__ __forceinline__ void deq_k_unit(int u, const uint32_t (&w)[PCfg<D, KC, VC>::K_UW / 4],
+                                           const uint16_t *ksc0, f16bits *khat) {
     using C = PCfg<D, KC, VC>;
-    constexpr int CH = C::K_LB / C::K_W;
-    const int L = u & 63;
-    const int c = (u >> 6) % CH;
-    const int tau = (u >> 6) / CH % 2;
-    const int blk = (u >> 6) / CH / 2;
-    const uint16_t *ksc = ksc0 + blk * C::K_BLOCK_SCALES;
-    const int i = L & 15, kq = L >> 4;
-    const int j = tau * 16 + i;        // row in block
-    const int row = blk * 32 + j;      // row in tile
-    constexpr int STEPS = is8(KC) ? C::K_W / 8 : C::K_W / 4;  // k-steps in this chunk
+    constexpr int STEPS = C::K_UW / C::K_BPS;  // k-steps in this unit
+    const KUnit k = k_unit<D, KC, VC>(u);
+    const uint16_t *ksc = ksc0 + k.blk * C::K_BLOCK_SCALES;
+    const int i = k.L & 15, kq = k.L >> 4;
+    const int j = k.tau * 16 + i;      // row in block
+    const int row = k.blk * 32 + j;    // row in tile
+    const int t0 = (k.c * C::K_CW + k.sub * C::K_UW) / C::K_BPS;
 #pragma unroll
     for (int st = 0; st < STEPS; ++st) {
-        const int t = c * STEPS + st;
+        const int t = t0 + st;
         const int g = (32 * t) / C::KG;
-        const float dq = (float)__builtin_bit_cast(_Float16, ksc[k_scale_index(KC, D, j, g)]);
-        bfbits o[8];
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            int code;
-            if constexpr (is8(KC)) code = (int)(int8_t)((w[2 * st + (s >> 2)] >> (8 * (s & 3))) & 0xFFu);
-            else code = nibble_code<KC>(w[st], slot_nibble(s));
-            o[s] = to_bf16((float)code * dq);
-        }
-        u4 pk;
-        pk.x = o[0] | ((uint32_t)o[1] << 16);
-        pk.y = o[2] | ((uint32_t)o[3] << 16);
-        pk.z = o[4] | ((uint32_t)o[5] << 16);
-        pk.w = o[6] | ((uint32_t)o[7] << 16);
-        *reinterpret_cast<u4 *>(khat + row * C::KS + 32 * t + 8 * kq) = pk;
+        const _Float16 dq = __builtin_bit_cast(_Float16, ksc[k_scale_index(KC, D, j, g)]);
+        const h2 dq4[4] = {h2{dq, dq}, h2{dq, dq}, h2{dq, dq}, h2{dq, dq}};
+        const h8 x = v_operand<KC>(&w[is8(KC) ? 2 * st : st], reinterpret_cast<const h2_alias *>(dq4));
+        *reinterpret_cast<u4 *>(khat + row * C::KS + 32 * t + 8 * kq) = __builtin_bit_cast(u4, x);
     }
 }
 
 // Dequantize V unit u from its code words into V_hat^T [channel][row]; vsc0:
-// the tile's V scales (both blocks) in LDS; rows at or past `vrows`
-// (tile-relative) are written as zero.
+// the tile's V scales (both blocks) in LDS.  With `tail`, rows at or past
+// `vrows` (tile-relative) get a zero scale, so bytes that were never written
+// cannot turn into NaN.
 template <int D, int KC, int VC>
-__device__ __forceinline__ void deq_v_unit(int u, const uint32_t (&w)[PCfg<D, KC, VC>::V_W / 4],
-                                           const uint16_t *vsc0, bfbits *vhat, int vrows) {
+__device__ __forceinline__ void deq_v_unit(int u, const uint32_t (&w)[PCfg<D, KC, VC>::V_UW / 4],
+                                           const uint16_t *vsc0, f16bits *vhat, bool tail, int vrows) {
     using C = PCfg<D, KC, VC>;
-    constexpr int CH = C::V_LB / C::V_W;
-    const int L = u & 63;
-    const int c = (u >> 6) % CH;
-    const int blk = (u >> 6) / CH;
-    const uint16_t *vsc = vsc0 + blk * C::V_BLOCK_SCALES;
-    const int c16 = L & 15, kq = L >> 4;
-    constexpr int CBS = is8(VC) ? C::V_W / 8 : C::V_W / 4;  // channel blocks in this chunk
+    constexpr int CBS = C::V_UW / C::V_BPC;  // channel blocks in this unit
+    const VUnit v = v_unit<D, KC, VC>(u);
+    const int c16 = v.L & 15, kq = v.L >> 4;
+    const int cb0 = (v.c * C::V_CW + v.sub * C::V_UW) / C::V_BPC;
+    // this lane's scale words: [group][pair m] holds slots (2m, 2m+1), i.e.
+    // rows (m/2)*16 + 4kq + 2(m%2) + {0, 1} of the block
+    const uint32_t *vsw = reinterpret_cast<const uint32_t *>(vsc0 + v.blk * C::V_BLOCK_SCALES + kq * 8 * C::VNG);
 #pragma unroll
     for (int k = 0; k < CBS; ++k) {
-        const int cb = c * CBS + k;
+        const int cb = cb0 + k;
         const int ch = 16 * cb + c16;
         const int g = (16 * cb) / C::VG;
-        bfbits o[8];
+        uint32_t s4[4];
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            const int j = (s >> 2) * 16 + 4 * kq + (s & 3);  // row in block
-            const float dq = (float)__builtin_bit_cast(_Float16, vsc[v_scale_index(VC, D, j, g)]);
-            int code;
-            if constexpr (is8(VC)) code = (int)(int8_t)((w[2 * k + (s >> 2)] >> (8 * (s & 3))) & 0xFFu);
-            else code = nibble_code<VC>(w[k], slot_nibble(s));
-            o[s] = blk * 32 + j < vrows ? to_bf16((float)code * dq) : (bfbits)0;
+        for (int m = 0; m < 4; ++m) s4[m] = vsw[g * 4 + m];
+        if (tail) {
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const int j0 = v.blk * 32 + (m >> 1) * 16 + 4 * kq + 2 * (m & 1);
+                if (j0 >= vrows) s4[m] &= 0xFFFF0000u;
+                if (j0 + 1 >= vrows) s4[m] &= 0x0000FFFFu;
+            }
         }
+        const h8 x = v_operand<VC>(&w[is8(VC) ? 2 * k : k], reinterpret_cast<const h2_alias *>(s4));
+        const u4 b = __builtin_bit_cast(u4, x);
         // slots 0..3 are rows 4kq..4kq+3, slots 4..7 rows 16+4kq..16+4kq+3
-        bfbits *dst = vhat + ch * C::VS + blk * 32 + 4 * kq;
-        *reinterpret_cast<u2 *>(dst) = u2{o[0] | ((uint32_t)o[1] << 16), o[2] | ((uint32_t)o[3] << 16)};
-        *reinterpret_cast<u2 *>(dst + 16) = u2{o[4] | ((uint32_t)o[5] << 16), o[6] | ((uint32_t)o[7] << 16)};
+        f16bits *dst = vhat + ch * C::VS + v.blk * 32 + 4 * kq;
+        *reinterpret_cast<u2 *>(dst) = u2{b.x, b.y};
+        *reinterpret_cast<u2 *>(dst + 16) = u2{b.z, b.w};
     }
 }
 
@@ -201,7 +230,7 @@ template <int D, int KC, int VC>
 __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
     using C = PCfg<D, KC, VC>;
     extern __shared__ __align__(16) unsigned char smem[];
-    bfbits *lds = reinterpret_cast<bfbits *>(smem);
+    f16bits *lds = reinterpret_cast<f16bits *>(smem);
 
     const int G = a.gqa;
     const int kvh = blockIdx.y;
@@ -215,9 +244,12 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
     const int64_t nrows = a.pos0 + last_col / G + 1;
     const int ntiles = (int)((nrows + kTileRows - 1) / kTileRows);
 
-    // ---- this wave's bf16 query columns (B operand of S^T), zero past the end
-    bf8 qop[C::NT][C::KSTEPS];
-    int diag[C::NT];  // absolute position of this lane's column (its last visible row)
+    // ---- this wave's query columns (B operand of S^T), zero past the end:
+    // bf16 widened exactly, scaled by 2^-e so the column's largest value lies
+    // in [1, 2), rounded to binary16; 2^e goes into the column's score scale
+    h8 qop[C::NT][C::KSTEPS];
+    int diag[C::NT];       // absolute position of this lane's column (its last visible row)
+    float cscale[C::NT];   // score scale of this lane's column (log2 units)
 #pragma unroll
     for (int nt = 0; nt < C::NT; ++nt) {
         const int col = col0 + (wave * C::NT + nt) * 16 + h16;
@@ -225,11 +257,29 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
         const int t = ok ? col / G : 0, hh = ok ? col % G : 0;
         diag[nt] = ok ? (int)(a.pos0 + t) : -1;
         const uint16_t *qp = a.q + ((int64_t)t * a.n_q_heads + (int64_t)kvh * G + hh) * D;
+        u4 raw[C::KSTEPS];
+        float mx = 0.0f;
 #pragma unroll
         for (int ks = 0; ks < C::KSTEPS; ++ks) {
-            u4 v = ok ? *reinterpret_cast<const u4 *>(qp + 32 * ks + 8 * q4) : u4{0u, 0u, 0u, 0u};
-            qop[nt][ks] = __builtin_bit_cast(bf8, v);
+            raw[ks] = ok ? *reinterpret_cast<const u4 *>(qp + 32 * ks + 8 * q4) : u4{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int s2 = 0; s2 < 8; ++s2) {
+                const uint32_t wd = raw[ks][s2 >> 1];
+                mx = fmaxf(mx, fabsf(__builtin_bit_cast(float, (s2 & 1) ? (wd & 0xFFFF0000u) : (wd << 16))));
+            }
         }
+        mx = fmaxf(mx, shfl_xor(mx, 16));
+        mx = fmaxf(mx, shfl_xor(mx, 32));
+        const int e = mx > 0.0f ? ilogbf(mx) : 0;
+        const float nrm = ldexpf(1.0f, -e);
+        cscale[nt] = a.scale_log2 * ldexpf(1.0f, e);
+#pragma unroll
+        for (int ks = 0; ks < C::KSTEPS; ++ks)
+#pragma unroll
+            for (int s2 = 0; s2 < 8; ++s2) {
+                const uint32_t wd = raw[ks][s2 >> 1];
+                qop[nt][ks][s2] = (_Float16)(__builtin_bit_cast(float, (s2 & 1) ? (wd & 0xFFFF0000u) : (wd << 16)) * nrm);
+            }
     }
 
     const int64_t head_lin = (int64_t)a.seq * a.k.n_kv_heads + kvh;
@@ -243,9 +293,9 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
     // scales staged in LDS one iteration before it is dequantized, which is
     // one iteration before its products, so neither the global loads nor the
     // dequant wait in line with the matrix products.
-    uint32_t rk[C::UK][C::K_W / 4], rv[C::UV][C::V_W / 4];
+    uint32_t rk[C::UK][C::K_UW / 4], rv[C::UV][C::V_UW / 4];
     u4 rsc = u4{0u, 0u, 0u, 0u};
-    uint16_t *sc_lds = reinterpret_cast<uint16_t *>(lds + 2 * C::BUF_ELEMS);  // [2][SC_BYTES / 2]
+    uint16_t *sc_lds = reinterpret_cast<uint16_t *>(lds + C::OFF_SC);  // [2][SC_BYTES / 2]
     auto load_tile = [&](int tile) {
         const int64_t b0 = (int64_t)tile * 2;  // first block of the tile
         const bool two = b0 + 1 < nblocks_plane;  // the second block exists
@@ -254,12 +304,12 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int i = 0; i < C::UK; ++i) {
             const int u = tid + i * kPThreads;
-            if (u < C::K_UNITS && (two || u < C::K_UNITS / 2)) load_chunk<C::K_W>(rk[i], kb + k_unit_offset<D, KC, VC>(u));
+            if (u < C::K_UNITS && (two || u < C::K_UNITS / 2)) load_chunk<C::K_UW>(rk[i], kb + k_unit_offset<D, KC, VC>(u));
         }
 #pragma unroll
         for (int i = 0; i < C::UV; ++i) {
             const int u = tid + i * kPThreads;
-            if (u < C::V_UNITS && (two || u < C::V_UNITS / 2)) load_chunk<C::V_W>(rv[i], vb + v_unit_offset<D, KC, VC>(u));
+            if (u < C::V_UNITS && (two || u < C::V_UNITS / 2)) load_chunk<C::V_UW>(rv[i], vb + v_unit_offset<D, KC, VC>(u));
         }
         // the tile's scales, 16 bytes per thread: K (both blocks) then V
         const int o = tid * 16;
@@ -277,14 +327,12 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
             *reinterpret_cast<u4 *>(reinterpret_cast<uint8_t *>(sc_lds + (tile & 1) * (C::SC_BYTES / 2)) + tid * 16) = rsc;
     };
     // dequantizes the tile whose codes are in rk/rv and whose scales are staged
-    auto dequant_tile = [&](int tile, bfbits *buf) {
+    auto dequant_tile = [&](int tile, f16bits *khat, f16bits *vhat) {
         const int64_t b0 = (int64_t)tile * 2;
         const int vrows = (int)min((int64_t)kTileRows, nrows - (int64_t)tile * kTileRows);
         const bool two = b0 + 1 < nblocks_plane;
         const uint16_t *ksc = sc_lds + (tile & 1) * (C::SC_BYTES / 2);
         const uint16_t *vsc = ksc + C::KSC_BYTES / 2;
-        bfbits *khat = buf;
-        bfbits *vhat = buf + C::K_TILE_ELEMS;
 #pragma unroll
         for (int i = 0; i < C::UK; ++i) {
             const int u = tid + i * kPThreads;
@@ -297,19 +345,19 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
             if (u >= C::V_UNITS) continue;
             if (!two && u >= C::V_UNITS / 2) {
                 // absent block: zero its V columns so masked products stay 0
-                const int L = u & 63, c16 = L & 15, kq = L >> 4;
-                constexpr int CH = C::V_LB / C::V_W;
-                constexpr int CBS = is8(VC) ? C::V_W / 8 : C::V_W / 4;
-                const int c = (u >> 6) % CH;
+                const VUnit vu = v_unit<D, KC, VC>(u);
+                const int c16 = vu.L & 15, kq = vu.L >> 4;
+                constexpr int CBS = C::V_UW / C::V_BPC;
+                const int cb0 = (vu.c * C::V_CW + vu.sub * C::V_UW) / C::V_BPC;
 #pragma unroll
                 for (int k = 0; k < CBS; ++k) {
-                    bfbits *dst = vhat + (16 * (c * CBS + k) + c16) * C::VS + 32 + 4 * kq;
+                    f16bits *dst = vhat + (16 * (cb0 + k) + c16) * C::VS + 32 + 4 * kq;
                     *reinterpret_cast<u2 *>(dst) = u2{0u, 0u};
                     *reinterpret_cast<u2 *>(dst + 16) = u2{0u, 0u};
                 }
                 continue;
             }
-            deq_v_unit<D, KC, VC>(u, rv[i], vsc, vhat, vrows);
+            deq_v_unit<D, KC, VC>(u, rv[i], vsc, vhat, vrows < kTileRows, vrows);
         }
     };
 
@@ -343,91 +391,133 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
         wave_max_diag = v;  // -1 when the wave has no valid column
     }
 
+    auto kbuf = [&](int tile) { return lds + (tile & 1) * C::K_TILE_ELEMS; };
+    auto vbuf = [&](int tile) { return lds + C::OFF_V + (tile % C::NVB) * C::V_TILE_ELEMS; };
+
+    // ---- S^T = K_hat Q^T for one tile: 4 row tiles x NT column tiles
+    f4 S[C::NT][4];
+    auto scores = [&](int tile) {
+        const f16bits *khat = kbuf(tile);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+            h8 kop[C::KSTEPS];
+#pragma unroll
+            for (int ks = 0; ks < C::KSTEPS; ++ks)
+                kop[ks] = *reinterpret_cast<const h8 *>(khat + (16 * mt + h16) * C::KS + 32 * ks + 8 * q4);
+#pragma unroll
+            for (int nt = 0; nt < C::NT; ++nt) {
+                f4 acc = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < C::KSTEPS; ++ks) acc = mfma16x16x32(kop[ks], qop[nt][ks], acc);
+                S[nt][mt] = acc * cscale[nt];
+            }
+        }
+    };
+    // ---- masking and the online-softmax update of one tile's scores; the
+    // probabilities become the P^T operands (k-step ks covers row tiles
+    // 2ks, 2ks+1)
+    h8 P[C::NT][2];
+    auto softmax = [&](int tile) {
+        const int row0 = tile * kTileRows;
+        const bool diag_tile = row0 + kTileRows - 1 > wave_min_diag;
+#pragma unroll
+        for (int nt = 0; nt < C::NT; ++nt) {
+            if (diag_tile) {
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (row0 + 16 * mt + 4 * q4 + r > diag[nt]) S[nt][mt][r] = -INFINITY;
+            }
+            float mx = -INFINITY;
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) mx = fmaxf(mx, S[nt][mt][r]);
+            mx = fmaxf(mx, shfl_xor(mx, 16));
+            mx = fmaxf(mx, shfl_xor(mx, 32));
+            // a column with every row of this tile masked keeps its state
+            const bool raise = mx > m_run[nt] + kPRescaleThreshold;
+            if (__any(raise)) {
+                const float m_new = raise ? mx : m_run[nt];
+                const float alpha = raise ? fast_exp2(m_run[nt] - m_new) : 1.0f;
+                l_run[nt] *= alpha;
+#pragma unroll
+                for (int cb = 0; cb < C::CB; ++cb) O[nt][cb] *= alpha;
+                m_run[nt] = m_new;
+            }
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float p = fast_exp2(S[nt][mt][r] - m_run[nt]);  // 0 when masked
+                    l_run[nt] += p;
+                    P[nt][mt >> 1][4 * (mt & 1) + r] = (_Float16)p;
+                }
+        }
+    };
+    // ---- O^T += V_hat^T P^T; each V_hat operand read serves every column
+    // tile of the wave
+    auto pv = [&](int tile) {
+        const f16bits *vhat = vbuf(tile);
+#pragma unroll
+        for (int cb = 0; cb < C::CB; ++cb) {
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                const f16bits *vp = vhat + (16 * cb + h16) * C::VS + 32 * ks + 4 * q4;
+                const u2 lo = *reinterpret_cast<const u2 *>(vp);
+                const u2 hi = *reinterpret_cast<const u2 *>(vp + 16);
+                const h8 vop = __builtin_bit_cast(h8, u4{lo.x, lo.y, hi.x, hi.y});
+#pragma unroll
+                for (int nt = 0; nt < C::NT; ++nt) O[nt][cb] = mfma16x16x32(vop, P[nt][ks], O[nt][cb]);
+            }
+        }
+    };
+
     // prologue: tile 0 dequantized, tile 1 loaded and its scales staged
     load_tile(0);
     stage_scales(0);
     __syncthreads();
-    dequant_tile(0, lds);
+    dequant_tile(0, kbuf(0), vbuf(0));
     if (1 < ntiles) {
         load_tile(1);
         stage_scales(1);
     }
     __syncthreads();
+    // Each tile passes through S (matrix cores), softmax (vector ALU) and PV
+    // (matrix cores).  Waves 0-3 run S(k), PV(k-1), softmax(k) between the
+    // barriers of iteration k; waves 4-7 (the other wave of each SIMD) run
+    // softmax(k-1), S(k), PV(k-1): the two waves of a SIMD then use the matrix
+    // cores and the vector ALU at the same time instead of in lockstep.  A
+    // tile's V_hat is therefore read one iteration after its K_hat (three
+    // V_hat buffers).  Without room for three, every wave runs S(k),
+    // softmax(k), PV(k).
+    const bool late = C::PINGPONG && wave >= kPWaves / 2;
+    bool have_s = false;  // S holds the scores of tile - 1 (late waves)
+    bool have_p = false;  // P holds the probabilities of tile - 1
     for (int tile = 0; tile < ntiles; ++tile) {
-        bfbits *cur = lds + (tile & 1) * C::BUF_ELEMS;
-        if (tile + 1 < ntiles) dequant_tile(tile + 1, lds + ((tile + 1) & 1) * C::BUF_ELEMS);
+        if (tile + 1 < ntiles) dequant_tile(tile + 1, kbuf(tile + 1), vbuf(tile + 1));
         if (tile + 2 < ntiles) load_tile(tile + 2);
-        const int row0 = tile * kTileRows;
-        if (row0 <= wave_max_diag) {  // some column of this wave sees rows of this tile
-            const bfbits *khat = cur;
-            const bfbits *vhat = cur + C::K_TILE_ELEMS;
-            // ---- S^T: 4 row tiles x NT column tiles
-            f4 S[C::NT][4];
-#pragma unroll
-            for (int mt = 0; mt < 4; ++mt) {
-                bf8 kop[C::KSTEPS];
-#pragma unroll
-                for (int ks = 0; ks < C::KSTEPS; ++ks)
-                    kop[ks] = *reinterpret_cast<const bf8 *>(khat + (16 * mt + h16) * C::KS + 32 * ks + 8 * q4);
-#pragma unroll
-                for (int nt = 0; nt < C::NT; ++nt) {
-                    f4 acc = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int ks = 0; ks < C::KSTEPS; ++ks) acc = mfma16x16x32_bf16(kop[ks], qop[nt][ks], acc);
-                    S[nt][mt] = acc * a.scale_log2;
-                }
-            }
-            const bool diag_tile = row0 + kTileRows - 1 > wave_min_diag;
-            // P^T operands: k-step ks covers row tiles 2ks, 2ks+1
-            bf8 P[C::NT][2];
-#pragma unroll
-            for (int nt = 0; nt < C::NT; ++nt) {
-                if (diag_tile) {
-#pragma unroll
-                    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            if (row0 + 16 * mt + 4 * q4 + r > diag[nt]) S[nt][mt][r] = -INFINITY;
-                }
-                float mx = -INFINITY;
-#pragma unroll
-                for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) mx = fmaxf(mx, S[nt][mt][r]);
-                mx = fmaxf(mx, shfl_xor(mx, 16));
-                mx = fmaxf(mx, shfl_xor(mx, 32));
-                // a column with every row of this tile masked keeps its state
-                const bool raise = mx > m_run[nt] + kPRescaleThreshold;
-                if (__any(raise)) {
-                    const float m_new = raise ? mx : m_run[nt];
-                    const float alpha = raise ? fast_exp2(m_run[nt] - m_new) : 1.0f;
-                    l_run[nt] *= alpha;
-#pragma unroll
-                    for (int cb = 0; cb < C::CB; ++cb) O[nt][cb] *= alpha;
-                    m_run[nt] = m_new;
-                }
-#pragma unroll
-                for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const float p = fast_exp2(S[nt][mt][r] - m_run[nt]);  // 0 when masked
-                        l_run[nt] += p;
-                        P[nt][mt >> 1][4 * (mt & 1) + r] = (__bf16)p;
-                    }
-            }
-            // ---- O^T += V_hat^T P^T; each V_hat operand read serves every
-            // column tile of the wave
-#pragma unroll
-            for (int cb = 0; cb < C::CB; ++cb) {
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    const bfbits *vp = vhat + (16 * cb + h16) * C::VS + 32 * ks + 4 * q4;
-                    const u2 lo = *reinterpret_cast<const u2 *>(vp);
-                    const u2 hi = *reinterpret_cast<const u2 *>(vp + 16);
-                    const bf8 vop = __builtin_bit_cast(bf8, u4{lo.x, lo.y, hi.x, hi.y});
-#pragma unroll
-                    for (int nt = 0; nt < C::NT; ++nt) O[nt][cb] = mfma16x16x32_bf16(vop, P[nt][ks], O[nt][cb]);
-                }
+        if (late && have_s) {
+            softmax(tile - 1);
+            have_s = false;
+            have_p = true;
+        }
+        // some column of this wave sees rows of this tile (false from some
+        // tile on, for every later one)
+        const bool act = tile * kTileRows <= wave_max_diag;
+        if (act) scores(tile);
+        if (have_p) {
+            pv(tile - 1);
+            have_p = false;
+        }
+        if (act) {
+            if (late) {
+                have_s = true;
+            } else {
+                softmax(tile);
+                if constexpr (C::PINGPONG) have_p = true;
+                else pv(tile);
             }
         }
         // tile + 2's scales go where tile's were (read by its dequant, one
@@ -435,6 +525,11 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
         if (tile + 2 < ntiles) stage_scales(tile + 2);
         __syncthreads();  // next tile's dequant and staging done; this tile's reads done
     }
+    if (have_s) {
+        softmax(ntiles - 1);
+        have_p = true;
+    }
+    if (have_p) pv(ntiles - 1);
 
     // ---- normalize and store: lane (column h16, q4) holds channels 16cb+4q4..+3
 #pragma unroll
@@ -456,7 +551,7 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
 template <int D, int KC, int VC>
 hipError_t launch_ptyped(const PrefillArgs &a, hipStream_t s) {
     using C = PCfg<D, KC, VC>;
-    const size_t lds = 2 * (size_t)C::BUF_ELEMS * sizeof(bfbits) + 2 * (size_t)C::SC_BYTES;
+    const size_t lds = (size_t)C::LDS_BYTES;
     if (lds > 65536) {
         hipError_t e = hipFuncSetAttribute((const void *)prefill_kernel<D, KC, VC>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
