@@ -273,8 +273,12 @@ size_t kvq_prefill_workspace_bytes(const kvq_layer *L, int32_t n_q_heads, int32_
  * attends rows [0, pos0 + t] (causal, itself included).
  *   q_bf16 : bfloat16 bit patterns [n_tokens][n_q_heads][head_dim], device
  *   out    : fp32 [n_tokens][n_q_heads][head_dim], device
- * The dequantized K and V tiles are rounded to bfloat16 for the bf16 matrix
- * cores, as are the probabilities; accumulation and softmax are fp32. */
+ * The dequantized K and V tiles (code * scale) and the probabilities are
+ * rounded once to binary16 for the matrix cores; each (token, head) query
+ * column is scaled by a power of two (largest value in [1, 2)) before its
+ * binary16 rounding, so any bfloat16 magnitude is accepted; accumulation and
+ * softmax are fp32.  K and V values must lie within the binary16 range
+ * (|x| <= 65504). */
 kvq_status kvq_attend_prefill(const kvq_layer *L, const uint16_t *q_bf16, int32_t seq, int64_t pos0,
                               int32_t n_tokens, int32_t n_q_heads, float softmax_scale, float *out,
                               void *workspace, size_t ws_bytes, void *hip_stream);

@@ -2,10 +2,11 @@
 the oracle's own quantization of the same rows; bf16 queries widened exactly).
 
 Bar: max|gpu - oracle| / max|oracle| <= 1e-2, the prefill tolerance of the
-workload statement (the matrix cores see K_hat, V_hat and P rounded to bf16).
+workload statement (the matrix cores see K_hat, V_hat, the scaled query and P
+rounded to binary16).
 Covered: the tiny prefill enumerated in full, ragged prefix/chunk lengths,
 every codec pair, head_dim 64/128/256, several GQA ratios, a chunk at
-position 0, and the 2048-token chunk over a 32768-token prefix on 256
+position 0, queries far outside the binary16 range, and the 2048-token chunk over a 32768-token prefix on 256
 sampled (token, head) rows including the first and last 64 tokens.
 """
 import numpy as np
@@ -22,22 +23,25 @@ TOL = 1e-2
 CODECS = ["q8_0", "q4_0", "q4_g64"]
 
 
-def _run(gpu, kc, vc, d, hq, hkv, P, T, seed=0, sample=None, cap_extra=0):
+def _run(gpu, kc, vc, d, hq, hkv, P, T, seed=0, sample=None, cap_extra=0, qmul=1.0):
     q, k, v = workloads.prefill_inputs(gpu, seed_layer=seed, prefix=P, chunk=T, n_q_heads=hq,
                                        n_kv_heads=hkv, head_dim=d)
+    if qmul != 1.0:  # a power of two: exact in bf16
+        q = (q.float() * qmul).to(torch.bfloat16)
     cap = (P + T + 31) // 32 * 32 + cap_extra
     layer = Layer.create(kc, vc, d, hkv, 1, cap, device=gpu)
     append_rows(layer, k, v, 0, 0)                      # prefix and chunk rows
-    out = kvq_attend_prefill(layer, q, 0, P, 1.0 / np.sqrt(d)).cpu().numpy()
+    scale = 1.0 / np.sqrt(d) / qmul
+    out = kvq_attend_prefill(layer, q, 0, P, scale).cpu().numpy()
     kh = oracle.quant_dequant(kc, k.cpu().numpy().transpose(1, 0, 2).copy())
     vh = oracle.quant_dequant(vc, v.cpu().numpy().transpose(1, 0, 2).copy())
     qn = q.float().cpu().numpy()
     if sample is None:
-        ref = oracle.attend_prefill(qn, kh, vh, P, 1.0 / np.sqrt(d))
+        ref = oracle.attend_prefill(qn, kh, vh, P, scale)
         got = out
     else:
         toks, heads = sample
-        ref = oracle.attend_prefill(qn, kh, vh, P, 1.0 / np.sqrt(d), tokens=toks, heads=heads)
+        ref = oracle.attend_prefill(qn, kh, vh, P, scale, tokens=toks, heads=heads)
         got = out[toks, heads]
     err = rel_err(got, ref)
     assert np.isfinite(out).all()
@@ -64,6 +68,14 @@ def test_ragged_lengths(gpu, P, T):
 @pytest.mark.parametrize("gqa", [1, 3, 4, 16])
 def test_gqa_ratios(gpu, gqa):
     _run(gpu, "q8_0", "q4_0", 64, 2 * gqa, 2, 90, 50, seed=gqa)
+
+
+@pytest.mark.parametrize("qmul", [2.0 ** -30, 2.0 ** 40])
+def test_query_outside_binary16_range(gpu, qmul):
+    # bf16 queries far below and above the binary16 range: each (token, head)
+    # column is scaled by a power of two before the binary16 rounding, and the
+    # softmax scale divided by qmul makes the exact result the unscaled one
+    _run(gpu, "q8_0", "q4_g64", 128, 8, 2, 70, 45, seed=11, qmul=qmul)
 
 
 def test_capacity_slack_rows_ignored(gpu):
