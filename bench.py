@@ -391,6 +391,8 @@ def main():
         run_multi_query(torch, dev, cfg, caches, k_new2, v_new2, seq_len, nb, args, stream, result)
         result["paged"] = run_paged(torch, dev, cfg, base, k_new, v_new, q, seq_len, nb, args)
         result["long_context"] = run_long_context(torch, dev, args)
+        result["decode_32k"] = run_decode_config(torch, dev, args, 2, rotate=20)
+        result["batched_decode"] = run_decode_config(torch, dev, args, 5, rotate=1)
     if speak is not None:
         result["stream_read_peak"] = speak
     if not args.no_baselines:
@@ -485,6 +487,65 @@ def run_long_context(torch, dev, args) -> dict:
             "ms_per_step": round(ms, 5), "kv_bytes_per_step": total,
             "value": round(total / (ms * 1e-3) / 1e9, 2), "unit": "GB/s",
             "step": "4 x kvq_attend_decode (one per layer), HIP-graph replay"}
+
+
+def run_decode_config(torch, dev, args, cid: int, rotate: int) -> dict:
+    """Attention-only decode of a workload configuration over all of its
+    sequences: one kvq_attend_decode call per step, timed as HIP-graph replays
+    that rotate over `rotate` independent caches (so the 256 MB MALL cannot
+    serve a call's K/V).  Algorithmic bytes: the quantized K and V of every
+    attended row, once per kv-head."""
+    import workloads
+    from block_quantized_kv_amd import Layer, decode_workspace, kvq_append, kvq_attend_decode
+    cfg = workloads.CONFIGS[cid]
+    (kc, vc), = cfg.layers
+    H, d = cfg.n_kv_heads, cfg.head_dim
+    lens = workloads.seq_lengths(cfg, dev)
+    lens_h = [int(x) for x in lens.cpu()]
+    base = Layer.create(kc, vc, d, H, cfg.n_seqs, cfg.capacity, device=dev)
+    for b, n in enumerate(lens_h):
+        for a in range(0, n, 32768):
+            e = min(n, a + 32768)
+            k = workloads.kv_rows(cfg, 0, b, "k", a, e - a, dev)
+            v = workloads.kv_rows(cfg, 0, b, "v", a, e - a, dev)
+            kvq_append(base, k, v, torch.full((e - a,), b, dtype=torch.int32, device=dev),
+                       torch.arange(a, e, dtype=torch.int64, device=dev))
+            del k, v
+    caches = [base] + [base.clone() for _ in range(rotate - 1)]
+    q = workloads.queries(cfg, 0, dev)
+    out = torch.empty_like(q)
+    max_len = max(lens_h)
+    ws = decode_workspace(base, cfg.n_q_heads, cfg.n_seqs, max_len)
+    cap = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    per_graph = max(4, rotate)
+    with torch.cuda.stream(cap):
+        for i in range(per_graph):
+            kvq_attend_decode(caches[i % rotate], q, lens, max_len, cfg.scale, out=out, workspace=ws, stream=cap)
+        with torch.cuda.graph(g, stream=cap):
+            for i in range(per_graph):
+                kvq_attend_decode(caches[i % rotate], q, lens, max_len, cfg.scale, out=out, workspace=ws,
+                                  stream=cap)
+    torch.cuda.synchronize()
+    reps = max(4, args.steps // (4 * per_graph))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g.replay()
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / (reps * per_graph)
+    row_bytes = sum(r + 2 * (d // (64 if c == "q4_g64" else 32))
+                    for r, c in ((d if kc == "q8_0" else d // 2, kc), (d if vc == "q8_0" else d // 2, vc)))
+    kv = sum(lens_h) * H * row_bytes
+    del caches, base
+    gbs = kv / (ms * 1e-3) / 1e9
+    return {"workload": cfg.name, "n_seqs": cfg.n_seqs, "lengths": lens_h if cfg.n_seqs > 1 else lens_h[0],
+            "n_q_heads": cfg.n_q_heads, "n_kv_heads": H, "head_dim": d, "k_codec": kc, "v_codec": vc,
+            "ms_per_call": round(ms, 5), "kv_bytes_per_call": kv, "rotated_caches": rotate,
+            "value": round(gbs, 2), "unit": "GB/s", "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+            "step": "kvq_attend_decode over every sequence, HIP-graph replay"}
 
 
 def run_paged(torch, dev, cfg, base, k_new, v_new, q, seq_len, nb, args) -> dict:
