@@ -111,7 +111,7 @@ struct Cfg {
     static constexpr int OFF_QOP = 0;                                 // [KSTEPS][hi,lo][64 lanes] h8
     static constexpr int OFF_TMAX = OFF_QOP + KSTEPS * 2 * 64 * 16;   // [KSTEPS][16] fp32
     static constexpr int OFF_CORR = OFF_TMAX + KSTEPS * 16 * 4;       // [KSTEPS][16] fp32
-    static constexpr int OFF_CNT = OFF_CORR + KSTEPS * 16 * 4;        // block hand-out counter
+    static constexpr int OFF_CNT = OFF_CORR + KSTEPS * 16 * 4;        // block hand-out counter, append flag
     static constexpr int OFF_ML = OFF_CNT + 16;                       // [wave][16] (max, sum)
     static constexpr int OFF_FIN = OFF_ML + kWaves * 16 * 8;          // [16] merged (max, sum)
     static constexpr int OFF_SLOTS = OFF_FIN + 16 * 8;                // [wave][NS] slots
@@ -487,11 +487,25 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
         qv[4] = use ? x1.x : 0.f; qv[5] = use ? x1.y : 0.f; qv[6] = use ? x1.z : 0.f; qv[7] = use ? x1.w : 0.f;
     }
     // ---- fused append (app_rows > 0): wave 0 quantizes and stores this
-    // split's share of the new rows [len - app_rows, len) and waits for its
-    // stores before the first barrier.  A DMA that could read those bytes
-    // (blocks from the new rows' first block minus one on: a line of scales
-    // can straddle two blocks) is issued only after that barrier.
-    int dma_late = nblk;  // local blocks >= dma_late wait for the first barrier
+    // split's share of the new rows [len - app_rows, len).  A DMA that could
+    // read those bytes (blocks from the new rows' first block minus one on: a
+    // line of scales can straddle two blocks) must not start before the
+    // stores are complete.  Two ways:
+    //  * flag mode (a one-block ring with a head start, the new rows in one
+    //    pass of the wave, and no such block among the ones the prologue
+    //    issues): wave 0 loads the new rows together with the query, stores
+    //    them without waiting, and raises an LDS flag once its first
+    //    complete wait (before its second block) has covered the stores; a
+    //    wave that is handed such a block waits for the flag first.  Nobody
+    //    else waits for the stores.
+    //  * otherwise wave 0 waits for its stores before the first barrier, and
+    //    such blocks are issued after that barrier.
+    int dma_late = nblk;  // local blocks >= dma_late wait for the stores
+    bool flag_mode = false;
+    float xk[8], xv[8];
+    int64_t app_hl = 0, app_row = 0;
+    int app_chunk = 0;
+    bool app_ok = false;
     if (a.app_rows > 0) {
         const int64_t first = len - a.app_rows;
         const int64_t lo = first > r0 ? first : r0;
@@ -500,9 +514,34 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
             const int nb0 = (int)((lo - r0) / kBlockRows);
             // paged: any block of the split may sit next to the new rows' one
             dma_late = paged ? 0 : (nb0 > 0 ? nb0 - 1 : 0);
+            constexpr int CH = D / 8;  // lanes per row (8 channels each)
+            flag_mode = C::HEAD2 && !paged && dma_late >= C::NSLOT * kWaves && (hi - lo) * CH <= 64;
             if (wave == 0) {
-                append_rows<D, KC, VC>(a, b, kvh, first, lo, hi, lane);
-                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                if (flag_mode) {
+                    const int items = (int)(hi - lo) * CH;
+                    const bool livei = lane < items;
+                    const int r = livei ? lane / CH : 0;
+                    app_chunk = lane % CH;
+                    const int64_t pos = lo + r;
+                    app_ok = livei && phys_row(a.k, a.pt, b, kvh, pos, app_hl, app_row);
+                    if (livei) {
+                        const int64_t off =
+                            (((int64_t)b * a.app_rows + (pos - first)) * a.k.n_kv_heads + kvh) * D + 8 * app_chunk;
+                        const float4 *pk = reinterpret_cast<const float4 *>(a.app_k + off);
+                        const float4 *pv = reinterpret_cast<const float4 *>(a.app_v + off);
+                        const float4 k0 = pk[0], k1 = pk[1], v0 = pv[0], v1 = pv[1];
+                        xk[0] = k0.x; xk[1] = k0.y; xk[2] = k0.z; xk[3] = k0.w;
+                        xk[4] = k1.x; xk[5] = k1.y; xk[6] = k1.z; xk[7] = k1.w;
+                        xv[0] = v0.x; xv[1] = v0.y; xv[2] = v0.z; xv[3] = v0.w;
+                        xv[4] = v1.x; xv[5] = v1.y; xv[6] = v1.z; xv[7] = v1.w;
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) xk[i] = xv[i] = 0.0f;
+                    }
+                } else {
+                    append_rows<D, KC, VC>(a, b, kvh, first, lo, hi, lane);
+                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                }
             }
         }
     }
@@ -513,6 +552,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     // through hand-issued accesses, so it never waits for these DMAs.
     asm volatile("s_waitcnt vmcnt(0)" : "+v"(qv[0]), "+v"(qv[1]), "+v"(qv[2]), "+v"(qv[3]), "+v"(qv[4]),
                  "+v"(qv[5]), "+v"(qv[6]), "+v"(qv[7])::"memory");
+    if (flag_mode && wave == 0) {
+        quantize_store<KC, ROLE_K>(a.k, app_hl, app_row, app_chunk, xk, app_ok);
+        quantize_store<VC, ROLE_V>(a.v, app_hl, app_row, app_chunk, xv, app_ok);
+    }
     if (wave < dma_late) issue(wave, myslots);
 
     const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_void *)smem;
@@ -523,7 +566,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
         m = quad_max(m, x32);
         if (q4 == 0) ds_wr(lds0 + (wave * 16 + h) * 4, __builtin_bit_cast(uint32_t, m), C::OFF_TMAX);
     }
-    if (tid == 0) ds_wr(lds0, (uint32_t)(C::NSLOT * kWaves), C::OFF_CNT);
+    if (tid == 0) {
+        ds_wr(lds0, (uint32_t)(C::NSLOT * kWaves), C::OFF_CNT);
+        ds_wr(lds0, 0u, C::OFF_CNT + 4);  // the new rows' stores are not known complete yet
+    }
     lds_barrier();
     if (wave >= dma_late) issue(wave, myslots);
 
@@ -721,6 +767,18 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     // increasing block indices, so the first one past the end ends the wave.
     // At the top of a slot the DMAs issued after its own are those of the
     // NS - 1 other slots: waiting until at most that many remain is exact.
+    // Waits until wave 0 has raised the flag (its stores of the new rows are
+    // complete).  Wave 0 raises it without waiting for any other wave, so the
+    // wait ends; the iteration cap only bounds it.
+    auto wait_appended = [&]() {
+        for (int it = 0; it < (1 << 20); ++it) {
+            uint32_t f;
+            ds_rd(f, lds0, C::OFF_CNT + 4);
+            lds_wait<1>(&f);
+            if (__builtin_amdgcn_readfirstlane(f) != 0u) break;
+            __builtin_amdgcn_s_sleep(2);
+        }
+    };
     auto grab = [&]() -> int {
         uint32_t v = 0;
         if (lane == 0) v = ds_add_rtn(lds0, 1u, C::OFF_CNT);
@@ -742,10 +800,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
         sidx[0] = nblk;
         if (wave + kWaves < nblk) {
             vm_wait<0>();
+            // in flag mode wave 0 always gets here (its second block exists),
+            // and this complete wait covered its stores of the new rows
+            if (flag_mode && wave == 0) ds_wr(lds0, 1u, C::OFF_CNT + 4);
             Payload<D, KC, VC> pl;
             read_slot<D, KC, VC>(pl, a16, a8, a4, aks, avs, C::SLOT);
             const int nxt = grab();
             sidx[0] = nxt;
+            if (flag_mode && nxt >= dma_late && nxt < nblk) wait_appended();
             issue(nxt, myslots);
             process(pl, wave + kWaves);
         }
@@ -784,6 +846,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
                  read_slot<D, KC, VC>(pl, a16, a8, a4, aks, avs, S * C::SLOT);
                  const int nxt = grab();
                  sidx[S] = nxt;
+                 if (flag_mode && nxt >= dma_late && nxt < nblk) wait_appended();
                  issue(nxt, myslots + S * C::SLOT);
                  process(pl, idx);
              }()),

@@ -13,8 +13,9 @@ Covered: every codec pair; head_dim 64, 128 and 256; the new row at the start
 of a block, at the end of a block, as the last row of a split and as the
 first row of a split of its own; a sequence of length 1; a sequence of
 length 0 (nothing written, output 0) among others; two and three new rows
-straddling a block and a split boundary; new rows at negative positions
-(length below q_len: skipped); a call split into several launches (q_len *
+straddling a block and a split boundary; the new row deep in a long split
+(its block waits for the appending wave, the rest does not); new rows at
+negative positions (length below q_len: skipped); a call split into several launches (q_len *
 gqa > 16); and the 64K-context Q4_G64 step against the unfused step.
 """
 import numpy as np
@@ -139,6 +140,16 @@ def test_several_launches(gpu):
 
 def test_many_splits(gpu):
     _case(gpu, "q8_0", "q4_0", 128, hq=32, hkv=8, lens=[20000, 3001], seed=9)
+
+
+@pytest.mark.parametrize("kc,vc,d", [("q8_0", "q4_0", 128), ("q4_g64", "q4_g64", 256), ("q4_0", "q4_g64", 64),
+                                     ("q8_0", "q8_0", 128)])
+def test_new_row_deep_in_a_long_split(gpu, kc, vc, d):
+    # 8 kv-heads x 20668 rows give 768-row splits; the last one holds 700 rows
+    # (22 blocks) with the new row in its last block, so the blocks that the
+    # prologue streams never include it and, with a one-block ring, only the
+    # blocks near the new row wait for the appending wave's stores
+    _case(gpu, kc, vc, d, hq=16, hkv=8, lens=[26 * 768 + 700], seed=d + CODECS.index(kc))
 
 
 def test_workload_64k_step_matches_unfused(gpu):
