@@ -496,8 +496,13 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
     bool have_s = false;  // S holds the scores of tile - 1 (late waves)
     bool have_p = false;  // P holds the probabilities of tile - 1
     for (int tile = 0; tile < ntiles; ++tile) {
-        if (tile + 1 < ntiles) dequant_tile(tile + 1, kbuf(tile + 1), vbuf(tile + 1));
-        if (tile + 2 < ntiles) load_tile(tile + 2);
+        // the late waves dequantize the next tile first (their matrix phase
+        // comes last), the early ones last (theirs comes first), so a SIMD's
+        // two waves overlap vector and matrix work in both halves
+        if (late || !C::PINGPONG) {
+            if (tile + 1 < ntiles) dequant_tile(tile + 1, kbuf(tile + 1), vbuf(tile + 1));
+            if (tile + 2 < ntiles) load_tile(tile + 2);
+        }
         if (late && have_s) {
             softmax(tile - 1);
             have_s = false;
@@ -520,8 +525,14 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
                 else pv(tile);
             }
         }
+        if (!late && C::PINGPONG) {
+            if (tile + 1 < ntiles) dequant_tile(tile + 1, kbuf(tile + 1), vbuf(tile + 1));
+            if (tile + 2 < ntiles) load_tile(tile + 2);
+        }
         // tile + 2's scales go where tile's were (read by its dequant, one
-        // iteration ago)
+        // iteration ago); under ping-pong the staging threads (wave 0) load
+        // them just before, which measured faster than staging them from
+        // the late waves, whose loads start at the top of the iteration
         if (tile + 2 < ntiles) stage_scales(tile + 2);
         __syncthreads();  // next tile's dequant and staging done; this tile's reads done
     }
