@@ -854,12 +854,82 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
         }(std::make_integer_sequence<int, NS>{});
     }
 
-    // ---- merge the waves.  Each wave publishes its (max, sum) per column;
-    // after one barrier (which also waited for every wave's last DMAs, so
-    // the slots are idle) every wave rescales its O to the columns' common
-    // max and parks it in the slot area; after a second barrier the threads
-    // add up the 8 parked copies, 4 channels each.
+    // ---- merge the waves.
     l_run = quad_sum(l_run, x32);
+    constexpr int D4 = D / 4;
+    // writes item (col, c) of the merged result: the output when the call has
+    // one split, else this split's partial (unnormalized O, max, sum)
+    auto emit = [&](int col, int c, const f4 &o, float M, float L) {
+        const int cq = col / G, ch = col % G;
+        if (a.max_splits == 1) {
+            const float r = L > 0.0f ? 1.0f / L : 0.0f;
+            float *dst = a.out + b * a.q_seq_stride + ((int64_t)cq * a.n_q_heads + (int64_t)kvh * G + ch) * D + c;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dst[i] = o[i] * r;
+            return;
+        }
+        const int64_t qh = ((int64_t)b * a.q_len + cq) * a.n_q_heads + (int64_t)kvh * G + ch;
+        const int64_t ph = qh * a.max_splits + sp;
+        *reinterpret_cast<f4 *>(a.part_o + ph * D + c) = o;
+        if (c == 0) {
+            a.part_ml[2 * ph] = M;
+            a.part_ml[2 * ph + 1] = L;
+        }
+    };
+    if (NC * C::DP * 4 <= C::NSLOT * C::SLOT) {
+        // Each wave parks its unscaled O and its (max, sum) as soon as its
+        // own blocks are done -- in its own slots, which no other wave
+        // touches -- so the parking overlaps the waves still streaming; after
+        // one barrier each thread weighs the 8 copies of 4 channels of one
+        // column by 2^(max_w - max).
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's last DMAs have landed
+        float *mm = reinterpret_cast<float *>(smem + C::OFF_ML);  // [16][wave] max, then [16][wave] sum
+        if (h < NC) {
+            float *own = reinterpret_cast<float *>(myslots) + h * C::DP + 4 * q4;
+#pragma unroll
+            for (int cb = 0; cb < C::CB; ++cb) *reinterpret_cast<f4 *>(own + 16 * cb) = O[cb];
+            if (q4 == 0) {
+                mm[h * kWaves + wave] = m_run;
+                mm[16 * kWaves + h * kWaves + wave] = l_run;
+            }
+        }
+        __syncthreads();
+        for (int idx = tid; idx < NC * D4; idx += kThreads) {
+            const int col = idx / D4, c = (idx % D4) * 4;
+            float mw[kWaves], lw[kWaves];
+#pragma unroll
+            for (int w = 0; w < kWaves; w += 4) {
+                const f4 x = *reinterpret_cast<const f4 *>(mm + col * kWaves + w);
+                const f4 y = *reinterpret_cast<const f4 *>(mm + 16 * kWaves + col * kWaves + w);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    mw[w + i] = x[i];
+                    lw[w + i] = y[i];
+                }
+            }
+            float M = mw[0];
+#pragma unroll
+            for (int w = 1; w < kWaves; ++w) M = fmaxf(M, mw[w]);
+            const float Mref = M > -INFINITY ? M : 0.0f;  // -inf: no visible row in the split
+            float L = 0.0f;
+            f4 o = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) {
+                const float e = fast_exp2(mw[w] - Mref);  // 0 for a wave without visible rows
+                L = fmaf(e, lw[w], L);
+                const f4 x = *reinterpret_cast<const f4 *>(
+                    reinterpret_cast<const float *>(smem + C::OFF_SLOTS + w * C::NSLOT * C::SLOT) + col * C::DP + c);
+                o = f4{fmaf(e, x[0], o[0]), fmaf(e, x[1], o[1]), fmaf(e, x[2], o[2]), fmaf(e, x[3], o[3])};
+            }
+            emit(col, c, o, M, L);
+        }
+        return;
+    }
+    // Otherwise each wave publishes its (max, sum) per column; after one
+    // barrier (which also waited for every wave's last DMAs, so the slots are
+    // idle) every wave rescales its O to the columns' common max and parks it
+    // in the slot area; after a second barrier the threads add up the 8
+    // parked copies, 4 channels each.
     float *sml = reinterpret_cast<float *>(smem + C::OFF_ML);    // [wave][16][2]
     float *sfin = reinterpret_cast<float *>(smem + C::OFF_FIN);  // [16][2]
     if (h < NC && q4 == 0) {
@@ -889,7 +959,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
         }
     }
     __syncthreads();
-    constexpr int D4 = D / 4;
     for (int idx = tid; idx < NC * D4; idx += kThreads) {
         const int col = idx / D4, c = (idx % D4) * 4;
         const float *src = reinterpret_cast<const float *>(smem + C::OFF_SLOTS) + col * C::DP + c;
@@ -899,22 +968,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
             const f4 x = *reinterpret_cast<const f4 *>(src + w * NC * C::DP);
             o = f4{o[0] + x[0], o[1] + x[1], o[2] + x[2], o[3] + x[3]};
         }
-        const float M = sfin[2 * col], L = sfin[2 * col + 1];
-        const int cq = col / G, ch = col % G;
-        if (a.max_splits == 1) {  // the call has one split: write the output
-            const float r = L > 0.0f ? 1.0f / L : 0.0f;
-            float *dst = a.out + b * a.q_seq_stride + ((int64_t)cq * a.n_q_heads + (int64_t)kvh * G + ch) * D + c;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) dst[i] = o[i] * r;
-            continue;
-        }
-        const int64_t qh = ((int64_t)b * a.q_len + cq) * a.n_q_heads + (int64_t)kvh * G + ch;
-        const int64_t ph = qh * a.max_splits + sp;
-        *reinterpret_cast<f4 *>(a.part_o + ph * D + c) = o;
-        if (c == 0) {
-            a.part_ml[2 * ph] = M;
-            a.part_ml[2 * ph + 1] = L;
-        }
+        emit(col, c, o, sfin[2 * col], sfin[2 * col + 1]);
     }
 }
 
