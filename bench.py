@@ -112,7 +112,7 @@ def write_traffic_summary(pmc_dir: str):
         "# HBM traffic of one decode step, kvq_append_attend_decode (decode_kernel + combine_kernel),",
         "# 64K-context Q4_G64 decode (1 seq, 24/4 heads, head_dim 256), from rocprofv3 counters",
         "#",
-        "# commands (GPU box, repo root; one counter per run):",
+        "# commands (on the GPU machine, from the repo root; one counter per run):",
         "#   rocprofv3 --pmc FETCH_SIZE --kernel-include-regex 'decode_kernel|combine_kernel' -d <dir>/fetch -o fetch "
         "--output-format csv -- python -u bench.py --steps 32 --warmup 8 --step-only",
         "#   rocprofv3 --pmc WRITE_SIZE (same, -d <dir>/write)",
