@@ -53,6 +53,8 @@ def _args():
     p.add_argument("--prefill-only", action="store_true",
                    help="run only the prefill leg (2048-token chunk over a 32768-row prefix) and print its JSON: "
                         "the run that the prefill kernel's profile uses")
+    p.add_argument("--write-busy-summary", nargs=2, metavar=("KERNEL", "PMC_DIR"),
+                   help="summarize a rocprofv3 counter pass (KERNEL = prefill or decode) into profiles/ and exit")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run plain 256 MiB device copies (HBM counter calibration)")
     p.add_argument("--write-traffic-summary", metavar="PMC_DIR",
@@ -73,13 +75,17 @@ DECODE_SOURCES = ["block_quantized_kv_amd/csrc/attn_decode.hip", "block_quantize
                   "block_quantized_kv_amd/csrc/kvq_quant.h"]
 
 
-def decode_source_hash() -> str:
+def source_hash(sources) -> str:
     import hashlib
     h = hashlib.sha256()
-    for rel in DECODE_SOURCES:
+    for rel in sources:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def decode_source_hash() -> str:
+    return source_hash(DECODE_SOURCES)
 
 
 def _pmc_mean(path_glob: str, counter: str, name_pat: str):
@@ -155,6 +161,77 @@ def read_traffic():
         return None
 
 
+# ---- counter-backed matrix-core and vector activity -------------------------
+# One rocprofv3 --pmc pass with the counters below over the prefill leg
+# (--prefill-only) or over the decode step (--step-only).  MFMA busy fraction =
+# SQ_VALU_MFMA_BUSY_CYCLES / (SIMDs x cycles), where GRBM_GUI_ACTIVE reads the
+# sum of the 8 XCDs' busy cycles; SQ_INSTS_VALU includes the MFMA
+# instructions.  A summary records a hash of the kernel's sources and is used
+# only while they are unchanged.
+BUSY_COUNTERS = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA",
+                 "SQ_INSTS_LDS", "SQ_WAVES", "GRBM_GUI_ACTIVE"]
+N_SIMDS, N_XCDS = 1024, 8
+PREFILL_SOURCES = ["block_quantized_kv_amd/csrc/attn_prefill.hip", "block_quantized_kv_amd/csrc/kvq_device.h",
+                   "block_quantized_kv_amd/csrc/kvq_layout.h", "block_quantized_kv_amd/csrc/kvq_internal.h"]
+BUSY_FILES = {
+    "prefill": (os.path.join(ROOT, "profiles", "prefill2k_over32k_counters.txt"), "prefill_kernel", PREFILL_SOURCES,
+                "python -u bench.py --prefill-only"),
+    "decode": (os.path.join(ROOT, "profiles", "decode64k_q4g64_counters.txt"), "decode_kernel", DECODE_SOURCES,
+               "python -u bench.py --steps 32 --warmup 8 --step-only"),
+}
+
+
+def write_busy_summary(which: str, pmc_dir: str):
+    path, kname, sources, cmd = BUSY_FILES[which]
+    g = os.path.join(pmc_dir, "*_counter_collection.csv")
+    vals, n = {}, 0
+    for c in BUSY_COUNTERS:
+        vals[c], n = _pmc_mean(g, c, kname)
+        if vals[c] is None:
+            sys.exit(f"counter {c} of {kname} missing under {pmc_dir}")
+    cycles = vals["GRBM_GUI_ACTIVE"] / N_XCDS
+    waves = vals["SQ_WAVES"]
+    lines = [
+        f"# {kname}: matrix-core and vector activity per dispatch, from one rocprofv3 counter pass",
+        "# command (on the GPU machine, from the repo root):",
+        f"#   rocprofv3 --pmc {' '.join(BUSY_COUNTERS)} -d <dir> -o run --output-format csv -- {cmd}",
+        f"#   python bench.py --write-busy-summary {which} <dir>",
+        "# mfma_busy_frac = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8 XCDs)",
+        f"source_hash: {source_hash(sources)}",
+        f"dispatches: {n}",
+    ] + [f"{c}: {vals[c]:.6g}" for c in BUSY_COUNTERS] + [
+        f"cycles_per_xcd: {cycles:.6g}",
+        f"mfma_busy_frac: {vals['SQ_VALU_MFMA_BUSY_CYCLES'] / (N_SIMDS * cycles):.4f}",
+        f"valu_insts_per_wave: {vals['SQ_INSTS_VALU'] / waves:.6g}",
+        f"mfma_insts_per_wave: {vals['SQ_INSTS_MFMA'] / waves:.6g}",
+        f"lds_insts_per_wave: {vals['SQ_INSTS_LDS'] / waves:.6g}",
+    ]
+    with open(path, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def read_busy(which: str):
+    """The counter summary of a kernel as a dict, or None when it is missing
+    or was taken on other sources."""
+    path, _, sources, _ = BUSY_FILES[which]
+    try:
+        kv = {}
+        with open(path) as fh:
+            for line in fh:
+                if ":" in line and not line.startswith("#"):
+                    k, v = line.split(":", 1)
+                    kv[k.strip()] = v.strip()
+        if kv.get("source_hash") != source_hash(sources):
+            return None
+        return {"mfma_busy_frac": float(kv["mfma_busy_frac"]),
+                "valu_insts_per_wave": float(kv["valu_insts_per_wave"]),
+                "mfma_insts_per_wave": float(kv["mfma_insts_per_wave"]),
+                "source": os.path.relpath(path, ROOT)}
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def calibrate_copy():
     """Plain device-to-device copies of a known size: what FETCH_SIZE /
     WRITE_SIZE read for exactly 256 MiB in and 256 MiB out per dispatch."""
@@ -189,6 +266,9 @@ def main():
         return
     if args.write_traffic_summary:
         write_traffic_summary(args.write_traffic_summary)
+        return
+    if args.write_busy_summary:
+        write_busy_summary(*args.write_busy_summary)
         return
     if args.prefill_only:
         import torch
@@ -384,7 +464,8 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "bytes_per_launch": nb["fused_kernel"], "avg_launch_ms": round(att_avg_ms, 5),
                      "stream_read_peak_gbs": speak["gbs"] if speak else None,
-                     "frac_of_stream_read_peak": round(achieved / speak["gbs"], 4) if speak else None},
+                     "frac_of_stream_read_peak": round(achieved / speak["gbs"], 4) if speak else None,
+                     "counters": read_busy("decode")},
     }
 
     if not args.step_only:
@@ -664,7 +745,8 @@ def run_prefill(torch, dev, args):
             "config": {"prefix": P, "chunk": T, "n_q_heads": hq, "n_kv_heads": hkv, "head_dim": d,
                        "k_codec": kc, "v_codec": vc},
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": None}}
+                         "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                         "counters": read_busy("prefill")}}
 
 
 def run_baselines(torch, dev, cfg, caches, q, seq_len, scale, steps):
