@@ -159,6 +159,11 @@ struct Streams {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
+// Cache policy of the block DMAs: non-temporal.  Every K/V byte is read once
+// per call, so the lines are not worth keeping; measured 22.4 -> 20.9 us per
+// 64K step and 238 -> 222 us per 196K four-layer step.
+constexpr int kStreamPolicy = 2;  // nt
+
 // Copies B bytes at byte goff of stream r to LDS at dst (a plain copy; lane
 // l carries bytes [16 l, 16 l + 16) of each 1 KB piece).
 template <int B>
@@ -166,16 +171,16 @@ __device__ __forceinline__ void dma_region(__amdgpu_buffer_rsrc_t r, uint32_t go
     constexpr int N16 = B / 1024, N4 = (B % 1024) / 256, TAIL = B % 256;
 #pragma unroll
     for (int c = 0; c < N16; ++c)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(dst + c * 1024), 16, goff + c * 1024 + lane * 16, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(dst + c * 1024), 16, goff + c * 1024 + lane * 16, 0, 0, kStreamPolicy);
 #pragma unroll
     for (int c = 0; c < N4; ++c)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(dst + N16 * 1024 + c * 256), 4,
-                                                 goff + N16 * 1024 + c * 256 + lane * 4, 0, 0, 0);
+                                                 goff + N16 * 1024 + c * 256 + lane * 4, 0, 0, kStreamPolicy);
     if constexpr (TAIL != 0) {
         static_assert(TAIL % 4 == 0, "scale regions are whole words");
         if (lane * 4 < TAIL)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)(dst + N16 * 1024 + N4 * 256), 4,
-                                                     goff + N16 * 1024 + N4 * 256 + lane * 4, 0, 0, 0);
+                                                     goff + N16 * 1024 + N4 * 256 + lane * 4, 0, 0, kStreamPolicy);
     }
 }
 

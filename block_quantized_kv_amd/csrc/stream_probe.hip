@@ -2,8 +2,9 @@
 // the decode kernel's HBM roofline is quoted against beside the published
 // peak.  Not part of the attention path.
 //
-// Each wave reads a contiguous stripe of the buffer with 16-byte buffer
-// loads, eight 1 KB pieces in flight, and folds the words into one value that
+// Each wave reads a contiguous stripe of the buffer with 16-byte
+// non-temporal buffer loads (the decode kernel's cache policy), eight 1 KB
+// pieces in flight, and folds the words into one value that
 // is stored only if it matches an impossible pattern (so the loads stay).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -29,7 +30,7 @@ __global__ __launch_bounds__(64 * kWavesPerGroup) void stream_read_kernel(const 
         u4v v[kDepth];
 #pragma unroll
         for (int d = 0; d < kDepth; ++d)
-            v[d] = __builtin_bit_cast(u4v, __builtin_amdgcn_raw_buffer_load_b128(r, w0 + off + d * kPiece + lane * 16, 0, 0));
+            v[d] = __builtin_bit_cast(u4v, __builtin_amdgcn_raw_buffer_load_b128(r, w0 + off + d * kPiece + lane * 16, 0, 2 /* nt */));
 #pragma unroll
         for (int d = 0; d < kDepth; ++d) acc ^= v[d].x ^ v[d].y ^ v[d].z ^ v[d].w;
     }
