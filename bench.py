@@ -727,6 +727,25 @@ def run_prefill(torch, dev, args):
         kvq_attend_prefill(layer, q, 0, P, 1.0 / d ** 0.5)
     except KvqError as e:
         return {"status": "unavailable", "reason": str(e)}
+    # the chunk's own append (quantize-on-write of its 2048 rows x kv-heads),
+    # which precedes the attention in a prefill step; it rewrites the same
+    # rows with the same values, so the cache is unchanged
+    kc_chunk, vc_chunk = k[P:P + T].contiguous(), v[P:P + T].contiguous()
+    seq0 = torch.zeros(T, dtype=torch.int32, device=dev)
+    pos = torch.arange(P, P + T, dtype=torch.int64, device=dev)
+    for _ in range(3):
+        kvq_append(layer, kc_chunk, vc_chunk, seq0, pos)
+    torch.cuda.synchronize()
+    a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a0.record()
+    for _ in range(20):
+        kvq_append(layer, kc_chunk, vc_chunk, seq0, pos)
+    a1.record()
+    torch.cuda.synchronize()
+    append_ms = a0.elapsed_time(a1) / 20
+    append_in = 2 * T * hkv * d * 4
+    append_out = T * hkv * sum(r + 2 * (d // (64 if c == "q4_g64" else 32))
+                               for r, c in ((d if kc == "q8_0" else d // 2, kc), (d if vc == "q8_0" else d // 2, vc)))
     out = torch.empty(T, hq, d, device=dev)
     for _ in range(3):
         kvq_attend_prefill(layer, q, 0, P, 1.0 / d ** 0.5, out=out)
@@ -742,6 +761,9 @@ def run_prefill(torch, dev, args):
     tf = flops / (ms * 1e-3) / 1e12
     return {"metric": "prefill TFLOP/s", "value": round(tf, 2), "unit": "TFLOP/s",
             "ms_per_chunk": round(ms, 4), "flop": flops,
+            "chunk_append": {"ms": round(append_ms, 4), "bytes_in": append_in, "bytes_out": append_out,
+                             "gbs": round((append_in + append_out) / (append_ms * 1e-3) / 1e9, 1),
+                             "step": "kvq_append of the chunk's 2048 rows (K and V, all kv-heads)"},
             "config": {"prefix": P, "chunk": T, "n_q_heads": hq, "n_kv_heads": hkv, "head_dim": d,
                        "k_codec": kc, "v_codec": vc},
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS,

@@ -59,25 +59,34 @@ __device__ __forceinline__ void store_codes(uint8_t *blk, int d, int j, int c0, 
 // `pos` of head `head_lin` (= seq * n_kv_heads + kv-head) and stores codes and
 // group scale.  Every lane of the wave must call it (the group maximum is
 // shuffled between lanes); only lanes with `store` set write.
-template <int CODEC, int ROLE>
-__device__ __forceinline__ void quantize_store(const PlaneView &pl, int64_t head_lin, int64_t pos, int chunk,
-                                               const float (&x)[8], bool store) {
-    const int d = pl.head_dim;
+// The codes q[0..7] of this thread's 8 channels and the group's binary16
+// scale.  Every lane of the wave must call it (the group maximum is shuffled
+// between the group's G/8 adjacent lanes).
+template <int CODEC>
+__device__ __forceinline__ _Float16 quantize8(const float (&x)[8], int (&q)[8]) {
     float amax = 0.0f;
     for (int s = 0; s < 8; ++s) amax = fmaxf(amax, fabsf(x[s]));
     constexpr int lanes_per_group = group_size(CODEC) / 8;
     for (int m = 1; m < lanes_per_group; m <<= 1) amax = fmaxf(amax, shfl_xor(amax, m));
-
     float dscale = __fdiv_rn(amax, (float)qmax(CODEC));
     dscale = fminf(dscale, 65504.0f);
     const _Float16 d16 = (_Float16)dscale;  // v_cvt_f16_f32: round to nearest even
     const float dq = (float)d16;
-    int q[8];
     for (int s = 0; s < 8; ++s) {
         float r = dq == 0.0f ? 0.0f : __builtin_rintf(__fdiv_rn(x[s], dq));
         r = fminf(fmaxf(r, (float)(-qmax(CODEC) - 1)), (float)qmax(CODEC));
         q[s] = (int)r;
     }
+    return d16;
+}
+
+template <int CODEC, int ROLE>
+__device__ __forceinline__ void quantize_store(const PlaneView &pl, int64_t head_lin, int64_t pos, int chunk,
+                                               const float (&x)[8], bool store) {
+    const int d = pl.head_dim;
+    constexpr int lanes_per_group = group_size(CODEC) / 8;
+    int q[8];
+    const _Float16 d16 = quantize8<CODEC>(x, q);
     if (!store) return;
     const int64_t blk_idx = pos / kBlockRows;
     const int j = (int)(pos % kBlockRows);

@@ -1,7 +1,9 @@
 """GPU quantize-on-append and dequant parity: codes and scales bit-exact
 against the oracle (den_llama.cpp, "Results": quantizer byte-identical to the
 CPU reference, dequant bit-identical), on every codec, both plane roles and
-head_dim 64/128/256, with inputs that stress every rounding path."""
+head_dim 64/128/256, with inputs that stress every rounding path; whole
+aligned 32-row blocks (written word by word) beside scattered rows in one
+call."""
 import numpy as np
 import pytest
 import torch
@@ -70,6 +72,35 @@ def test_append_bit_exact_scattered(gpu, codec, d):
             m = seq == s
             assert np.array_equal(got[:, pos[m]].transpose(1, 0, 2).view(np.uint32),
                                   want_hat[m].view(np.uint32))
+
+
+@pytest.mark.parametrize("kc,vc,d", [("q8_0", "q4_0", 128), ("q4_g64", "q4_g64", 256), ("q4_0", "q8_0", 64)])
+def test_append_whole_blocks_and_others_in_one_call(gpu, kc, vc, d):
+    # one call whose 32-token groups are: an aligned block of sequence 0, a
+    # block-sized run starting mid-block, an aligned block of sequence 1,
+    # 32 tokens that straddle two sequences, and a ragged tail of 7: whole V
+    # blocks are written word by word, the rest value by value
+    rng = np.random.default_rng(d + len(kc) * 10 + len(vc))
+    H, S, cap = 2, 2, 256
+    seq = np.concatenate([np.zeros(32), np.zeros(32), np.ones(32), np.r_[np.zeros(16), np.ones(16)],
+                          np.ones(7)]).astype(np.int32)
+    pos = np.concatenate([np.arange(64, 96), np.arange(144, 176), np.arange(32, 64),
+                          np.r_[np.arange(200, 216), np.arange(100, 116)], np.arange(240, 247)]).astype(np.int64)
+    n = len(seq)
+    xk = _stress_rows(rng, n, H, d, kc)
+    xv = _stress_rows(rng, n, H, d, vc)
+    layer = Layer.create(kc, vc, d, H, S, cap, device=gpu)
+    kvq_append(layer, torch.from_numpy(xk).to(gpu), torch.from_numpy(xv).to(gpu),
+               torch.from_numpy(seq).to(gpu), torch.from_numpy(pos).to(gpu))
+    for plane, x, codec in ((layer.k, xk, kc), (layer.v, xv, vc)):
+        codes, scales = layout.plane_to_rows(plane)
+        want_c, want_s = oracle.quantize_rows(codec, x)
+        assert np.array_equal(codes[seq, :, pos], want_c), codec
+        assert np.array_equal(scales[seq, :, pos], want_s), codec
+        untouched = np.ones((S, cap), bool)
+        untouched[seq, pos] = False
+        assert not codes.transpose(0, 2, 1, 3)[untouched].any()
+        assert not scales.transpose(0, 2, 1, 3)[untouched].any()
 
 
 @pytest.mark.parametrize("codec", CODECS)
