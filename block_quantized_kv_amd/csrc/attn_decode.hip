@@ -134,6 +134,10 @@ struct Cfg {
     // instead of requesting it only once the first has arrived.
     static constexpr bool HEAD2 = NS == 1 && NS_FIT >= 2 && !TWO_PHASE;
     static constexpr int NSLOT = NS + (HEAD2 ? 1 : 0);  // slots per wave
+    // A block's code bytes are always whole 128-byte lines; its scales are
+    // too except for Q4_G64 at head_dim 64 (64 bytes), where a line of scales
+    // is shared with a neighbouring block
+    static constexpr bool SCALES_WHOLE_LINES = (2 * K_BLOCK_SCALES) % 128 == 0 && (2 * V_BLOCK_SCALES) % 128 == 0;
     static_assert(NS >= 1, "one block slot per wave must fit in LDS");
     static_assert((NS - 1) * N_DMA <= 63, "DMAs in flight exceed the wait counter");
     static_assert(SL_V % 16 == 0 && SL_KS % 16 == 0 && SL_VS % 16 == 0 && SLOT % 16 == 0, "slot alignment");
@@ -493,8 +497,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     }
     // ---- fused append (app_rows > 0): wave 0 quantizes and stores this
     // split's share of the new rows [len - app_rows, len).  A DMA that could
-    // read those bytes (blocks from the new rows' first block minus one on: a
-    // line of scales can straddle two blocks) must not start before the
+    // read those bytes, or pull a line holding them into a cache before they
+    // land (blocks from the new rows' first block minus one on; in paged
+    // planes, where any block may be a memory neighbour, every block if a
+    // line of scales can straddle two blocks), must not start before the
     // stores are complete.  Two ways:
     //  * flag mode (a one-block ring with a head start, the new rows in one
     //    pass of the wave, and no such block among the ones the prologue
@@ -518,9 +524,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
         if (lo < hi) {
             const int nb0 = (int)((lo - r0) / kBlockRows);
             // paged: any block of the split may sit next to the new rows' one
-            dma_late = paged ? 0 : (nb0 > 0 ? nb0 - 1 : 0);
+            // in memory, which matters only where it can share a line with it
+            dma_late = (paged && !C::SCALES_WHOLE_LINES) ? 0 : (nb0 > 0 ? nb0 - 1 : 0);
             constexpr int CH = D / 8;  // lanes per row (8 channels each)
-            flag_mode = C::HEAD2 && !paged && dma_late >= C::NSLOT * kWaves && (hi - lo) * CH <= 64;
+            flag_mode = C::HEAD2 && dma_late >= C::NSLOT * kWaves && (hi - lo) * CH <= 64;
             if (wave == 0) {
                 if (flag_mode) {
                     const int items = (int)(hi - lo) * CH;
