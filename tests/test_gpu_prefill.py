@@ -6,7 +6,8 @@ workload statement (the matrix cores see K_hat, V_hat, the scaled query and P
 rounded to binary16).
 Covered: the tiny prefill enumerated in full, ragged prefix/chunk lengths,
 every codec pair, head_dim 64/128/256, several GQA ratios, a chunk at
-position 0, queries far outside the binary16 range, and the 2048-token chunk over a 32768-token prefix on 256
+position 0, queries far outside the binary16 range, the chunk of a middle sequence of a three-sequence
+cache over several workgroups at every head_dim, and the 2048-token chunk over a 32768-token prefix on 256
 sampled (token, head) rows including the first and last 64 tokens.
 """
 import numpy as np
@@ -95,3 +96,28 @@ def test_workload_prefill_2048_over_32768(gpu):
     heads = [t % hq for t in edge] + list(rng.integers(0, hq, 128))
     _run(gpu, W["k_codec"], W["v_codec"], W["head_dim"], hq, W["n_kv_heads"], P, T,
          sample=(np.array(toks), np.array(heads)))
+
+
+@pytest.mark.parametrize("kc,vc,d", [("q4_0", "q8_0", 64), ("q8_0", "q4_0", 128), ("q4_g64", "q4_g64", 256)])
+def test_middle_sequence_over_several_workgroups(gpu, kc, vc, d):
+    # the chunk of sequence 1 of a three-sequence cache whose neighbours hold
+    # other rows (reading the wrong sequence shows), 4 x 200 (token, head)
+    # columns per kv-head: several workgroups of columns, at every head_dim
+    hq, hkv, P, T = 8, 2, 150, 200
+    q, k, v = workloads.prefill_inputs(gpu, seed_layer=d, prefix=P, chunk=T, n_q_heads=hq, n_kv_heads=hkv,
+                                       head_dim=d)
+    cap = (P + T + 31) // 32 * 32
+    layer = Layer.create(kc, vc, d, hkv, 3, cap, device=gpu)
+    for s in (0, 2):
+        _, ko, vo = workloads.prefill_inputs(gpu, seed_layer=d + 1 + s, prefix=P, chunk=T, n_q_heads=hq,
+                                             n_kv_heads=hkv, head_dim=d)
+        append_rows(layer, 4.0 * ko, -3.0 * vo, s, 0)
+    append_rows(layer, k, v, 1, 0)
+    scale = 1.0 / np.sqrt(d)
+    out = kvq_attend_prefill(layer, q, 1, P, scale).cpu().numpy()
+    kh = oracle.quant_dequant(kc, k.cpu().numpy().transpose(1, 0, 2).copy())
+    vh = oracle.quant_dequant(vc, v.cpu().numpy().transpose(1, 0, 2).copy())
+    ref = oracle.attend_prefill(q.float().cpu().numpy(), kh, vh, P, scale)
+    assert np.isfinite(out).all()
+    err = rel_err(out, ref)
+    assert err <= TOL, (kc, vc, d, err)
