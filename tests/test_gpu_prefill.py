@@ -16,7 +16,7 @@ import torch
 
 import oracle
 import workloads
-from block_quantized_kv_amd import Layer, kvq_append, kvq_attend_prefill
+from block_quantized_kv_amd import Layer, kvq_attend_prefill
 from gpu_helpers import append_rows, rel_err
 
 pytestmark = pytest.mark.gpu
