@@ -290,7 +290,7 @@ def main():
                                         kvq_attend_decode, load_library)
     load_library()
     dev = torch.device("cuda:0")
-    cfg = workloads.CONFIGS[3]
+    cfg = workloads.DECODE_64K
     kc, vc = cfg.layers[0]
     n, H, d = cfg.ctx, cfg.n_kv_heads, cfg.head_dim
 
@@ -472,8 +472,8 @@ def main():
         run_multi_query(torch, dev, cfg, caches, k_new2, v_new2, seq_len, nb, args, stream, result)
         result["paged"] = run_paged(torch, dev, cfg, base, k_new, v_new, q, seq_len, nb, args)
         result["long_context"] = run_long_context(torch, dev, args)
-        result["decode_32k"] = run_decode_config(torch, dev, args, 2, rotate=20)
-        result["batched_decode"] = run_decode_config(torch, dev, args, 5, rotate=1)
+        result["decode_32k"] = run_decode_config(torch, dev, args, workloads.DECODE_32K, rotate=20)
+        result["batched_decode"] = run_decode_config(torch, dev, args, workloads.BATCHED, rotate=1)
     if speak is not None:
         result["stream_read_peak"] = speak
     if not args.no_baselines:
@@ -526,7 +526,7 @@ def run_long_context(torch, dev, args) -> dict:
     rotation is needed)."""
     import workloads
     from block_quantized_kv_amd import Layer, decode_workspace, kvq_append, kvq_attend_decode
-    cfg = workloads.CONFIGS[4]
+    cfg = workloads.DECODE_196K
     n, H, d = cfg.ctx, cfg.n_kv_heads, cfg.head_dim
     layers, qs, outs, kv_bytes = [], [], [], []
     for li, (kc, vc) in enumerate(cfg.layers):
@@ -570,7 +570,7 @@ def run_long_context(torch, dev, args) -> dict:
             "step": "4 x kvq_attend_decode (one per layer), HIP-graph replay"}
 
 
-def run_decode_config(torch, dev, args, cid: int, rotate: int) -> dict:
+def run_decode_config(torch, dev, args, cfg, rotate: int) -> dict:
     """Attention-only decode of a workload configuration over all of its
     sequences: one kvq_attend_decode call per step, timed as HIP-graph replays
     that rotate over `rotate` independent caches (so the 256 MB MALL cannot
@@ -578,7 +578,6 @@ def run_decode_config(torch, dev, args, cid: int, rotate: int) -> dict:
     attended row, once per kv-head."""
     import workloads
     from block_quantized_kv_amd import Layer, decode_workspace, kvq_append, kvq_attend_decode
-    cfg = workloads.CONFIGS[cid]
     (kc, vc), = cfg.layers
     H, d = cfg.n_kv_heads, cfg.head_dim
     lens = workloads.seq_lengths(cfg, dev)
@@ -836,8 +835,7 @@ def run_quality(torch, dev, args):
     import workloads
     from block_quantized_kv_amd import Layer, kvq_append, kvq_attend_decode, kvq_dequant
     res = {}
-    for cid in (2, 3):
-        cfg = workloads.CONFIGS[cid]
+    for cfg in (workloads.DECODE_32K, workloads.DECODE_64K):
         n, H, d, hq = cfg.ctx, cfg.n_kv_heads, cfg.head_dim, cfg.n_q_heads
         G = hq // H
         k = workloads.kv_rows(cfg, 0, 0, "k", 0, n, dev)

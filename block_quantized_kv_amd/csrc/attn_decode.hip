@@ -42,14 +42,22 @@
 //    would wait for every DMA before any LDS read), so the slot reads are
 //    hand-issued with an explicit wait for exactly the DMAs of that slot.
 //    Every DMA is issued unconditionally: one past the end of the split is
-//    cut off by the buffer range check and touches no memory.
+//    cut off by the buffer range check and touches no memory.  The DMAs are
+//    non-temporal (each K/V byte is read once per call).  A one-block ring
+//    starts with two blocks per wave where LDS has room (head start); big
+//    head_dim 256 blocks are copied and consumed K half, then V half.
 //  * The query operand (hi/lo halves for every channel step) and the bias
 //    corrections are prepared once per workgroup, each wave taking one channel
 //    step, and shared through LDS.
-//  * The 8 waves merge through LDS (each rescales its own O to the common
-//    max, then the copies are summed); each workgroup writes one partial
-//    (unnormalized O, max, sum) per query head, or the final output when the
-//    sequence fits in one split; combine_kernel merges the splits
+//  * Fused append: the workgroup whose split holds the step's new rows
+//    quantizes and stores them first (wave 0); DMAs of the blocks those
+//    stores touch wait for them (an LDS flag where possible, else a barrier).
+//  * The 8 waves merge through LDS: each parks its unscaled O and (max, sum)
+//    in its own slots as soon as its blocks are done, and after one barrier
+//    each thread weighs the 8 copies (or, where the parked columns do not
+//    fit, rescale to the common max, then sum).  Each workgroup writes one
+//    partial (unnormalized O, max, sum) per query head, or the final output
+//    when the sequence fits in one split; combine_kernel merges the splits
 //    (log-sum-exp) with many partial loads in flight at once.
 #include <utility>
 

@@ -1,8 +1,9 @@
 // kv_append.hip -- quantize-on-append and dequant kernels for gfx950.
 //
 // Quantizer (den_llama.cpp, "What this fork is": Q4_G64 = signed INT4 + one
-// FP16 scale per 64 values, byte-identical to the CPU reference; the q8_0 and
-// q4_0 scale rules of the workload statement):
+// FP16 scale per 64 values, byte-identical to the CPU reference; q8_0 and
+// q4_0, which the page names beside it, take the same rule at 32 values per
+// group with Qmax 127 and 7):
 //   amax = max|x| over the group (exact), d = amax / Qmax (IEEE binary32
 //   divide), d16 = binary16 nearest-even of min(d, 65504), dq = (float)d16,
 //   q = clamp(rint(x / dq), -Qmax-1, Qmax) with an IEEE divide, 0 if dq == 0.

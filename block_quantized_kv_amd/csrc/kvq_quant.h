@@ -1,7 +1,8 @@
 // kvq_quant.h -- quantize-on-append device code (den_llama.cpp, "What this
-// fork is": Q4_G64 = signed INT4 + one FP16 scale per 64 values; the q8_0 and
-// q4_0 scale rules of the workload statement), shared by the append kernel and
-// the decode kernel's fused append.
+// fork is": Q4_G64 = signed INT4 + one FP16 scale per 64 values; q8_0 and
+// q4_0, which the page names beside it, take the same rule at 32 values per
+// group with Qmax 127 and 7), shared by the append kernel and the decode
+// kernel's fused append.
 //   amax = max|x| over the group (exact), d = amax / Qmax (IEEE binary32
 //   divide), d16 = binary16 nearest-even of min(d, 65504), dq = (float)d16,
 //   q = clamp(rint(x / dq), -Qmax-1, Qmax) with an IEEE divide, 0 if dq == 0.

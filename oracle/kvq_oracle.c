@@ -175,7 +175,8 @@ int kvq_oracle_quantize_group(int codec, const float *x, uint16_t *scale_bits, i
 }
 
 /* Storage of one row's codes ([den] "What this fork is": signed INT4 for
- * Q4_G64; workload statement: q8_0 int8, q4_0 4-bit codes with offset 8).
+ * Q4_G64; q8_0 as int8 and q4_0 as 4-bit codes with offset 8, the storage
+ * of those two codecs that the page names beside it).
  * Logical row layout used by the oracle:
  *   q8_0   : byte i = two's complement int8 of q_i
  *   q4_0   : nibble i = q_i + 8

@@ -28,7 +28,7 @@ def _csv(path, rows):
 def test_step_bytes_of_the_64k_workload():
     # 65536 rows x 4 kv-heads x (136 + 136) B of Q4_G64 K and V at head_dim 256
     # (128 code bytes + 4 binary16 scales per row and plane)
-    nb = bench.decode_bytes(workloads.CONFIGS[3])
+    nb = bench.decode_bytes(workloads.DECODE_64K)
     assert nb["kv"] == 71_303_168
     assert nb["q_out"] == 2 * 24 * 256 * 4
     assert nb["append"] == 4 * 256 * 4 * 2 + 4 * 272

@@ -143,7 +143,7 @@ def test_append_out_of_range_positions_flagged(gpu):
 def test_append_full_workload_plane_bit_exact(gpu):
     """The 64K-context Q4_G64 plane of the decode workload, checked whole."""
     import workloads
-    cfg = workloads.CONFIGS[3]
+    cfg = workloads.DECODE_64K
     layer = Layer.create("q4_g64", "q4_g64", cfg.head_dim, cfg.n_kv_heads, 1, cfg.capacity, device=gpu)
     k = workloads.kv_rows(cfg, 0, 0, "k", 0, cfg.ctx, gpu)
     v = workloads.kv_rows(cfg, 0, 0, "v", 0, cfg.ctx, gpu)

@@ -2,7 +2,7 @@
 oracle's own quantization of the same fp32 rows).
 
 Bar: max|gpu - oracle| / max|oracle| <= 1e-3 over the outputs of one call
-(per layer), the decode tolerance of the workload statement.  Covered: all
+(per layer), the decode tolerance.  Covered: all
 9 codec pairs, head_dim 64/128/256, GQA 1..16, lengths 0, 1, ragged tails and
 several tiles, split-count sweeps, softmax invariants, and the five workload
 configurations at full size (sampled q-heads where the oracle would be slow).
@@ -176,8 +176,7 @@ def test_graph_replay_matches_eager(gpu):
 
 # ---- the five workload configurations at full size ------------------------------
 
-def _full_config(gpu, cid, layer_idx=0, heads_per_seq=None, append_last=False):
-    cfg = workloads.CONFIGS[cid]
+def _full_workload(gpu, cfg, layer_idx=0, heads_per_seq=None, append_last=False):
     kc, vc = cfg.layers[layer_idx]
     lens = workloads.seq_lengths(cfg, "cpu").tolist()
     layer = Layer.create(kc, vc, cfg.head_dim, cfg.n_kv_heads, cfg.n_seqs, cfg.capacity, device=gpu)
@@ -206,26 +205,26 @@ def _full_config(gpu, cid, layer_idx=0, heads_per_seq=None, append_last=False):
             heads = list(range(g * G, (g + 1) * G))
             ref = _oracle_decode(kc, vc, qn[s][heads], kh, vh, n, cfg.scale)
             worst = max(worst, rel_err(out[s][heads], ref))
-    assert worst <= TOL, (cid, layer_idx, worst)
+    assert worst <= TOL, (cfg.name, layer_idx, worst)
     return worst
 
 
-def test_config1_tiny_full(gpu):
-    _full_config(gpu, 1)
+def test_tiny_decode_full(gpu):
+    _full_workload(gpu, workloads.TINY)
 
 
-def test_config2_decode_32k_full(gpu):
-    _full_config(gpu, 2, heads_per_seq=lambda s: [0, 3, 7])
+def test_decode_32k_full(gpu):
+    _full_workload(gpu, workloads.DECODE_32K, heads_per_seq=lambda s: [0, 3, 7])
 
 
-def test_config3_decode_64k_with_append(gpu):
-    _full_config(gpu, 3, heads_per_seq=lambda s: [0, 3], append_last=True)
+def test_decode_64k_with_append(gpu):
+    _full_workload(gpu, workloads.DECODE_64K, heads_per_seq=lambda s: [0, 3], append_last=True)
 
 
 @pytest.mark.parametrize("layer_idx", [0, 1])
-def test_config4_decode_196k_split_kv(gpu, layer_idx):
-    _full_config(gpu, 4, layer_idx=layer_idx, heads_per_seq=lambda s: [layer_idx + 1])
+def test_decode_196k_split_kv(gpu, layer_idx):
+    _full_workload(gpu, workloads.DECODE_196K, layer_idx=layer_idx, heads_per_seq=lambda s: [layer_idx + 1])
 
 
-def test_config5_batched_decode(gpu):
-    _full_config(gpu, 5, heads_per_seq=lambda s: [s % 8])
+def test_batched_decode_16_sequences(gpu):
+    _full_workload(gpu, workloads.BATCHED, heads_per_seq=lambda s: [s % 8])

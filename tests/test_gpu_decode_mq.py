@@ -99,7 +99,7 @@ def test_one_query_matches_plain_decode_bitwise(gpu):
 def test_workload_64k_two_queries_sampled(gpu):
     """The 64K-context Q4_G64 decode with two drafted tokens per step: append
     both rows, attend from both, check 6 sampled q-heads of each query."""
-    cfg = workloads.CONFIGS[3]
+    cfg = workloads.DECODE_64K
     n, H, d, hq = cfg.ctx, cfg.n_kv_heads, cfg.head_dim, cfg.n_q_heads
     kc, vc = cfg.layers[0]
     layer = Layer.create(kc, vc, d, H, 1, cfg.capacity, device=gpu)

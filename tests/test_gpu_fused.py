@@ -155,7 +155,7 @@ def test_new_row_deep_in_a_long_split(gpu, kc, vc, d):
 def test_workload_64k_step_matches_unfused(gpu):
     """The 64K-context Q4_G64 decode step: one fused call against kvq_append +
     kvq_attend_decode on a copy of the same cache."""
-    cfg = workloads.CONFIGS[3]
+    cfg = workloads.DECODE_64K
     n, H, d = cfg.ctx, cfg.n_kv_heads, cfg.head_dim
     kc, vc = cfg.layers[0]
     fused = Layer.create(kc, vc, d, H, 1, cfg.capacity, device=gpu)

@@ -184,7 +184,7 @@ def test_entry_outside_the_pool(gpu):
 def test_workload_64k_on_256_row_pages(gpu):
     """The 64K-context Q4_G64 step on 256 shuffled 256-row pages, fused,
     against the same step on contiguous planes."""
-    cfg = workloads.CONFIGS[3]
+    cfg = workloads.DECODE_64K
     n, H, d = cfg.ctx, cfg.n_kv_heads, cfg.head_dim
     kc, vc = cfg.layers[0]
     pl = _pool_for(kc, vc, d, H, 1, n // 256, 256, gpu, seed=64)

@@ -1,9 +1,8 @@
 """GPU chunked-prefill parity against the oracle (binary64 causal attention over
 the oracle's own quantization of the same rows; bf16 queries widened exactly).
 
-Bar: max|gpu - oracle| / max|oracle| <= 1e-2, the prefill tolerance of the
-workload statement (the matrix cores see K_hat, V_hat, the scaled query and P
-rounded to binary16).
+Bar: max|gpu - oracle| / max|oracle| <= 1e-2, the prefill tolerance (the
+matrix cores see K_hat, V_hat, the scaled query and P rounded to binary16).
 Covered: the tiny prefill enumerated in full, ragged prefix/chunk lengths,
 every codec pair, head_dim 64/128/256, several GQA ratios, a chunk at
 position 0, queries far outside the binary16 range, the chunk of a middle sequence of a three-sequence

@@ -4,7 +4,8 @@ What fixes the expected values (none of it is the oracle itself):
   * hand-worked blocks in tests/golden/quant_blocks.txt, each derived by hand
     from the codec definitions (den_llama.cpp, section "What this fork is":
     Q4_G64 = signed INT4 + one FP16 scale per 64 values, 4.25 bits/value;
-    the workload statement for q8_0 / q4_0);
+    q8_0 / q4_0, named on the same page, take the same rule at 32 values per
+    group);
   * the 4.25 / 4.5 / 8.5 bits-per-value size arithmetic;
   * brute force: the stored scale is the binary16 nearest to amax/Qmax (searched
     over all 65536 patterns) and every code is the integer in range nearest to

@@ -8,20 +8,20 @@ Workload recipe (den_llama.cpp serves a 27B model at 32K / 65K / 196K context
 with a q8_0 K / q4_0 V cache and 2048-token micro-batches, "Results" and
 "Quick start"; Q4_G64 and layer-wise split KV in "What this fork is").  Real
 K/V activations are replaced by:
-  1 tiny      : 1 seq, 4 q-heads / 1 kv-head, d 64, ctx 256, N(0,1); K q8_0, V Q4_G64, scale 1/8
-  2 decode32k : 1 seq, 32/8, d 128, ctx 32768; N(0,1) with 10 of the 1024
+  TINY        : 1 seq, 4 q-heads / 1 kv-head, d 64, ctx 256, N(0,1); K q8_0, V Q4_G64, scale 1/8
+  DECODE_32K  : 1 seq, 32/8, d 128, ctx 32768; N(0,1) with 10 of the 1024
                 (kv-head, channel) pairs x8 on every row (1% outlier channels),
                 drawn separately for K and V; K q8_0, V q4_0
-  3 decode64k : 1 seq, 24/4, d 256, ctx 65536; N(0,1) * s[h,c], s = exp(U[ln 1/4, ln 4])
+  DECODE_64K  : 1 seq, 24/4, d 256, ctx 65536; N(0,1) * s[h,c], s = exp(U[ln 1/4, ln 4])
                 per (kv-head, channel), independent for K and V; Q4_G64 / Q4_G64;
                 65535 rows pre-filled, the step appends row 65535 and attends 65536
-  4 decode196k: 1 seq, 24/4, d 256, ctx 196608, 4 layers; layer 0 q8_0/q8_0,
+  DECODE_196K : 1 seq, 24/4, d 256, ctx 196608, 4 layers; layer 0 q8_0/q8_0,
                 layers 1-3 Q4_G64/Q4_G64; N(0,1)
-  5 batched   : 16 seqs, 32/8, d 128, lengths U{4096..131072}; N(0,1); K q8_0, V q4_0
-  5 prefill   : 1 seq, 32/8, d 128, prefix 32768 + chunk 2048; Q bf16(N(0,1)),
+  BATCHED     : 16 seqs, 32/8, d 128, lengths U{4096..131072}; N(0,1); K q8_0, V q4_0
+  PREFILL     : 1 seq, 32/8, d 128, prefix 32768 + chunk 2048; Q bf16(N(0,1)),
                 K/V N(0,1) fp32; K q8_0, V q4_0
-Every tensor comes from its own torch.Generator seeded from (config, layer,
-stream), so any piece can be regenerated alone on any device.
+Every tensor comes from its own torch.Generator seeded from (the workload's
+seed id, layer, stream), so any piece can be regenerated alone on any device.
 """
 from __future__ import annotations
 
@@ -33,7 +33,7 @@ import torch
 
 @dataclass(frozen=True)
 class Config:
-    cid: int
+    seed_id: int              # first component of every generator seed
     name: str
     n_seqs: int
     n_q_heads: int
@@ -59,27 +59,26 @@ class Config:
         return (self.ctx + 31) // 32 * 32
 
 
-CONFIGS = {
-    1: Config(1, "tiny_decode_ctx256", 1, 4, 1, 64, 256, (("q8_0", "q4_g64"),)),
-    2: Config(2, "decode_ctx32k_q8_0k_q4_0v", 1, 32, 8, 128, 32768, (("q8_0", "q4_0"),),
-              structure="outliers"),
-    3: Config(3, "decode_ctx64k_q4g64", 1, 24, 4, 256, 65536, (("q4_g64", "q4_g64"),),
-              structure="channel_scale", append_step=True),
-    4: Config(4, "decode_ctx196k_split_kv_4layers", 1, 24, 4, 256, 196608,
-              (("q8_0", "q8_0"), ("q4_g64", "q4_g64"), ("q4_g64", "q4_g64"), ("q4_g64", "q4_g64"))),
-    5: Config(5, "batched_decode_16seq_4k_128k", 16, 32, 8, 128, 131072, (("q8_0", "q4_0"),),
-              batched_lengths=True),
-}
-PREFILL = dict(cid=5, n_q_heads=32, n_kv_heads=8, head_dim=128, prefix=32768, chunk=2048,
+TINY = Config(1, "tiny_decode_ctx256", 1, 4, 1, 64, 256, (("q8_0", "q4_g64"),))
+DECODE_32K = Config(2, "decode_ctx32k_q8_0k_q4_0v", 1, 32, 8, 128, 32768, (("q8_0", "q4_0"),),
+                    structure="outliers")
+DECODE_64K = Config(3, "decode_ctx64k_q4g64", 1, 24, 4, 256, 65536, (("q4_g64", "q4_g64"),),
+                    structure="channel_scale", append_step=True)
+DECODE_196K = Config(4, "decode_ctx196k_split_kv_4layers", 1, 24, 4, 256, 196608,
+                     (("q8_0", "q8_0"), ("q4_g64", "q4_g64"), ("q4_g64", "q4_g64"), ("q4_g64", "q4_g64")))
+BATCHED = Config(5, "batched_decode_16seq_4k_128k", 16, 32, 8, 128, 131072, (("q8_0", "q4_0"),),
+                 batched_lengths=True)
+CONFIGS = {c.name: c for c in (TINY, DECODE_32K, DECODE_64K, DECODE_196K, BATCHED)}
+PREFILL = dict(n_q_heads=32, n_kv_heads=8, head_dim=128, prefix=32768, chunk=2048,
                k_codec="q8_0", v_codec="q4_0")
 
-# stream ids inside a config
+# stream ids inside a workload
 _Q, _K, _V, _AUX, _LEN, _QP = 1, 2, 3, 4, 5, 6
 
 
-def _gen(device, cid, layer, stream, seq=0):
+def _gen(device, seed_id, layer, stream, seq=0):
     g = torch.Generator(device=device)
-    g.manual_seed(((cid * 131 + layer) * 1009 + stream) * 65537 + seq)
+    g.manual_seed(((seed_id * 131 + layer) * 1009 + stream) * 65537 + seq)
     return g
 
 
@@ -87,20 +86,20 @@ def seq_lengths(cfg: Config, device="cpu") -> torch.Tensor:
     """int64 [n_seqs] attended lengths."""
     if not cfg.batched_lengths:
         return torch.full((cfg.n_seqs,), cfg.ctx, dtype=torch.int64, device=device)
-    g = _gen("cpu", cfg.cid, 0, _LEN)
+    g = _gen("cpu", cfg.seed_id, 0, _LEN)
     lens = torch.randint(4096, 131072 + 1, (cfg.n_seqs,), generator=g, dtype=torch.int64)
     return lens.to(device)
 
 
 def queries(cfg: Config, layer: int, device) -> torch.Tensor:
     """fp32 [n_seqs][n_q_heads][head_dim] ~ N(0, 1)."""
-    g = _gen(device, cfg.cid, layer, _Q)
+    g = _gen(device, cfg.seed_id, layer, _Q)
     return torch.randn(cfg.n_seqs, cfg.n_q_heads, cfg.head_dim, generator=g, device=device)
 
 
 def _structure(cfg: Config, layer: int, which: int, device) -> torch.Tensor | None:
     """Per-(kv-head, channel) multiplier [n_kv_heads][head_dim] or None."""
-    g = _gen("cpu", cfg.cid, layer, _AUX * 10 + which)
+    g = _gen("cpu", cfg.seed_id, layer, _AUX * 10 + which)
     H, d = cfg.n_kv_heads, cfg.head_dim
     if cfg.structure == "outliers":
         n = max(1, round(0.01 * H * d))
@@ -126,7 +125,7 @@ def kv_rows(cfg: Config, layer: int, seq: int, which: str, row0: int, n_rows: in
     CH = 4096
     c0, c1 = row0 // CH, (row0 + n_rows - 1) // CH if n_rows > 0 else row0 // CH - 1
     for ch in range(c0, c1 + 1):
-        g = _gen(device, cfg.cid, layer, _K if w == 0 else _V, seq * 100003 + ch)
+        g = _gen(device, cfg.seed_id, layer, _K if w == 0 else _V, seq * 100003 + ch)
         blk = torch.randn(CH, H, d, generator=g, device=device)
         a, b = max(row0, ch * CH), min(row0 + n_rows, (ch + 1) * CH)
         out[a - row0:b - row0] = blk[a - ch * CH:b - ch * CH]
