@@ -277,7 +277,7 @@ def main():
         print(json.dumps(run_prefill(torch, torch.device("cuda:0"), args)), flush=True)
         return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build has no "
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the library has no "
               "multi-GPU path", file=sys.stderr)
         sys.exit(2)
     import numpy as np
