@@ -3,7 +3,7 @@ against the oracle (den_llama.cpp, "Results": quantizer byte-identical to the
 CPU reference, dequant bit-identical), on every codec, both plane roles and
 head_dim 64/128/256, with inputs that stress every rounding path; whole
 aligned 32-row blocks (written word by word) beside scattered rows in one
-call."""
+call; one plane at a time (the other input absent)."""
 import numpy as np
 import pytest
 import torch
@@ -120,6 +120,31 @@ def test_append_overwrites_rows(gpu, codec):
             wc, ws = oracle.quantize_rows(codec, x)
             assert np.array_equal(codes[0].transpose(1, 0, 2), wc)
             assert np.array_equal(scales[0].transpose(1, 0, 2), ws)
+
+
+@pytest.mark.parametrize("kc,vc,d", [("q8_0", "q4_0", 128), ("q4_g64", "q4_g64", 256)])
+def test_append_one_plane_at_a_time(gpu, kc, vc, d):
+    # k only, then v only (a whole aligned block and a ragged tail of 9 rows):
+    # the plane without input is left as it was
+    rng = np.random.default_rng(d + 3)
+    H, cap = 2, 64
+    n = 41
+    pos = np.arange(n, dtype=np.int64)
+    seq = np.zeros(n, np.int32)
+    xk = _stress_rows(rng, n, H, d, kc)
+    xv = _stress_rows(rng, n, H, d, vc)
+    layer = Layer.create(kc, vc, d, H, 1, cap, device=gpu)
+    sq, ps = torch.from_numpy(seq).to(gpu), torch.from_numpy(pos).to(gpu)
+    kvq_append(layer, torch.from_numpy(xk).to(gpu), None, sq, ps)
+    codes_v, scales_v = layout.plane_to_rows(layer.v)
+    assert not codes_v.any() and not scales_v.any()
+    kvq_append(layer, None, torch.from_numpy(xv).to(gpu), sq, ps)
+    for plane, x, codec in ((layer.k, xk, kc), (layer.v, xv, vc)):
+        codes, scales = layout.plane_to_rows(plane)
+        want_c, want_s = oracle.quantize_rows(codec, x)
+        assert np.array_equal(codes[seq, :, pos], want_c), codec
+        assert np.array_equal(scales[seq, :, pos], want_s), codec
+        assert not codes[0, :, n:].any() and not scales[0, :, n:].any()
 
 
 def test_append_out_of_range_positions_flagged(gpu):
