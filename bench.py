@@ -46,7 +46,6 @@ def _args():
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-quality", action="store_true")
     p.add_argument("--no-baselines", action="store_true")
-    p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--step-only", action="store_true",
                    help="time only the headline step (no two-call step, attention-only, multi-query, "
                         "baseline, prefill, quality or CPU legs): the run that profiles and counters use")
@@ -57,22 +56,35 @@ def _args():
                    help="summarize a rocprofv3 counter pass (KERNEL = prefill or decode) into profiles/ and exit")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run plain 256 MiB device copies (HBM counter calibration)")
-    p.add_argument("--write-traffic-summary", metavar="PMC_DIR",
-                   help="summarize rocprofv3 FETCH_SIZE/WRITE_SIZE runs (PMC_DIR/{fetch,write,cfetch,cwrite}) "
-                        "into " + os.path.relpath(TRAFFIC_FILE, ROOT) + " and exit")
+    p.add_argument("--write-traffic-summary", nargs=2, metavar=("KERNEL", "PMC_DIR"),
+                   help="summarize rocprofv3 FETCH_SIZE/WRITE_SIZE runs (PMC_DIR/{fetch,write,cfetch,cwrite}) of "
+                        "KERNEL (decode or prefill) into profiles/ and exit")
     return p.parse_args()
 
 
-# ---- counter-backed HBM traffic of kvq_attend_decode ------------------------
+# ---- counter-backed HBM traffic ---------------------------------------------
 # rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) over this benchmark gives KiB
-# per dispatch of decode_kernel and combine_kernel; the same counters over
-# --calibrate-copy (exactly 256 MiB read and 256 MiB written per dispatch)
-# give the scale factors.  The summary records a hash of the decode sources
-# and is used only while they are unchanged.
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode64k_q4g64_traffic.txt")
+# per dispatch of a kernel; the same counters over --calibrate-copy (exactly
+# 256 MiB read and 256 MiB written per dispatch) give the scale factors.  A
+# summary records a hash of the kernel's sources and is used only while they
+# are unchanged.
 DECODE_SOURCES = ["block_quantized_kv_amd/csrc/attn_decode.hip", "block_quantized_kv_amd/csrc/kvq_device.h",
                   "block_quantized_kv_amd/csrc/kvq_layout.h", "block_quantized_kv_amd/csrc/kvq_internal.h",
                   "block_quantized_kv_amd/csrc/kvq_quant.h"]
+PREFILL_SOURCES = ["block_quantized_kv_amd/csrc/attn_prefill.hip", "block_quantized_kv_amd/csrc/kvq_device.h",
+                   "block_quantized_kv_amd/csrc/kvq_layout.h", "block_quantized_kv_amd/csrc/kvq_internal.h"]
+TRAFFIC = {
+    # which: (summary file, kernels of one launch, sources, profiled command, what one launch is)
+    "decode": (os.path.join(ROOT, "profiles", "decode64k_q4g64_traffic.txt"), ["decode_kernel", "combine_kernel"],
+               DECODE_SOURCES, "python -u bench.py --steps 32 --warmup 8 --step-only",
+               "one decode step, kvq_append_attend_decode, 64K-context Q4_G64 decode (1 seq, 24/4 heads, "
+               "head_dim 256)"),
+    "prefill": (os.path.join(ROOT, "profiles", "prefill2k_over32k_traffic.txt"), ["prefill_kernel"],
+                PREFILL_SOURCES, "python -u bench.py --prefill-only",
+                "one kvq_attend_prefill call, 2048-token chunk over a 32768-row prefix (q8_0 K / q4_0 V, 32/8 "
+                "heads, head_dim 128)"),
+}
+TRAFFIC_FILE = TRAFFIC["decode"][0]
 
 
 def source_hash(sources) -> str:
@@ -100,37 +112,38 @@ def _pmc_mean(path_glob: str, counter: str, name_pat: str):
     return (sum(vals) / len(vals), len(vals)) if vals else (None, 0)
 
 
-def write_traffic_summary(pmc_dir: str):
+def write_traffic_summary(which: str, pmc_dir: str):
+    path, kernels, sources, cmd, what = TRAFFIC[which]
     g = lambda sub: os.path.join(pmc_dir, sub, "*_counter_collection.csv")
-    f_dec, n1 = _pmc_mean(g("fetch"), "FETCH_SIZE", "decode_kernel")
-    f_cmb, _ = _pmc_mean(g("fetch"), "FETCH_SIZE", "combine_kernel")
-    w_dec, n2 = _pmc_mean(g("write"), "WRITE_SIZE", "decode_kernel")
-    w_cmb, _ = _pmc_mean(g("write"), "WRITE_SIZE", "combine_kernel")
+    fetch, write, n = {}, {}, []
+    for kn in kernels:
+        fetch[kn], n1 = _pmc_mean(g("fetch"), "FETCH_SIZE", kn)
+        write[kn], n2 = _pmc_mean(g("write"), "WRITE_SIZE", kn)
+        n.append((n1, n2))
     f_cal, _ = _pmc_mean(g("cfetch"), "FETCH_SIZE", "copy")
     w_cal, _ = _pmc_mean(g("cwrite"), "WRITE_SIZE", "copy")
-    if None in (f_dec, f_cmb, w_dec, w_cmb, f_cal, w_cal):
+    if None in list(fetch.values()) + list(write.values()) + [f_cal, w_cal]:
         sys.exit("missing counter runs under " + pmc_dir)
     kib256 = 256 * 1024  # KiB in 256 MiB
     ff, fw = kib256 / f_cal, kib256 / w_cal
-    fetch_b = (f_dec + f_cmb) * ff * 1024
-    write_b = (w_dec + w_cmb) * fw * 1024
+    fetch_b = sum(fetch.values()) * ff * 1024
+    write_b = sum(write.values()) * fw * 1024
+    regex = "|".join(kernels)
     lines = [
-        "# HBM traffic of one decode step, kvq_append_attend_decode (decode_kernel + combine_kernel),",
-        "# 64K-context Q4_G64 decode (1 seq, 24/4 heads, head_dim 256), from rocprofv3 counters",
+        f"# HBM traffic of {what} ({' + '.join(kernels)}), from rocprofv3 counters",
         "#",
         "# commands (on the GPU machine, from the repo root; one counter per run):",
-        "#   rocprofv3 --pmc FETCH_SIZE --kernel-include-regex 'decode_kernel|combine_kernel' -d <dir>/fetch -o fetch "
-        "--output-format csv -- python -u bench.py --steps 32 --warmup 8 --step-only",
-        "#   rocprofv3 --pmc WRITE_SIZE (same, -d <dir>/write)",
+        f"#   rocprofv3 --pmc FETCH_SIZE --kernel-include-regex '{regex}' -d <dir>/fetch -o fetch "
+        f"--output-format csv -- {cmd}",
+        "#   rocprofv3 --pmc WRITE_SIZE (same, -d <dir>/write -o write)",
         "#   rocprofv3 --pmc FETCH_SIZE -d <dir>/cfetch -o cfetch --output-format csv -- python -u bench.py --calibrate-copy",
-        "#   rocprofv3 --pmc WRITE_SIZE -d <dir>/cwrite ... -- python -u bench.py --calibrate-copy",
-        "#   python bench.py --write-traffic-summary <dir>",
-        f"decode_source_hash: {decode_source_hash()}",
-        f"dispatches: {n1} {n2}",
-        f"fetch_kib_decode: {f_dec:.1f}",
-        f"fetch_kib_combine: {f_cmb:.1f}",
-        f"write_kib_decode: {w_dec:.1f}",
-        f"write_kib_combine: {w_cmb:.1f}",
+        "#   rocprofv3 --pmc WRITE_SIZE -d <dir>/cwrite -o cwrite --output-format csv -- python -u bench.py "
+        "--calibrate-copy",
+        f"#   python bench.py --write-traffic-summary {which} <dir>",
+        f"source_hash: {source_hash(sources)}",
+        f"dispatches: {' '.join(f'{a} {b}' for a, b in n)}",
+    ] + [f"fetch_kib_{kn}: {fetch[kn]:.1f}" for kn in kernels] + \
+        [f"write_kib_{kn}: {write[kn]:.1f}" for kn in kernels] + [
         f"copy_fetch_kib_per_256MiB: {f_cal:.1f}",
         f"copy_write_kib_per_256MiB: {w_cal:.1f}",
         f"fetch_scale: {ff:.4f}",
@@ -139,22 +152,23 @@ def write_traffic_summary(pmc_dir: str):
         f"fetch_bytes_per_launch: {fetch_b:.0f}",
         f"write_bytes_per_launch: {write_b:.0f}",
     ]
-    with open(TRAFFIC_FILE, "w") as fh:
+    with open(path, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
 
-def read_traffic():
-    """Counter-backed bytes per kvq_attend_decode launch, or None when the
-    summary is missing or was taken on other decode sources."""
+def read_traffic(which: str = "decode"):
+    """Counter-backed HBM bytes per launch of a kernel, or None when the
+    summary is missing or was taken on other sources."""
+    path, _, sources, _, _ = TRAFFIC[which]
     try:
         kv = {}
-        with open(TRAFFIC_FILE) as fh:
+        with open(path) as fh:
             for line in fh:
                 if ":" in line and not line.startswith("#"):
                     k, v = line.split(":", 1)
                     kv[k.strip()] = v.strip()
-        if kv.get("decode_source_hash") != decode_source_hash():
+        if kv.get("source_hash") != source_hash(sources):
             return None
         return float(kv["traffic_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
@@ -171,8 +185,6 @@ def read_traffic():
 BUSY_COUNTERS = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA",
                  "SQ_INSTS_LDS", "SQ_WAVES", "GRBM_GUI_ACTIVE"]
 N_SIMDS, N_XCDS = 1024, 8
-PREFILL_SOURCES = ["block_quantized_kv_amd/csrc/attn_prefill.hip", "block_quantized_kv_amd/csrc/kvq_device.h",
-                   "block_quantized_kv_amd/csrc/kvq_layout.h", "block_quantized_kv_amd/csrc/kvq_internal.h"]
 BUSY_FILES = {
     "prefill": (os.path.join(ROOT, "profiles", "prefill2k_over32k_counters.txt"), "prefill_kernel", PREFILL_SOURCES,
                 "python -u bench.py --prefill-only"),
@@ -259,13 +271,56 @@ def decode_bytes(cfg) -> dict:
             "fused_kernel": kv + cfg.n_seqs * cfg.n_q_heads * d * 4 + app}
 
 
+def headline_setup(torch, dev, rotate: int, keep_host: bool = False):
+    """The timed step of the headline workload, built exactly as the benchmark
+    times it (the parity tests build it through this function too):
+    the 64K-context Q4_G64 cache (24/4 heads, d 256) holds rows 0..65534,
+    appended in 16384-row kvq_append calls; `rotate` copies of it are made
+    (so timed loops can defeat the last-level cache); step(i, stream) is one
+    kvq_append_attend_decode call on copy i % rotate that appends row 65535
+    (k_new, v_new) and attends from the query over all 65536 rows, with the
+    workspace sized by decode_workspace for that call."""
+    import types
+
+    import workloads
+    from block_quantized_kv_amd import Layer, decode_workspace, kvq_append, kvq_append_attend_decode
+    cfg = workloads.DECODE_64K
+    kc, vc = cfg.layers[0]
+    n, H, d = cfg.ctx, cfg.n_kv_heads, cfg.head_dim
+    # ---- setup (untimed): fill rows 0..n-2, keep row n-1 as the step's new token
+    base = Layer.create(kc, vc, d, H, 1, cfg.capacity, device=dev)
+    k = workloads.kv_rows(cfg, 0, 0, "k", 0, n, dev)
+    v = workloads.kv_rows(cfg, 0, 0, "v", 0, n, dev)
+    for a in range(0, n - 1, 16384):
+        b = min(n - 1, a + 16384)
+        kvq_append(base, k[a:b].contiguous(), v[a:b].contiguous(),
+                   torch.zeros(b - a, dtype=torch.int32, device=dev),
+                   torch.arange(a, b, dtype=torch.int64, device=dev))
+    k_new, v_new = k[n - 1:n].contiguous(), v[n - 1:n].contiguous()
+    k_new2, v_new2 = k[n - 2:n].contiguous(), v[n - 2:n].contiguous()  # two drafted tokens
+    host_kv = (k.cpu().numpy(), v.cpu().numpy()) if keep_host else None
+    del k, v
+    caches = [base] + [base.clone() for _ in range(rotate - 1)]
+    q = workloads.queries(cfg, 0, dev)
+    seq_len = torch.tensor([n], dtype=torch.int64, device=dev)
+    ws = decode_workspace(base, cfg.n_q_heads, 1, n)
+    out = torch.empty_like(q)
+
+    def step(i, st=None):
+        kvq_append_attend_decode(caches[i % rotate], k_new, v_new, q, seq_len, n, cfg.scale, out=out,
+                                 workspace=ws, stream=st)
+
+    return types.SimpleNamespace(cfg=cfg, base=base, caches=caches, k_new=k_new, v_new=v_new, k_new2=k_new2,
+                                 v_new2=v_new2, host_kv=host_kv, q=q, seq_len=seq_len, ws=ws, out=out, step=step)
+
+
 def main():
     args = _args()
     if args.calibrate_copy:
         calibrate_copy()
         return
     if args.write_traffic_summary:
-        write_traffic_summary(args.write_traffic_summary)
+        write_traffic_summary(*args.write_traffic_summary)
         return
     if args.write_busy_summary:
         write_busy_summary(*args.write_busy_summary)
@@ -286,39 +341,18 @@ def main():
     if args.step_only:
         args.no_cpu_baseline = args.no_baselines = args.no_prefill = args.no_quality = True
     import workloads
-    from block_quantized_kv_amd import (Layer, decode_workspace, kvq_append, kvq_append_attend_decode,
-                                        kvq_attend_decode, load_library)
+    from block_quantized_kv_amd import kvq_append, kvq_attend_decode, load_library
     load_library()
     dev = torch.device("cuda:0")
-    cfg = workloads.DECODE_64K
+    hs = headline_setup(torch, dev, ROTATE)
+    cfg, base, caches, q, seq_len, ws, out = hs.cfg, hs.base, hs.caches, hs.q, hs.seq_len, hs.ws, hs.out
+    k_new, v_new, k_new2, v_new2 = hs.k_new, hs.v_new, hs.k_new2, hs.v_new2
     kc, vc = cfg.layers[0]
     n, H, d = cfg.ctx, cfg.n_kv_heads, cfg.head_dim
-
-    # ---- setup (untimed): fill rows 0..n-2, keep row n-1 as the step's new token
-    base = Layer.create(kc, vc, d, H, 1, cfg.capacity, device=dev)
-    k = workloads.kv_rows(cfg, 0, 0, "k", 0, n, dev)
-    v = workloads.kv_rows(cfg, 0, 0, "v", 0, n, dev)
-    for a in range(0, n - 1, 16384):
-        b = min(n - 1, a + 16384)
-        kvq_append(base, k[a:b].contiguous(), v[a:b].contiguous(),
-                   torch.zeros(b - a, dtype=torch.int32, device=dev),
-                   torch.arange(a, b, dtype=torch.int64, device=dev))
-    k_new, v_new = k[n - 1:n].contiguous(), v[n - 1:n].contiguous()
-    k_new2, v_new2 = k[n - 2:n].contiguous(), v[n - 2:n].contiguous()  # two drafted tokens
-    host_kv = (k.cpu().numpy(), v.cpu().numpy()) if not args.no_cpu_baseline else None
-    del k, v
-    caches = [base] + [base.clone() for _ in range(ROTATE - 1)]
-    q = workloads.queries(cfg, 0, dev)
-    seq_len = torch.tensor([n], dtype=torch.int64, device=dev)
     new_seq = torch.zeros(1, dtype=torch.int32, device=dev)
     new_pos = torch.tensor([n - 1], dtype=torch.int64, device=dev)
-    ws = decode_workspace(base, cfg.n_q_heads, 1, n)
-    out = torch.empty_like(q)
     stream = torch.cuda.current_stream()
-
-    def step(i, st=stream):
-        kvq_append_attend_decode(caches[i % ROTATE], k_new, v_new, q, seq_len, n, cfg.scale, out=out,
-                                 workspace=ws, stream=st)
+    step = hs.step
 
     def step_unfused(i, st=stream):
         L = caches[i % ROTATE]
@@ -421,7 +455,7 @@ def main():
         u1.record()
         torch.cuda.synchronize()
         attend_only_ms = round(u0.elapsed_time(u1) / (reps * ROTATE), 5)
-    traffic = read_traffic()
+    traffic = read_traffic("decode")
     # the graph timing repeated 5 times (medians are steadier than one run)
     reps5 = []
     for _ in range(5):
@@ -489,8 +523,23 @@ def main():
     if not args.no_quality:
         result["quality"] = run_quality(torch, dev, args)
 
-    if host_kv is not None:
-        result["cpu_baseline"] = cpu_baseline(cfg, host_kv, q.cpu().numpy(), nb, args.cpu_seconds)
+    if not args.no_cpu_baseline:
+        cb = cpu_baselines(torch, dev)
+        per = cb["per_config"]
+        h = per[cfg.name]
+        result["cpu_baseline"] = {
+            "value": h["value"], "unit": "GB/s", "cores": cb["threads"], "kind": "oracle",
+            "sample": f"the whole 64K-context step (dequantize all 65536 rows of the 4 kv-heads, binary64 "
+                      f"attention of all 24 q-heads) on {cb['threads']} threads, {h['seconds']} s",
+            "single_thread": h.get("single_thread"), "cpu_model": cb["cpu_model"], "nproc": cb["nproc"],
+            "per_config": per}
+        # the oracle beside each GPU figure
+        for leg, name in (("decode_32k", workloads.DECODE_32K.name), ("long_context", workloads.DECODE_196K.name),
+                          ("batched_decode", workloads.BATCHED.name)):
+            if leg in result:
+                result[leg]["cpu_oracle"] = per[name]
+        if "prefill" in result:
+            result["prefill"]["cpu_oracle"] = per["prefill_2048_over_32768"]
     print(json.dumps(result), flush=True)
 
 
@@ -499,7 +548,7 @@ def stream_peak(torch, dev, reps: int = 48) -> dict:
     rotating through 1 GiB (so the 256 MB last-level cache cannot serve them),
     for 256, 512 and 1024 workgroups of 8 waves; the best is the practical
     ceiling the decode roofline is also quoted against."""
-    from block_quantized_kv_amd import kvq_probe_stream_read
+    from block_quantized_kv_amd.probe import kvq_probe_stream_read
     win, total = 64 << 20, 1 << 30
     buf = torch.ones(total, dtype=torch.uint8, device=dev)
     sink = torch.zeros(1, dtype=torch.int32, device=dev)
@@ -758,6 +807,9 @@ def run_prefill(torch, dev, args):
     torch.cuda.synchronize()
     ms = a_ev.elapsed_time(b_ev) / reps
     tf = flops / (ms * 1e-3) / 1e12
+    mp = mfma_peak(torch, dev)
+    kv_bytes = (P + T) * hkv * sum(r + 2 * (d // (64 if c == "q4_g64" else 32))
+                                   for r, c in ((d if kc == "q8_0" else d // 2, kc), (d if vc == "q8_0" else d // 2, vc)))
     return {"metric": "prefill TFLOP/s", "value": round(tf, 2), "unit": "TFLOP/s",
             "ms_per_chunk": round(ms, 4), "flop": flops,
             "chunk_append": {"ms": round(append_ms, 4), "bytes_in": append_in, "bytes_out": append_out,
@@ -766,8 +818,33 @@ def run_prefill(torch, dev, args):
             "config": {"prefix": P, "chunk": T, "n_q_heads": hq, "n_kv_heads": hkv, "head_dim": d,
                        "k_codec": kc, "v_codec": vc},
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                         "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
+                         "traffic": read_traffic("prefill"), "kv_bytes": kv_bytes,
+                         "onbox_mfma_peak": mp, "frac_of_onbox_peak": round(tf / mp["tflops"], 4),
                          "counters": read_busy("prefill")}}
+
+
+def mfma_peak(torch, dev) -> dict:
+    """On-box matrix-core peak: kvq_probe_mfma_f16 (a register-only loop of
+    v_mfma_f32_16x16x32_f16, the prefill kernel's product) for 256, 512 and
+    1024 workgroups of 8 waves; the best is the practical ceiling the prefill
+    roofline is also quoted against."""
+    from block_quantized_kv_amd.probe import kvq_probe_mfma_f16
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    by = {}
+    for nwg in (256, 512, 1024):
+        iters = 4096 * 256 // nwg
+        kvq_probe_mfma_f16(nwg, iters, sink)
+        torch.cuda.synchronize()
+        flop = 0.0
+        e0.record()
+        for _ in range(5):
+            flop += kvq_probe_mfma_f16(nwg, iters, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        by[str(nwg)] = round(flop / (e0.elapsed_time(e1) * 1e-3) / 1e12, 1)
+    return {"tflops": max(by.values()), "by_workgroups_of_8_waves": by, "instruction": "v_mfma_f32_16x16x32_f16"}
 
 
 def run_baselines(torch, dev, cfg, caches, q, seq_len, scale, steps):
@@ -872,38 +949,141 @@ def run_quality(torch, dev, args):
     return res
 
 
-def cpu_baseline(cfg, host_kv, q, nb, seconds):
-    """The CPU oracle (single-threaded C, binary64 attention) doing the same
-    decode step on the host: dequantize the cached rows of one KV head and
-    attend its 6 query heads; repeated over KV heads until ~`seconds`."""
+# ---- the CPU oracle beside every result ------------------------------------
+# The oracle is plain single-threaded C (oracle/kvq_oracle.c); its decode step
+# is "dequantize the cached rows, then binary64 attention".  Here it runs on
+# the host's cores with one task per (sequence, kv-head) dequantization and
+# one per (sequence, q-head) attention (ctypes releases the interpreter lock
+# during each call), and, for the three smallest configurations, on one
+# thread as well.  Quantizing the rows into the oracle's own codes is setup,
+# as filling the cache is for the GPU.
+
+CPU_THREADS_MAX = 16  # the host share of one GPU
+
+
+def cpu_info() -> dict:
+    model = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "nproc": os.cpu_count(),
+            "threads": max(1, min(CPU_THREADS_MAX, os.cpu_count() or 1))}
+
+
+def _oracle_codes(pool, codec, rows_nhd):
+    """rows fp32 [n][H][d] -> [(codes, scales)] per kv-head (setup, threaded)."""
     import numpy as np
 
     import oracle
-    kc, vc = cfg.layers[0]
-    k, v = host_kv
-    G = cfg.gqa
-    # the cache the oracle reads: its own codes of every row (setup, untimed)
-    codes = []
-    for g in range(cfg.n_kv_heads):
-        codes.append((oracle.quantize_rows(kc, np.ascontiguousarray(k[:, g])),
-                      oracle.quantize_rows(vc, np.ascontiguousarray(v[:, g]))))
-    done_heads = 0
-    t0 = time.perf_counter()
-    while True:
-        g = done_heads % cfg.n_kv_heads
-        (kc_, ks_), (vc_, vs_) = codes[g]
-        kh = oracle.dequant_rows(kc, kc_, ks_, cfg.head_dim)[None]
-        vh = oracle.dequant_rows(vc, vc_, vs_, cfg.head_dim)[None]
-        oracle.attend_decode(q[0][g * G:(g + 1) * G], kh, vh, cfg.ctx, cfg.scale)
-        done_heads += 1
-        if time.perf_counter() - t0 >= seconds:
-            break
-    el = time.perf_counter() - t0
-    bytes_done = nb["kv"] / cfg.n_kv_heads * done_heads
-    return {"value": round(bytes_done / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done_heads} kv-head passes (dequant + fp64 attention of {G} q-heads over "
-                      f"{cfg.ctx} rows each) of the 64K-context step, {el:.1f} s",
-            "cpu": platform.processor() or platform.machine(), "host_cores": os.cpu_count()}
+    H = rows_nhd.shape[1]
+    return list(pool.map(lambda g: oracle.quantize_rows(codec, np.ascontiguousarray(rows_nhd[:, g])), range(H)))
+
+
+def _oracle_decode_seq(pool, kc, vc, d, kcodes, vcodes, q_hd, n, scale):
+    """One sequence's oracle decode step: dequantize every kv-head's K and V
+    rows, then attend from every q-head (each a task of `pool`)."""
+    import oracle
+    H = len(kcodes)
+    G = q_hd.shape[0] // H
+    hats = list(pool.map(lambda g: (oracle.dequant_rows(kc, kcodes[g][0], kcodes[g][1], d)[None],
+                                    oracle.dequant_rows(vc, vcodes[g][0], vcodes[g][1], d)[None]), range(H)))
+    list(pool.map(lambda h: oracle.attend_decode(q_hd[h:h + 1], hats[h // G][0], hats[h // G][1], n, scale),
+                  range(q_hd.shape[0])))
+
+
+def cpu_decode_config(torch, dev, cfg, layers, threads, single_thread: bool) -> dict:
+    """The oracle's decode step of a whole configuration (every sequence, every
+    q-head of the given layers) on `threads` threads, and on one thread if
+    asked; value in GB/s of the same algorithmic bytes as the GPU figure."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+    import workloads
+    oracle._load()
+    d, H = cfg.head_dim, cfg.n_kv_heads
+    lens = [int(x) for x in workloads.seq_lengths(cfg, "cpu")]
+    kv_bytes = 0
+    t_mt = t_st = 0.0
+    with ThreadPoolExecutor(threads) as pool, ThreadPoolExecutor(1) as one:
+        for li in layers:
+            kc, vc = cfg.layers[li]
+            row = sum(r + 2 * (d // (64 if c == "q4_g64" else 32))
+                      for r, c in ((d if kc == "q8_0" else d // 2, kc), (d if vc == "q8_0" else d // 2, vc)))
+            q = workloads.queries(cfg, li, dev).cpu().numpy()
+            for b, n in enumerate(lens):
+                k = workloads.kv_rows(cfg, li, b, "k", 0, n, dev).cpu().numpy()
+                v = workloads.kv_rows(cfg, li, b, "v", 0, n, dev).cpu().numpy()
+                kcodes, vcodes = _oracle_codes(pool, kc, k), _oracle_codes(pool, vc, v)
+                del k, v
+                t0 = time.perf_counter()
+                _oracle_decode_seq(pool, kc, vc, d, kcodes, vcodes, q[b], n, cfg.scale)
+                t_mt += time.perf_counter() - t0
+                if single_thread:
+                    t0 = time.perf_counter()
+                    _oracle_decode_seq(one, kc, vc, d, kcodes, vcodes, q[b], n, cfg.scale)
+                    t_st += time.perf_counter() - t0
+                kv_bytes += n * H * row
+    r = {"value": round(kv_bytes / t_mt / 1e9, 4), "unit": "GB/s", "threads": threads, "seconds": round(t_mt, 3),
+         "kv_bytes": kv_bytes,
+         "sample": f"whole step: {len(lens)} sequence(s) x {cfg.n_q_heads} q-heads x {len(layers)} layer(s)"}
+    if single_thread:
+        r["single_thread"] = {"value": round(kv_bytes / t_st / 1e9, 4), "unit": "GB/s", "seconds": round(t_st, 3)}
+    return r
+
+
+def cpu_prefill(torch, dev, threads, n_rows: int = 1024) -> dict:
+    """The oracle's chunked prefill (2048 tokens over a 32768-row prefix, q8_0 K /
+    q4_0 V, 32/8 heads, d 128) on a sample of n_rows (token, head) rows spread
+    evenly over the chunk and the heads; value in GFLOP/s of the causal flop
+    count (4 d per (row, attended row)) of the sample."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import numpy as np
+
+    import oracle
+    import workloads
+    oracle._load()
+    W = workloads.PREFILL
+    P, T, hq, H, d = W["prefix"], W["chunk"], W["n_q_heads"], W["n_kv_heads"], W["head_dim"]
+    kc, vc = W["k_codec"], W["v_codec"]
+    q, k, v = workloads.prefill_inputs(dev)
+    qn, k, v = q.float().cpu().numpy(), k.cpu().numpy(), v.cpu().numpy()
+    idx = np.linspace(0, T * hq - 1, n_rows).astype(np.int64)
+    toks, heads = (idx // hq).astype(np.int32), (idx % hq).astype(np.int32)
+    flop = float(sum(4 * d * (P + int(t) + 1) for t in toks))
+    with ThreadPoolExecutor(threads) as pool:
+        kcodes, vcodes = _oracle_codes(pool, kc, k), _oracle_codes(pool, vc, v)
+        del k, v
+        t0 = time.perf_counter()
+        hats = list(pool.map(lambda g: (oracle.dequant_rows(kc, kcodes[g][0], kcodes[g][1], d),
+                                        oracle.dequant_rows(vc, vcodes[g][0], vcodes[g][1], d)), range(H)))
+        kh = np.stack([x[0] for x in hats])
+        vh = np.stack([x[1] for x in hats])
+        pieces = np.array_split(np.arange(n_rows), 4 * threads)
+        list(pool.map(lambda ix: oracle.attend_prefill(qn, kh, vh, P, 1.0 / np.sqrt(d), tokens=toks[ix],
+                                                       heads=heads[ix]), pieces))
+        el = time.perf_counter() - t0
+    return {"value": round(flop / el / 1e9, 3), "unit": "GFLOP/s", "threads": threads, "seconds": round(el, 3),
+            "flop": flop, "sample": f"{n_rows} of the {T * hq} (token, head) rows, evenly spaced"}
+
+
+def cpu_baselines(torch, dev) -> dict:
+    """The oracle beside every configuration (see the section comment)."""
+    import workloads
+    info = cpu_info()
+    th = info["threads"]
+    per = {}
+    for cfg, layers, st in ((workloads.TINY, [0], True), (workloads.DECODE_32K, [0], True),
+                            (workloads.DECODE_64K, [0], True), (workloads.DECODE_196K, [0, 1, 2, 3], False),
+                            (workloads.BATCHED, [0], False)):
+        per[cfg.name] = cpu_decode_config(torch, dev, cfg, layers, th, st)
+    per["prefill_2048_over_32768"] = cpu_prefill(torch, dev, th)
+    return dict(info, per_config=per)
 
 
 if __name__ == "__main__":

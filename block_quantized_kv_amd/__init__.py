@@ -26,7 +26,6 @@ from ._binding import (  # noqa: F401
     decode_mq_workspace,
     kvq_decode_mq_workspace_bytes,
     kvq_prefill_workspace_bytes,
-    kvq_probe_stream_read,
     kvq_paged_append,
     kvq_paged_attend_decode_mq,
     kvq_paged_append_attend_decode_mq,

@@ -73,7 +73,6 @@ def load_library():
         "kvq_prefill_workspace_bytes": (sz, [LY, i32, i32]),
         "kvq_attend_prefill": (i32, [LY, P, i32, i64, i32, i32, f32, P, P, sz, P]),
         "kvq_dequant": (i32, [PL, i32, i64, i64, P, P]),
-        "kvq_probe_stream_read": (i32, [P, sz, i32, P, P]),
         "kvq_paged_append": (i32, [PG, P, P, P, P, i32, P, P]),
         "kvq_paged_decode_workspace_bytes": (sz, [PG, i32, i32, i32, i64]),
         "kvq_paged_attend_decode_mq": (i32, [PG, P, P, i32, i32, i32, i64, f32, P, P, sz, P]),
@@ -345,16 +344,6 @@ def kvq_dequant(plane: Plane, seq: int, row0: int, n_rows: int, out=None, stream
     P = plane.struct()
     _check(load_library().kvq_dequant(ctypes.byref(P), seq, row0, n_rows, _ptr(out), _stream(stream)))
     return out
-
-
-def kvq_probe_stream_read(buf, n_workgroups: int, sink, stream=None) -> None:
-    """Streaming read of the whole contiguous device tensor `buf` (measurement
-    helper, not part of the attention path); sink: int32 [1] device."""
-    if not buf.is_cuda or not buf.is_contiguous():
-        raise ValueError("buf must be a contiguous device tensor")
-    _need(sink, "sink", torch.int32, (1,))
-    _check(load_library().kvq_probe_stream_read(_ptr(buf), buf.numel() * buf.element_size(), n_workgroups,
-                                                _ptr(sink), _stream(stream)))
 
 
 class PagedLayer:

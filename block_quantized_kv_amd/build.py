@@ -1,15 +1,24 @@
-"""Builds libkvq.so (the HIP kernels and the C ABI) for gfx950 with hipcc."""
+"""Builds the gfx950 libraries with hipcc, in place:
+
+  libkvq.so        the HIP kernels of the attention path and the C ABI (include/kvq.h)
+  libkvq_probe.so  on-box measurement helpers (include/kvq_probe.h), used by the
+                   benchmark only; not linked into libkvq.so
+
+Sources compile in parallel; each library is linked from its own objects."""
 from __future__ import annotations
 
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkvq.so")
-SOURCES = ["kvq_api.cpp", "kv_append.hip", "attn_decode.hip", "attn_prefill.hip", "stream_probe.hip"]
+PROBE_LIB = os.path.join(HERE, "libkvq_probe.so")
+SOURCES = ["kvq_api.cpp", "kv_append.hip", "attn_decode.hip", "attn_prefill.hip"]
+PROBE_SOURCES = ["probe/stream_probe.hip", "probe/mfma_probe.hip"]
 ARCH = "gfx950"
 PER_SOURCE_FLAGS: dict = {}
 
@@ -21,31 +30,49 @@ def hipcc() -> str:
     return "hipcc"
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source with hipcc and link libkvq.so in place."""
+def _common_flags() -> list:
+    return ["-O3", "-fPIC", "-std=c++20", f"--offload-arch={ARCH}",
+            "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+            # no packed fp32 arithmetic anywhere in the device code
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # LDS and global words are re-read through other types
+            "-fno-strict-aliasing",
+            "-Wall", "-Wno-unused-function"]
+
+
+def _compile(src: str, objdir: str, verbose: bool) -> str:
+    obj = os.path.join(objdir, src.replace("/", "_").replace(".", "_") + ".o")
+    lang = ["-x", "hip"] if src.endswith(".hip") else []
+    cmd = [hipcc()] + _common_flags() + PER_SOURCE_FLAGS.get(src, []) + lang + \
+        ["-c", os.path.join(CSRC, src), "-o", obj]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout)
+        raise subprocess.CalledProcessError(r.returncode, cmd, r.stdout)
+    if verbose and r.stdout:
+        print(r.stdout, flush=True)
+    return obj
+
+
+def _link(objs: list, lib: str) -> str:
+    tmp = lib + ".tmp"
+    subprocess.run([hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs, check=True)
+    os.replace(tmp, lib)
+    return lib
+
+
+def build(verbose: bool = False, jobs: int | None = None) -> str:
+    """Compile every source with hipcc and link libkvq.so and libkvq_probe.so."""
     objdir = os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
-    common = ["-O3", "-fPIC", "-std=c++20", f"--offload-arch={ARCH}",
-              "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-              # no packed fp32 arithmetic anywhere in the device code
-              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-              # LDS and global words are re-read through other types
-              "-fno-strict-aliasing",
-              "-Wall", "-Wno-unused-function"]
-    objs = []
-    for src in SOURCES:
-        obj = os.path.join(objdir, src.replace(".", "_") + ".o")
-        lang = ["-x", "hip"] if src.endswith(".hip") else []
-        extra = PER_SOURCE_FLAGS.get(src, [])
-        cmd = [hipcc()] + common + extra + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
-        if verbose:
-            print(" ".join(cmd), flush=True)
-        subprocess.run(cmd, check=True, stderr=None if verbose else subprocess.PIPE)
-        objs.append(obj)
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
-    subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    srcs = SOURCES + PROBE_SOURCES
+    jobs = jobs or min(len(srcs), max(1, os.cpu_count() or 1))
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(lambda s: _compile(s, objdir, verbose), srcs))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], PROBE_LIB)
     return LIB
 
 

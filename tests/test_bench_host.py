@@ -47,15 +47,35 @@ def test_traffic_summary_round_trip(tmp_path, monkeypatch):
     _csv(str(d / "cfetch" / "c_counter_collection.csv"), [("copyBuffer", "FETCH_SIZE", 131072.0)])
     _csv(str(d / "cwrite" / "c_counter_collection.csv"), [("copyBuffer", "WRITE_SIZE", 262144.0)])
     out = tmp_path / "traffic.txt"
-    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(out))
-    bench.write_traffic_summary(str(d))
+    path, kernels, sources, cmd, what = bench.TRAFFIC["decode"]
+    monkeypatch.setitem(bench.TRAFFIC, "decode", (str(out), kernels, sources, cmd, what))
+    bench.write_traffic_summary("decode", str(d))
     fetch = (1100.0 + 50.0) * 2.0 * 1024
     write = (80.0 + 4.0) * 1.0 * 1024
-    assert bench.read_traffic() == pytest.approx(fetch + write, rel=1e-6)
+    assert bench.read_traffic("decode") == pytest.approx(fetch + write, rel=1e-6)
     # a summary taken on other sources is not used
-    text = out.read_text().replace(bench.decode_source_hash(), "0000000000000000")
+    text = out.read_text().replace(bench.source_hash(sources), "0000000000000000")
     out.write_text(text)
-    assert bench.read_traffic() is None
+    assert bench.read_traffic("decode") is None
+
+
+def test_prefill_traffic_summary(tmp_path, monkeypatch):
+    d = tmp_path / "pmc"
+    _csv(str(d / "fetch" / "f_counter_collection.csv"), [("prefill_kernel<128>", "FETCH_SIZE", 60000.0)])
+    _csv(str(d / "write" / "w_counter_collection.csv"), [("prefill_kernel<128>", "WRITE_SIZE", 32768.0)])
+    _csv(str(d / "cfetch" / "c_counter_collection.csv"), [("copyBuffer", "FETCH_SIZE", 131072.0)])
+    _csv(str(d / "cwrite" / "c_counter_collection.csv"), [("copyBuffer", "WRITE_SIZE", 262144.0)])
+    out = tmp_path / "ptraffic.txt"
+    path, kernels, sources, cmd, what = bench.TRAFFIC["prefill"]
+    monkeypatch.setitem(bench.TRAFFIC, "prefill", (str(out), kernels, sources, cmd, what))
+    bench.write_traffic_summary("prefill", str(d))
+    assert bench.read_traffic("prefill") == pytest.approx((60000.0 * 2.0 + 32768.0) * 1024, rel=1e-6)
+
+
+def test_cpu_info_names_the_model_and_threads():
+    info = bench.cpu_info()
+    assert info["nproc"] == os.cpu_count()
+    assert 1 <= info["threads"] <= 16 and info["cpu_model"]
 
 
 def test_busy_summary_round_trip(tmp_path, monkeypatch):

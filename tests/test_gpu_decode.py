@@ -4,8 +4,8 @@ oracle's own quantization of the same fp32 rows).
 Bar: max|gpu - oracle| / max|oracle| <= 1e-3 over the outputs of one call
 (per layer), the decode tolerance.  Covered: all
 9 codec pairs, head_dim 64/128/256, GQA 1..16, lengths 0, 1, ragged tails and
-several tiles, split-count sweeps, softmax invariants, and the five workload
-configurations at full size (sampled q-heads where the oracle would be slow).
+several tiles, split-count sweeps, softmax invariants, and the tiny workload
+configuration in full (the others, every head, in test_gpu_fullsize.py).
 """
 import numpy as np
 import pytest
@@ -176,7 +176,7 @@ def test_graph_replay_matches_eager(gpu):
 
 # ---- the five workload configurations at full size ------------------------------
 
-def _full_workload(gpu, cfg, layer_idx=0, heads_per_seq=None, append_last=False):
+def _full_workload(gpu, cfg, layer_idx=0, append_last=False):
     kc, vc = cfg.layers[layer_idx]
     lens = workloads.seq_lengths(cfg, "cpu").tolist()
     layer = Layer.create(kc, vc, cfg.head_dim, cfg.n_kv_heads, cfg.n_seqs, cfg.capacity, device=gpu)
@@ -197,8 +197,7 @@ def _full_workload(gpu, cfg, layer_idx=0, heads_per_seq=None, append_last=False)
     G = cfg.gqa
     worst = 0.0
     for s, n in enumerate(lens):
-        kv_heads = range(cfg.n_kv_heads) if heads_per_seq is None else heads_per_seq(s)
-        for g in kv_heads:
+        for g in range(cfg.n_kv_heads):
             k, v = host_rows[s]
             kh = k[:, g:g + 1].cpu().numpy()
             vh = v[:, g:g + 1].cpu().numpy()
@@ -213,18 +212,5 @@ def test_tiny_decode_full(gpu):
     _full_workload(gpu, workloads.TINY)
 
 
-def test_decode_32k_full(gpu):
-    _full_workload(gpu, workloads.DECODE_32K, heads_per_seq=lambda s: [0, 3, 7])
-
-
-def test_decode_64k_with_append(gpu):
-    _full_workload(gpu, workloads.DECODE_64K, heads_per_seq=lambda s: [0, 3], append_last=True)
-
-
-@pytest.mark.parametrize("layer_idx", [0, 1])
-def test_decode_196k_split_kv(gpu, layer_idx):
-    _full_workload(gpu, workloads.DECODE_196K, layer_idx=layer_idx, heads_per_seq=lambda s: [layer_idx + 1])
-
-
-def test_batched_decode_16_sequences(gpu):
-    _full_workload(gpu, workloads.BATCHED, heads_per_seq=lambda s: [s % 8])
+# The 32K, 64K, 196K and batched configurations at full size, every head and
+# layer, are in test_gpu_fullsize.py.

@@ -7,8 +7,8 @@ Bar: max|gpu - oracle| / max|oracle| <= 1e-3 per call, as for decode.
 Covered: q_len 1-4 on every head_dim, GQA ratios whose q_len * gqa exceeds
 one 16-column tile (several launches per call), sequences shorter than
 q_len, the newest rows alone in the last split, many splits, q_len = 1
-against kvq_attend_decode bit for bit, and the 64K Q4_G64 workload with two
-queries per step on sampled heads.
+against kvq_attend_decode bit for bit (the 64K Q4_G64 workload with two
+queries per step, every head, is in test_gpu_fullsize.py).
 """
 import numpy as np
 import pytest
@@ -94,29 +94,3 @@ def test_one_query_matches_plain_decode_bitwise(gpu):
     lens = torch.tensor([2000, 100], dtype=torch.int64, device=gpu)
     plain = kvq_attend_decode(layer, q1, lens, 2000, 1.0 / 16.0).cpu().numpy()
     assert np.array_equal(plain, out[:, 0])
-
-
-def test_workload_64k_two_queries_sampled(gpu):
-    """The 64K-context Q4_G64 decode with two drafted tokens per step: append
-    both rows, attend from both, check 6 sampled q-heads of each query."""
-    cfg = workloads.DECODE_64K
-    n, H, d, hq = cfg.ctx, cfg.n_kv_heads, cfg.head_dim, cfg.n_q_heads
-    kc, vc = cfg.layers[0]
-    layer = Layer.create(kc, vc, d, H, 1, cfg.capacity, device=gpu)
-    k = workloads.kv_rows(cfg, 0, 0, "k", 0, n, gpu)
-    v = workloads.kv_rows(cfg, 0, 0, "v", 0, n, gpu)
-    append_rows(layer, k, v, 0, 0)
-    g = torch.Generator(device="cpu").manual_seed(77)
-    q = torch.randn(1, 2, hq, d, generator=g).to(gpu)
-    out = kvq_attend_decode_mq(layer, q, torch.tensor([n], dtype=torch.int64, device=gpu), n, cfg.scale)
-    heads = [0, 5, 11, 12, 17, 23]
-    kn, vn = k.cpu().numpy(), v.cpu().numpy()
-    qn, on = q.cpu().numpy(), out.cpu().numpy()
-    for i in range(2):
-        for h in heads:
-            g_kv = h // (hq // H)
-            kh = oracle.quant_dequant(kc, np.ascontiguousarray(kn[:, g_kv:g_kv + 1].transpose(1, 0, 2)))
-            vh = oracle.quant_dequant(vc, np.ascontiguousarray(vn[:, g_kv:g_kv + 1].transpose(1, 0, 2)))
-            ref = oracle.attend_decode(qn[0, i, h:h + 1], kh, vh, n - 1 + i, cfg.scale)
-            err = rel_err(on[0, i, h:h + 1], ref)
-            assert err <= TOL, (i, h, err)

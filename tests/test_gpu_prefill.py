@@ -6,8 +6,9 @@ matrix cores see K_hat, V_hat, the scaled query and P rounded to binary16).
 Covered: the tiny prefill enumerated in full, ragged prefix/chunk lengths,
 every codec pair, head_dim 64/128/256, several GQA ratios, a chunk at
 position 0, queries far outside the binary16 range, the chunk of a middle sequence of a three-sequence
-cache over several workgroups at every head_dim, and the 2048-token chunk over a 32768-token prefix on 256
-sampled (token, head) rows including the first and last 64 tokens.
+cache over several workgroups at every head_dim, and the 2048-token chunk over a 32768-token prefix on 4096
+(token, head) rows: every head of the first and last 32 tokens and 2048 random
+pairs.
 """
 import numpy as np
 import pytest
@@ -16,14 +17,14 @@ import torch
 import oracle
 import workloads
 from block_quantized_kv_amd import Layer, kvq_attend_prefill
-from gpu_helpers import append_rows, rel_err
+from gpu_helpers import append_rows, pool, rel_err, report
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-2
 CODECS = ["q8_0", "q4_0", "q4_g64"]
 
 
-def _run(gpu, kc, vc, d, hq, hkv, P, T, seed=0, sample=None, cap_extra=0, qmul=1.0):
+def _run(gpu, kc, vc, d, hq, hkv, P, T, seed=0, sample=None, cap_extra=0, qmul=1.0, capsys=None):
     q, k, v = workloads.prefill_inputs(gpu, seed_layer=seed, prefix=P, chunk=T, n_q_heads=hq,
                                        n_kv_heads=hkv, head_dim=d)
     if qmul != 1.0:  # a power of two: exact in bf16
@@ -41,9 +42,16 @@ def _run(gpu, kc, vc, d, hq, hkv, P, T, seed=0, sample=None, cap_extra=0, qmul=1
         got = out
     else:
         toks, heads = sample
-        ref = oracle.attend_prefill(qn, kh, vh, P, scale, tokens=toks, heads=heads)
+        # the sample in pieces, side by side on the host's cores
+        pieces = np.array_split(np.arange(len(toks)), 64)
+        parts = pool().map(lambda ix: oracle.attend_prefill(qn, kh, vh, P, scale, tokens=toks[ix], heads=heads[ix]),
+                           pieces)
+        ref = np.concatenate(list(parts))
         got = out[toks, heads]
     err = rel_err(got, ref)
+    if capsys is not None:
+        report(capsys, f"prefill {T} tokens over a {P}-row prefix ({kc}/{vc}, d {d}, {hq}/{hkv} heads), "
+                       f"{len(got) if sample is not None else T * hq} (token, head) rows", err, TOL)
     assert np.isfinite(out).all()
     assert err <= TOL, (kc, vc, d, hq, hkv, P, T, err)
     return err
@@ -83,18 +91,19 @@ def test_capacity_slack_rows_ignored(gpu):
     _run(gpu, "q8_0", "q4_0", 128, 8, 2, 40, 30, cap_extra=64)
 
 
-def test_workload_prefill_2048_over_32768(gpu):
+def test_workload_prefill_2048_over_32768(gpu, capsys):
     """The chunked-prefill workload (q8_0 K / q4_0 V, 32/8 heads, d 128) on
-    256 sampled rows: the first and last 64 tokens (cycling through the heads)
-    and 128 random (token, head) pairs."""
+    4096 (token, head) rows: every head of the first and the last 32 tokens,
+    and 2048 random pairs."""
     W = workloads.PREFILL
     P, T, hq = W["prefix"], W["chunk"], W["n_q_heads"]
     rng = np.random.default_rng(5)
-    edge = list(range(64)) + list(range(T - 64, T))
-    toks = edge + list(rng.integers(0, T, 128))
-    heads = [t % hq for t in edge] + list(rng.integers(0, hq, 128))
-    _run(gpu, W["k_codec"], W["v_codec"], W["head_dim"], hq, W["n_kv_heads"], P, T,
-         sample=(np.array(toks), np.array(heads)))
+    edge = [t for t in list(range(32)) + list(range(T - 32, T)) for _ in range(hq)]
+    edge_h = [h for _ in range(64) for h in range(hq)]
+    toks = np.array(edge + list(rng.integers(0, T, 2048)))
+    heads = np.array(edge_h + list(rng.integers(0, hq, 2048)))
+    _run(gpu, W["k_codec"], W["v_codec"], W["head_dim"], hq, W["n_kv_heads"], P, T, sample=(toks, heads),
+         capsys=capsys)
 
 
 @pytest.mark.parametrize("kc,vc,d", [("q4_0", "q8_0", 64), ("q8_0", "q4_0", 128), ("q4_g64", "q4_g64", 256)])

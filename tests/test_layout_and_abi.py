@@ -17,21 +17,34 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 
-def _declared_functions():
-    names = set()
-    for h in HEADERS:
-        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
-        names |= set(re.findall(r"\b(kvq_[a-z_]+)\s*\(", text))
-    return sorted(names)
+def _declared_functions(header):
+    text = re.sub(r"/\*.*?\*/", "", open(header).read(), flags=re.S)
+    return sorted(set(re.findall(r"\b(kvq_[a-z0-9_]+)\s*\(", text)))
+
+
+def _library_of(header):
+    """kvq_probe.h is exported by the measurement library, every other header by libkvq.so."""
+    if os.path.basename(header) == "kvq_probe.h":
+        from block_quantized_kv_amd import probe
+        return probe.load_probe_library()
+    return B.load_library()
 
 
 def test_library_exports_every_declared_symbol():
-    lib = B.load_library()
-    names = _declared_functions()
+    seen = set()
+    for h in HEADERS:
+        lib = _library_of(h)
+        for n in _declared_functions(h):
+            assert hasattr(lib, n), (os.path.basename(h), n)
+            seen.add(n)
     assert {"kvq_append", "kvq_attend_decode", "kvq_attend_prefill", "kvq_dequant",
-            "kvq_append_attend_decode", "kvq_probe_stream_read"} <= set(names)
-    for n in names:
-        assert hasattr(lib, n), n
+            "kvq_append_attend_decode", "kvq_probe_stream_read", "kvq_probe_mfma_f16"} <= seen
+
+
+def test_probes_are_not_in_the_attention_library():
+    lib = B.load_library()
+    for n in ("kvq_probe_stream_read", "kvq_probe_mfma_f16"):
+        assert not hasattr(lib, n), n
 
 
 @pytest.mark.parametrize("codec,bpv", [("q4_g64", 4.25), ("q4_0", 4.5), ("q8_0", 8.5)])
@@ -141,13 +154,18 @@ def test_fused_append_decode_validation():
     assert call_mq(0x5000, 0x6000, 65) == 1
 
 
-def test_stream_probe_validation():
+def test_probe_validation():
     # sizes that do not split into whole 8 KiB stripes per wave are refused
-    lib = B.load_library()
+    from block_quantized_kv_amd import probe
+    lib = probe.load_probe_library()
     assert lib.kvq_probe_stream_read(None, 1 << 20, 8, 0x1000, None) == 1
     assert lib.kvq_probe_stream_read(0x10000, (1 << 20) + 4096, 8, 0x1000, None) == 1
     assert lib.kvq_probe_stream_read(0x10000, 1 << 20, 0, 0x1000, None) == 1
     assert lib.kvq_probe_stream_read(0x10000, 1 << 31, 8, 0x1000, None) == 1
+    # the matrix-core loop refuses a null sink and non-positive sizes
+    assert lib.kvq_probe_mfma_f16(256, 100, None, None, None) == 1
+    assert lib.kvq_probe_mfma_f16(0, 100, 0x1000, None, None) == 1
+    assert lib.kvq_probe_mfma_f16(256, 0, 0x1000, None, None) == 1
 
 
 def test_decode_workspace_grows_with_length():
