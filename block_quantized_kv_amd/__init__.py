@@ -17,6 +17,8 @@ from ._binding import (  # noqa: F401
     kvq_append,
     kvq_append_attend_decode,
     kvq_append_attend_decode_mq,
+    kvq_append_attend_decode_noalloc,
+    kvq_noalloc_scratch_bytes,
     kvq_attend_decode,
     kvq_attend_decode_mq,
     kvq_attend_prefill,

@@ -70,6 +70,8 @@ def load_library():
         "kvq_attend_decode_mq": (i32, [LY, P, P, i32, i32, i32, i64, f32, P, P, sz, P]),
         "kvq_append_attend_decode": (i32, [LY, P, P, P, P, i32, i32, i64, f32, P, P, sz, P]),
         "kvq_append_attend_decode_mq": (i32, [LY, P, P, P, P, i32, i32, i32, i64, f32, P, P, sz, P]),
+        "kvq_append_attend_decode_noalloc": (i32, [LY, P, P, P, P, i32, i32, i64, f32, P, P]),
+        "kvq_noalloc_scratch_bytes": (sz, []),
         "kvq_prefill_workspace_bytes": (sz, [LY, i32, i32]),
         "kvq_attend_prefill": (i32, [LY, P, i32, i64, i32, i32, f32, P, P, sz, P]),
         "kvq_dequant": (i32, [PL, i32, i64, i64, P, P]),
@@ -281,6 +283,29 @@ def kvq_append_attend_decode(layer: Layer, k_new, v_new, q, seq_len, max_len: in
                                                    _ptr(seq_len), n_seqs, hq, max_len, softmax_scale,
                                                    _ptr(out), _ptr(workspace), workspace.numel(),
                                                    _stream(stream)))
+    return out
+
+
+def kvq_noalloc_scratch_bytes() -> int:
+    return int(load_library().kvq_noalloc_scratch_bytes())
+
+
+def kvq_append_attend_decode_noalloc(layer: Layer, k_new, v_new, q, seq_len, max_len: int, softmax_scale: float,
+                                     out, stream=None):
+    """kvq_append_attend_decode without a workspace: the library's own device
+    scratch holds the split partials (the call allocates nothing; `out` must
+    be given)."""
+    n_seqs, hq, d = q.shape
+    H = layer.k.n_kv_heads
+    _need(q, "q", torch.float32, (n_seqs, hq, layer.k.head_dim))
+    _need(k_new, "k_new", torch.float32, (n_seqs, H, layer.k.head_dim))
+    _need(v_new, "v_new", torch.float32, (n_seqs, H, layer.k.head_dim))
+    _need(seq_len, "seq_len", torch.int64, (n_seqs,))
+    _need(out, "out", torch.float32, (n_seqs, hq, layer.k.head_dim))
+    L = layer.struct()
+    _check(load_library().kvq_append_attend_decode_noalloc(ctypes.byref(L), _ptr(k_new), _ptr(v_new), _ptr(q),
+                                                           _ptr(seq_len), n_seqs, hq, max_len, softmax_scale,
+                                                           _ptr(out), _stream(stream)))
     return out
 
 

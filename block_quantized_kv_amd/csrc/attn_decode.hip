@@ -59,6 +59,7 @@
 //    partial (unnormalized O, max, sum) per query head, or the final output
 //    when the sequence fits in one split; combine_kernel merges the splits
 //    (log-sum-exp) with many partial loads in flight at once.
+#include <mutex>
 #include <utility>
 
 #include "kvq_device.h"
@@ -1127,6 +1128,42 @@ DecodePlan plan_decode(int head_dim, int n_kv_heads, int n_q_heads, int n_seqs, 
     p.off_part_o = p.off_part_ml + up(p.part_ml_bytes);
     p.total_bytes = p.off_part_o + up(p.part_o_bytes);
     return p;
+}
+
+// ---- the no-allocation entry point's scratch ----------------------------------
+// Split partials of kvq_append_attend_decode_noalloc.  In host code the
+// array's name stands for a host-side handle, not a device address: only the
+// address hipGetSymbolAddress returns (per GPU, with that GPU current) is
+// ever passed to a kernel.
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t static_scratch(hipStream_t s, void **ptr) {
+    int dev = -1;
+    hipError_t e = s ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        int cur = -1;
+        e = hipGetDevice(&cur);
+        if (e != hipSuccess) return e;
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        const hipError_t e2 = cur != dev ? hipSetDevice(cur) : hipSuccess;
+        if (e != hipSuccess) return e;
+        if (e2 != hipSuccess) return e2;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 bool decode_supported(int k_codec, int v_codec, int head_dim) {

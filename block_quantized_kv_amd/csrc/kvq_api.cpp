@@ -201,10 +201,12 @@ size_t decode_ws_bytes(const kvq_layer *L, int32_t n_q_heads, int32_t n_seqs, in
 // sequence before the attention (the first launch writes them).
 // pt: the page table of a paged layer (table null: contiguous planes; the
 // caller has checked L).
+// static_ws: the partials go to the library's own device scratch (the
+// no-allocation entry point; workspace/ws_bytes are ignored).
 kvq_status attend_decode(const kvq_layer *L, const kvq::PageTable &pt, const float *app_k, const float *app_v,
                          const float *q, const int64_t *seq_len, int32_t n_seqs, int32_t q_len, int32_t n_q_heads,
                          int64_t max_len, float softmax_scale, float *out, void *workspace, size_t ws_bytes,
-                         void *hip_stream) {
+                         void *hip_stream, bool static_ws = false) {
     kvq_status st = KVQ_OK;
     const int32_t seq_limit = pt.table ? pt.n_seqs : L->k.n_seqs;
     const int64_t cap = pt.table ? (int64_t)pt.table_stride * pt.page_rows : L->k.capacity;
@@ -229,6 +231,16 @@ kvq_status attend_decode(const kvq_layer *L, const kvq::PageTable &pt, const flo
     if (!kvq::decode_supported(L->k.codec, L->v.codec, L->k.head_dim))
         return fail(KVQ_EUNSUPPORTED, "no decode kernel for this codec pair/head_dim");
     const size_t need = decode_ws_bytes(L, n_q_heads, n_seqs, q_len, max_len);
+    if (static_ws) {
+        // every size check above ran before the device is touched
+        if (need > kvq::kStaticScratchBytes)
+            return fail(KVQ_EWORKSPACE, "this call needs %zu bytes of scratch; the no-allocation entry point "
+                        "holds %zu (use the workspace variant)", need, kvq::kStaticScratchBytes);
+        st = hip_status(kvq::static_scratch(static_cast<hipStream_t>(hip_stream), &workspace),
+                        "locating the library's device scratch");
+        if (st != KVQ_OK) return st;
+        ws_bytes = kvq::kStaticScratchBytes;
+    }
     if (!workspace || ws_bytes < need)
         return fail(KVQ_EWORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, need);
     if (!aligned(workspace, 256)) return fail(KVQ_EINVAL, "workspace not 256-byte aligned");
@@ -316,6 +328,19 @@ kvq_status kvq_append_attend_decode(const kvq_layer *L, const float *k_new, cons
     return attend_decode(L, no_pages(), k_new, v_new, q, seq_len, n_seqs, 1, n_q_heads, max_len, softmax_scale,
                          out, workspace, ws_bytes, hip_stream);
 }
+
+kvq_status kvq_append_attend_decode_noalloc(const kvq_layer *L, const float *k_new, const float *v_new,
+                                            const float *q, const int64_t *seq_len, int32_t n_seqs,
+                                            int32_t n_q_heads, int64_t max_len, float softmax_scale, float *out,
+                                            void *hip_stream) {
+    if (!k_new || !v_new) return fail(KVQ_EINVAL, "null k_new/v_new");
+    kvq_status st = check_layer(L);
+    if (st != KVQ_OK) return st;
+    return attend_decode(L, no_pages(), k_new, v_new, q, seq_len, n_seqs, 1, n_q_heads, max_len, softmax_scale,
+                         out, nullptr, 0, hip_stream, true);
+}
+
+size_t kvq_noalloc_scratch_bytes(void) { return kvq::kStaticScratchBytes; }
 
 kvq_status kvq_append_attend_decode_mq(const kvq_layer *L, const float *k_new, const float *v_new,
                                        const float *q, const int64_t *seq_len, int32_t n_seqs, int32_t q_len,

@@ -106,6 +106,13 @@ struct DecodePlan {
 DecodePlan plan_decode(int head_dim, int n_kv_heads, int n_q_heads, int n_seqs, int64_t max_len,
                        int q_len);
 
+// The device scratch of the no-allocation decode entry point: a file-scope
+// array of kStaticScratchBytes in the library's code object, one copy per
+// GPU.  static_scratch() returns its address on the GPU that `s` runs on
+// (looked up once per GPU with that GPU current, then cached).
+constexpr size_t kStaticScratchBytes = (size_t)16 << 20;
+hipError_t static_scratch(hipStream_t s, void **ptr);
+
 hipError_t launch_append(const AppendArgs &a, hipStream_t s);
 hipError_t launch_dequant(const DequantArgs &a, hipStream_t s);
 // Returns hipErrorInvalidValue when no kernel instance exists for the codec

@@ -200,6 +200,25 @@ kvq_status kvq_append_attend_decode(const kvq_layer *L, const float *k_new, cons
                                     int32_t n_q_heads, int64_t max_len, float softmax_scale, float *out,
                                     void *workspace, size_t ws_bytes, void *hip_stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation):
+ * kvq_append_attend_decode without the workspace arguments.  The split
+ * partials go to a scratch array inside the library's code object, one per
+ * GPU, of kvq_noalloc_scratch_bytes() bytes (16 MiB; held until the process
+ * ends).  A call whose partials would not fit -- the size
+ * kvq_decode_workspace_bytes reports for the same arguments exceeds it --
+ * returns KVQ_EWORKSPACE before anything is enqueued.  The call allocates
+ * nothing; the first call on a GPU looks the array's address up once.  Every
+ * call on one GPU shares that array, so calls that may overlap on one GPU
+ * (other streams, other threads) race and must be serialized by the caller.
+ * Every other argument and the result as for kvq_append_attend_decode. */
+kvq_status kvq_append_attend_decode_noalloc(const kvq_layer *L, const float *k_new, const float *v_new,
+                                            const float *q, const int64_t *seq_len, int32_t n_seqs,
+                                            int32_t n_q_heads, int64_t max_len, float softmax_scale, float *out,
+                                            void *hip_stream);
+/* The scratch size of kvq_append_attend_decode_noalloc (host only). */
+size_t kvq_noalloc_scratch_bytes(void);
+
 /* The same for q_len new tokens per sequence (a verifying multi-query step):
  * rows len_b - q_len + i (those >= 0) receive k_new[b][i] / v_new[b][i], then
  * the call returns what kvq_attend_decode_mq returns on the updated cache.

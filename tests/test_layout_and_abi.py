@@ -208,3 +208,18 @@ def test_unpack_inverts_a_scatter(codec, role):
                 blocks[bi, byte[j, c]] |= np.uint8(v << shift[j, c])
     back = layout.unpack_codes(codec, role, d, blocks)
     assert np.array_equal(back, rows)
+
+
+def test_noalloc_size_check_runs_before_the_device():
+    # a call whose partials exceed the library's scratch is refused on the
+    # host (KVQ_EWORKSPACE), before the scratch is looked up on any GPU
+    lib = B.load_library()
+    assert lib.kvq_noalloc_scratch_bytes() == 16 << 20
+    big = B._Layer(_fake_plane(heads=8, seqs=64, cap=131072),
+                   _fake_plane(codec="q4_0", role=1, heads=8, seqs=64, cap=131072, codes=0x30000, scales=0x40000))
+    st = lib.kvq_append_attend_decode_noalloc(ctypes.byref(big), 0x5000, 0x6000, 0x1000, 0x2000, 64, 32, 131072,
+                                              0.1, 0x3000, None)
+    assert st == 4 and b"no-allocation" in lib.kvq_last_error()
+    # argument errors are still reported first
+    assert lib.kvq_append_attend_decode_noalloc(ctypes.byref(big), None, 0x6000, 0x1000, 0x2000, 1, 32, 64, 0.1,
+                                                0x3000, None) == 1
