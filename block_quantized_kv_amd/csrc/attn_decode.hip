@@ -395,6 +395,56 @@ __device__ __forceinline__ void append_rows(const DecodeArgs &a, int b, int kvh,
     }
 }
 
+// Splits of sequence b in this call: its rows [0, len_b) in split_rows
+// pieces, at least one (an empty sequence still has its output written).
+__device__ __forceinline__ int seq_splits(const DecodeArgs &a, int64_t len) {
+    len = len < 0 ? 0 : (len > a.max_len ? a.max_len : len);
+    const int64_t n = (len + a.split_rows - 1) / a.split_rows;
+    return n < 1 ? 1 : (int)n;
+}
+
+// The work list of a call over several sequences: workgroup w takes the
+// w-th (sequence, kv-head, split) triple, sequence-major, then kv-head, then
+// split, over the splits each sequence's length needs -- so every workgroup
+// with work comes before every idle one (a batch of ragged sequences sized
+// by the longest leaves the idle workgroups at the end of the grid, where
+// they exit at once).  The lengths stay on the device: every wave reads
+// them, 64 sequences per step, and finds its triple with a prefix sum over
+// the lanes; len receives the sequence's length.  False past the last
+// triple.
+__device__ __forceinline__ bool work_item(const DecodeArgs &a, int w, int lane, int &b, int &kvh, int &sp,
+                                          int64_t &len) {
+    const int H = a.k.n_kv_heads;
+    int base = 0;
+    for (int s0 = 0; s0 < a.n_seqs; s0 += 64) {
+        const int s = s0 + lane;
+        const int64_t ls = s < a.n_seqs ? a.seq_len[s] : 0;
+        const int ns = s < a.n_seqs ? seq_splits(a, ls) : 0;
+        const int items = ns * H;
+        int incl = items;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int t = __shfl_up(incl, o, 64);
+            if (lane >= o) incl += t;
+        }
+        const int total = __shfl(incl, 63, 64);
+        if (w < base + total) {
+            const int r = w - base;
+            const uint64_t past = __ballot(incl > r);
+            const int l = __builtin_ctzll(past);
+            const int first = __shfl(incl - items, l, 64);
+            const int nsl = __shfl(ns, l, 64);
+            b = s0 + l;
+            kvh = (r - first) / nsl;
+            sp = (r - first) % nsl;
+            len = __shfl(ls, l, 64);
+            return true;
+        }
+        base += total;
+    }
+    return false;
+}
+
 // PAGED: the planes are a page pool addressed through a.pt (else contiguous).
 template <int D, int KC, int VC, bool PAGED>
 __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
@@ -402,14 +452,31 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     constexpr int NS = C::NS;
     extern __shared__ __align__(16) unsigned char smem[];
 
-    const int sp = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-    int64_t len = a.seq_len[b];
+    int sp, kvh, b;
+    int64_t len;
+    if (a.n_seqs == 1) {
+        // one sequence: the grid is (kv-head, split); splits past the
+        // length need no partial (the combine reads as many as it needs),
+        // and the query load does not wait for the length
+        b = 0;
+        sp = (int)(blockIdx.x % (unsigned)a.max_splits);
+        kvh = (int)(blockIdx.x / (unsigned)a.max_splits);
+        len = a.seq_len[0];
+        if (sp >= seq_splits(a, len)) return;  // idle: the whole workgroup
+    } else {
+        if (!work_item(a, blockIdx.x, threadIdx.x & 63, b, kvh, sp, len)) return;  // idle: the whole workgroup
+        b = __builtin_amdgcn_readfirstlane(b);
+        kvh = __builtin_amdgcn_readfirstlane(kvh);
+        sp = __builtin_amdgcn_readfirstlane(sp);
+        len = (int64_t)__builtin_amdgcn_readfirstlane((int)(len >> 32)) << 32 |
+              (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)len);
+    }
     len = len < 0 ? 0 : (len > a.max_len ? a.max_len : len);
     const int64_t r0 = (int64_t)sp * a.split_rows;
     if (r0 >= len) {  // whole workgroup: no barrier reached
         if (a.max_splits > 1) {
-            // an empty split: its partials merge as nothing (max -inf, sum 0,
-            // o 0), so the combine needs no lengths
+            // the one split of an empty sequence: its partials merge as
+            // nothing (max -inf, sum 0, o 0), so the combine outputs 0
             for (int i = threadIdx.x; i < a.q_len * a.gqa * D; i += kThreads) {
                 const int col = i / D, qi = col / a.gqa, hh = col % a.gqa;
                 const int64_t ph = (((int64_t)b * a.q_len + qi) * a.n_q_heads + (int64_t)kvh * a.gqa + hh) *
@@ -996,15 +1063,16 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
 // Log-sum-exp merge of the splits of one (sequence, query, head), 64 channels
 // per workgroup: 4 thread groups take every 4th split; each thread issues the
 // loads of 16 splits at once and folds them into a running (max, sum, output)
-// triple, then the 4 groups merge through LDS.  Every split of the call has
-// a partial (an empty or invisible one carries max -inf, sum 0, o 0), so no
-// length is read; a query that sees no row at all gets 0.
+// triple, then the 4 groups merge through LDS.  The sequence's splits (as
+// many as its length needs, see seq_splits) each have a partial (an empty or
+// invisible one carries max -inf, sum 0, o 0); a query that sees no row at
+// all gets 0.
 template <int D>
 __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a) {
     __shared__ float s_o[4][64], s_m[4][64], s_l[4][64];
     const int hq = blockIdx.y, row = blockIdx.z, tid = threadIdx.x;
     const int b = row / a.q_len, qi = row % a.q_len;
-    const int nsp = a.max_splits;
+    const int nsp = seq_splits(a, a.seq_len[b]);
     const int64_t qh = (int64_t)row * a.n_q_heads + hq;
     const int cl = tid & 63, sg = tid >> 6, c = blockIdx.x * 64 + cl;
     const float *ml = a.part_ml + 2 * qh * a.max_splits;
@@ -1071,7 +1139,9 @@ hipError_t launch_typed(const DecodeArgs &a, hipStream_t s) {
     using C = Cfg<D, KC, VC>;
     const size_t merge_lds = (size_t)C::OFF_SLOTS + (size_t)kWaves * a.gqa * a.q_len * C::DP * sizeof(float);
     const size_t lds = (size_t)C::LDS_STREAM > merge_lds ? (size_t)C::LDS_STREAM : merge_lds;
-    const dim3 grid((unsigned)a.max_splits, (unsigned)a.k.n_kv_heads, (unsigned)a.n_seqs);
+    // one workgroup per (sequence, kv-head, split) the longest sequence would
+    // need; those past the work list (shorter sequences) exit at once
+    const dim3 grid((unsigned)((int64_t)a.max_splits * a.k.n_kv_heads * a.n_seqs));
     const void *fn = a.pt.table ? (const void *)decode_kernel<D, KC, VC, true>
                                 : (const void *)decode_kernel<D, KC, VC, false>;
     if (lds > 65536) {

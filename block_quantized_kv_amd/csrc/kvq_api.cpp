@@ -251,6 +251,9 @@ kvq_status attend_decode(const kvq_layer *L, const kvq::PageTable &pt, const flo
     if (p.max_splits > 16384)
         return fail(KVQ_EUNSUPPORTED, "max_len %lld needs %d splits (limit 16384)",
                     (long long)max_len, p.max_splits);
+    if ((int64_t)p.max_splits * L->k.n_kv_heads * n_seqs > INT32_MAX)
+        return fail(KVQ_EUNSUPPORTED, "%d splits x %d kv-heads x %d sequences exceed one launch",
+                    p.max_splits, L->k.n_kv_heads, n_seqs);
     kvq::DecodeArgs a;
     a.k = view(L->k);
     a.v = view(L->v);
