@@ -31,6 +31,7 @@ from ._binding import (  # noqa: F401
     kvq_paged_append,
     kvq_paged_attend_decode_mq,
     kvq_paged_append_attend_decode_mq,
+    kvq_paged_attend_prefill,
     kvq_paged_decode_workspace_bytes,
     paged_decode_workspace,
     kvq_plane_bytes,

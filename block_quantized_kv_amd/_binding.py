@@ -79,6 +79,7 @@ def load_library():
         "kvq_paged_decode_workspace_bytes": (sz, [PG, i32, i32, i32, i64]),
         "kvq_paged_attend_decode_mq": (i32, [PG, P, P, i32, i32, i32, i64, f32, P, P, sz, P]),
         "kvq_paged_append_attend_decode_mq": (i32, [PG, P, P, P, P, i32, i32, i32, i64, f32, P, P, sz, P]),
+        "kvq_paged_attend_prefill": (i32, [PG, P, i32, i64, i32, i32, f32, P, P, sz, P]),
         "kvq_status_str": (ctypes.c_char_p, [i32]),
         "kvq_last_error": (ctypes.c_char_p, []),
     }
@@ -454,3 +455,18 @@ def kvq_paged_append_attend_decode_mq(pl: PagedLayer, k_new, v_new, q, seq_len, 
     """kvq_append_attend_decode_mq over paged planes (k_new, v_new fp32
     [n_seqs][q_len][n_kv_heads][head_dim])."""
     return _paged_decode(pl, k_new, v_new, q, seq_len, max_len, softmax_scale, out, workspace, stream)
+
+
+def kvq_paged_attend_prefill(pl: PagedLayer, q_bf16, seq: int, pos0: int, softmax_scale: float, out=None,
+                             stream=None):
+    """kvq_attend_prefill over paged planes: q_bf16 bfloat16 [n_tokens][n_q_heads][head_dim];
+    the chunk's rows must already be appended (through the table) at pos0..pos0+n_tokens-1."""
+    T, hq, d = q_bf16.shape
+    _need(q_bf16, "q_bf16", torch.bfloat16, (T, hq, pl.pool.k.head_dim))
+    if out is None:
+        out = torch.empty((T, hq, d), dtype=torch.float32, device=q_bf16.device)
+    _need(out, "out", torch.float32, (T, hq, pl.pool.k.head_dim))
+    P = pl.struct()
+    _check(load_library().kvq_paged_attend_prefill(ctypes.byref(P), _ptr(q_bf16), seq, pos0, T, hq, softmax_scale,
+                                                   _ptr(out), None, 0, _stream(stream)))
+    return out

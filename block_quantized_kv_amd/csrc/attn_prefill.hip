@@ -52,7 +52,7 @@ typedef uint16_t f16bits;
 
 constexpr int clamp_width(int w, int lo, int hi) { return w < lo ? lo : (w > hi ? hi : w); }
 
-template <int D, int KC, int VC>
+template <int D, int KC, int VC, bool PAGED = false>
 struct PCfg {
     static constexpr int KSTEPS = D / 32;
     static constexpr int CB = D / 16;
@@ -95,12 +95,15 @@ struct PCfg {
     // Two K_hat buffers; three V_hat buffers where LDS allows, so that a
     // tile's V_hat outlives the next tile's K_hat (the two wave groups below
     // run half a tile apart), else two
+    static constexpr int PAGE_LDS = PAGED ? 4 * kPrefillMaxPages : 0;  // paged: the sequence's page numbers
     static constexpr int NVB =
-        (2 * K_TILE_ELEMS + 3 * V_TILE_ELEMS) * 2 + 2 * SC_BYTES_ <= 160 * 1024 ? 3 : 2;
+        (2 * K_TILE_ELEMS + 3 * V_TILE_ELEMS) * 2 + 2 * SC_BYTES_ + PAGE_LDS <= 160 * 1024 ? 3 : 2;
     static constexpr bool PINGPONG = NVB == 3;
     static constexpr int OFF_V = 2 * K_TILE_ELEMS;               // elements
     static constexpr int OFF_SC = OFF_V + NVB * V_TILE_ELEMS;    // elements
-    static constexpr int LDS_BYTES = OFF_SC * 2 + 2 * SC_BYTES_;
+    static constexpr int OFF_PAGES = OFF_SC * 2 + 2 * SC_BYTES_;  // bytes
+    static constexpr int LDS_BYTES = OFF_PAGES + PAGE_LDS;
+    static_assert(LDS_BYTES <= 160 * 1024, "the tiles fit in LDS");
     // dequant units per thread, and a tile's scales (both blocks, K then V)
     static constexpr int UK = (K_UNITS + kPThreads - 1) / kPThreads;
     static constexpr int UV = (V_UNITS + kPThreads - 1) / kPThreads;
@@ -226,9 +229,10 @@ __device__ __forceinline__ void deq_v_unit(int u, const uint32_t (&w)[PCfg<D, KC
     }
 }
 
-template <int D, int KC, int VC>
+// PAGED: the planes are a page pool addressed through a.pt (else contiguous).
+template <int D, int KC, int VC, bool PAGED>
 __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
-    using C = PCfg<D, KC, VC>;
+    using C = PCfg<D, KC, VC, PAGED>;
     extern __shared__ __align__(16) unsigned char smem[];
     f16bits *lds = reinterpret_cast<f16bits *>(smem);
 
@@ -287,7 +291,45 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
     const uint8_t *vcodes = a.v.codes + head_lin * a.v.head_code_stride;
     const uint16_t *kscales = a.k.scales + head_lin * a.k.head_scale_stride;
     const uint16_t *vscales = a.v.scales + head_lin * a.v.head_scale_stride;
-    const int64_t nblocks_plane = a.k.capacity / kBlockRows;
+    // blocks of the sequence: the capacity of its plane, or of its table
+    const int64_t nblocks_plane =
+        PAGED ? (int64_t)a.pt.table_stride * (a.pt.page_rows / kBlockRows) : a.k.capacity / kBlockRows;
+    // paged: the sequence's page numbers, for every block this workgroup
+    // reads, copied to LDS once (read back before every tile load)
+    const int32_t *page_lds = reinterpret_cast<const int32_t *>(smem + C::OFF_PAGES);
+    const int pblk = PAGED ? a.pt.page_rows / kBlockRows : 1;
+    if constexpr (PAGED) {
+        // every block of every tile (the last tile may reach one block past
+        // nrows), within the table
+        const int64_t trows = (int64_t)ntiles * kTileRows < nblocks_plane * kBlockRows
+                                  ? (int64_t)ntiles * kTileRows : nblocks_plane * kBlockRows;
+        const int npages = (int)((trows + a.pt.page_rows - 1) / a.pt.page_rows);
+        int32_t *dst = reinterpret_cast<int32_t *>(smem + C::OFF_PAGES);
+        for (int i = tid; i < npages; i += kPThreads) dst[i] = a.pt.table[(int64_t)a.seq * a.pt.table_stride + i];
+    }
+    // Where block gb of the sequence lives: code and scale pointers of each
+    // plane; false when its page entry points outside the pool (the block
+    // then reads as zeros).
+    auto block_at = [&](int64_t gb, const uint8_t *&kc, const uint8_t *&vc, const uint16_t *&ks,
+                        const uint16_t *&vs) -> bool {
+        if constexpr (!PAGED) {
+            kc = kcodes + gb * C::K_BLOCK_BYTES;
+            vc = vcodes + gb * C::V_BLOCK_BYTES;
+            ks = kscales + gb * C::K_BLOCK_SCALES;
+            vs = vscales + gb * C::V_BLOCK_SCALES;
+            return true;
+        } else {
+            const int page = page_lds[gb / pblk];
+            if (page < 0 || page >= a.k.n_seqs) return false;
+            const int64_t hl = (int64_t)page * a.k.n_kv_heads + kvh;
+            const int64_t within = gb % pblk;
+            kc = a.k.codes + hl * a.k.head_code_stride + within * C::K_BLOCK_BYTES;
+            vc = a.v.codes + hl * a.v.head_code_stride + within * C::V_BLOCK_BYTES;
+            ks = a.k.scales + hl * a.k.head_scale_stride + within * C::K_BLOCK_SCALES;
+            vs = a.v.scales + hl * a.v.head_scale_stride + within * C::V_BLOCK_SCALES;
+            return true;
+        }
+    };
 
     // The tile pipeline: a tile's codes are loaded into registers and its
     // scales staged in LDS one iteration before it is dequantized, which is
@@ -299,27 +341,75 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
     auto load_tile = [&](int tile) {
         const int64_t b0 = (int64_t)tile * 2;  // first block of the tile
         const bool two = b0 + 1 < nblocks_plane;  // the second block exists
-        const uint8_t *kb = kcodes + b0 * C::K_BLOCK_BYTES;
-        const uint8_t *vb = vcodes + b0 * C::V_BLOCK_BYTES;
+        if constexpr (!PAGED) {
+            // contiguous planes: the tile's two blocks are adjacent
+            const uint8_t *kb = kcodes + b0 * C::K_BLOCK_BYTES;
+            const uint8_t *vb = vcodes + b0 * C::V_BLOCK_BYTES;
+#pragma unroll
+            for (int i = 0; i < C::UK; ++i) {
+                const int u = tid + i * kPThreads;
+                if (u < C::K_UNITS && (two || u < C::K_UNITS / 2))
+                    load_chunk<C::K_UW>(rk[i], kb + k_unit_offset<D, KC, VC>(u));
+            }
+#pragma unroll
+            for (int i = 0; i < C::UV; ++i) {
+                const int u = tid + i * kPThreads;
+                if (u < C::V_UNITS && (two || u < C::V_UNITS / 2))
+                    load_chunk<C::V_UW>(rv[i], vb + v_unit_offset<D, KC, VC>(u));
+            }
+            // the tile's scales, 16 bytes per thread: K (both blocks) then V
+            const int o = tid * 16;
+            if (o < C::KSC_BYTES) {
+                if (two || o < C::KSC_BYTES / 2)
+                    rsc = *reinterpret_cast<const u4 *>(reinterpret_cast<const uint8_t *>(kscales + b0 * C::K_BLOCK_SCALES) + o);
+            } else if (o < C::SC_BYTES) {
+                const int ov = o - C::KSC_BYTES;
+                if (two || ov < C::VSC_BYTES / 2)
+                    rsc = *reinterpret_cast<const u4 *>(reinterpret_cast<const uint8_t *>(vscales + b0 * C::V_BLOCK_SCALES) + ov);
+            }
+            return;
+        }
+        // paged: each block's planes (a tile's two blocks may sit in
+        // different pages); an absent second block is never read
+        const uint8_t *kb[2], *vb[2];
+        const uint16_t *ksb[2], *vsb[2];
+        bool ok[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) ok[j] = (j == 0 || two) && block_at(b0 + j, kb[j], vb[j], ksb[j], vsb[j]);
 #pragma unroll
         for (int i = 0; i < C::UK; ++i) {
             const int u = tid + i * kPThreads;
-            if (u < C::K_UNITS && (two || u < C::K_UNITS / 2)) load_chunk<C::K_UW>(rk[i], kb + k_unit_offset<D, KC, VC>(u));
+            if (u >= C::K_UNITS) continue;
+            const int j = u >= C::K_UNITS / 2;  // units of block 0 come first
+            if (ok[j])
+                load_chunk<C::K_UW>(rk[i], kb[j] + k_unit_offset<D, KC, VC>(u) - j * C::K_BLOCK_BYTES);
+            else
+#pragma unroll
+                for (int w = 0; w < C::K_UW / 4; ++w) rk[i][w] = 0u;
         }
 #pragma unroll
         for (int i = 0; i < C::UV; ++i) {
             const int u = tid + i * kPThreads;
-            if (u < C::V_UNITS && (two || u < C::V_UNITS / 2)) load_chunk<C::V_UW>(rv[i], vb + v_unit_offset<D, KC, VC>(u));
+            if (u >= C::V_UNITS) continue;
+            const int j = u >= C::V_UNITS / 2;
+            if (ok[j])
+                load_chunk<C::V_UW>(rv[i], vb[j] + v_unit_offset<D, KC, VC>(u) - j * C::V_BLOCK_BYTES);
+            else
+#pragma unroll
+                for (int w = 0; w < C::V_UW / 4; ++w) rv[i][w] = 0u;
         }
-        // the tile's scales, 16 bytes per thread: K (both blocks) then V
+        // the tile's scales, 16 bytes per thread: K (both blocks) then V;
+        // a block outside the pool gets zero scales
         const int o = tid * 16;
         if (o < C::KSC_BYTES) {
-            if (two || o < C::KSC_BYTES / 2)
-                rsc = *reinterpret_cast<const u4 *>(reinterpret_cast<const uint8_t *>(kscales + b0 * C::K_BLOCK_SCALES) + o);
+            const int j = o >= C::KSC_BYTES / 2, oj = o - j * (C::KSC_BYTES / 2);
+            if (ok[j]) rsc = *reinterpret_cast<const u4 *>(reinterpret_cast<const uint8_t *>(ksb[j]) + oj);
+            else rsc = u4{0u, 0u, 0u, 0u};
         } else if (o < C::SC_BYTES) {
             const int ov = o - C::KSC_BYTES;
-            if (two || ov < C::VSC_BYTES / 2)
-                rsc = *reinterpret_cast<const u4 *>(reinterpret_cast<const uint8_t *>(vscales + b0 * C::V_BLOCK_SCALES) + ov);
+            const int j = ov >= C::VSC_BYTES / 2, oj = ov - j * (C::VSC_BYTES / 2);
+            if (ok[j]) rsc = *reinterpret_cast<const u4 *>(reinterpret_cast<const uint8_t *>(vsb[j]) + oj);
+            else rsc = u4{0u, 0u, 0u, 0u};
         }
     };
     auto stage_scales = [&](int tile) {
@@ -475,6 +565,7 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
     };
 
     // prologue: tile 0 dequantized, tile 1 loaded and its scales staged
+    if constexpr (PAGED) __syncthreads();  // the page numbers are in LDS
     load_tile(0);
     stage_scales(0);
     __syncthreads();
@@ -559,19 +650,24 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
     }
 }
 
-template <int D, int KC, int VC>
-hipError_t launch_ptyped(const PrefillArgs &a, hipStream_t s) {
-    using C = PCfg<D, KC, VC>;
+template <int D, int KC, int VC, bool PAGED>
+hipError_t launch_ptyped_p(const PrefillArgs &a, hipStream_t s) {
+    using C = PCfg<D, KC, VC, PAGED>;
     const size_t lds = (size_t)C::LDS_BYTES;
     if (lds > 65536) {
-        hipError_t e = hipFuncSetAttribute((const void *)prefill_kernel<D, KC, VC>,
+        hipError_t e = hipFuncSetAttribute((const void *)prefill_kernel<D, KC, VC, PAGED>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
     }
     const int ncols = a.n_tokens * a.gqa;
     const dim3 grid((unsigned)((ncols + C::COLS - 1) / C::COLS), (unsigned)a.k.n_kv_heads);
-    prefill_kernel<D, KC, VC><<<grid, dim3(kPThreads), lds, s>>>(a);
+    prefill_kernel<D, KC, VC, PAGED><<<grid, dim3(kPThreads), lds, s>>>(a);
     return hipGetLastError();
+}
+
+template <int D, int KC, int VC>
+hipError_t launch_ptyped(const PrefillArgs &a, hipStream_t s) {
+    return a.pt.table ? launch_ptyped_p<D, KC, VC, true>(a, s) : launch_ptyped_p<D, KC, VC, false>(a, s);
 }
 
 template <int D>

@@ -391,20 +391,31 @@ size_t kvq_prefill_workspace_bytes(const kvq_layer *L, int32_t n_q_heads, int32_
     return 0;
 }
 
-kvq_status kvq_attend_prefill(const kvq_layer *L, const uint16_t *q_bf16, int32_t seq, int64_t pos0,
-                              int32_t n_tokens, int32_t n_q_heads, float softmax_scale, float *out,
-                              void *workspace, size_t ws_bytes, void *hip_stream) {
-    (void)workspace;
-    (void)ws_bytes;
-    kvq_status st = check_layer(L);
-    if (st != KVQ_OK) return st;
+namespace {
+
+// pt: the page table of a paged layer (table null: contiguous planes; the
+// caller has checked L).
+kvq_status attend_prefill(const kvq_layer *L, const kvq::PageTable &pt, const uint16_t *q_bf16, int32_t seq,
+                          int64_t pos0, int32_t n_tokens, int32_t n_q_heads, float softmax_scale, float *out,
+                          void *hip_stream) {
+    const int32_t seq_limit = pt.table ? pt.n_seqs : L->k.n_seqs;
+    const int64_t cap = pt.table ? (int64_t)pt.table_stride * pt.page_rows : L->k.capacity;
     if (!q_bf16 || !out) return fail(KVQ_EINVAL, "null q/out");
     if (!aligned(q_bf16, 16) || !aligned(out, 16)) return fail(KVQ_EINVAL, "q/out not 16-byte aligned");
-    if (seq < 0 || seq >= L->k.n_seqs) return fail(KVQ_EINVAL, "seq %d out of range", seq);
+    if (seq < 0 || seq >= seq_limit) return fail(KVQ_EINVAL, "seq %d out of range", seq);
     if (n_tokens < 0) return fail(KVQ_EINVAL, "n_tokens %d < 0", n_tokens);
-    if (pos0 < 0 || pos0 + n_tokens > L->k.capacity)
+    if (pos0 < 0 || pos0 + n_tokens > cap)
         return fail(KVQ_ERANGE, "chunk [%lld, %lld) outside capacity %lld", (long long)pos0,
-                    (long long)(pos0 + n_tokens), (long long)L->k.capacity);
+                    (long long)(pos0 + n_tokens), (long long)cap);
+    if (pt.table) {
+        // the pages the chunk's 64-row tiles touch, kept in LDS by the kernel
+        int64_t rows = (pos0 + n_tokens + 63) / 64 * 64;
+        rows = rows < cap ? rows : cap;
+        const int64_t pages = (rows + pt.page_rows - 1) / pt.page_rows;
+        if (pages > kvq::kPrefillMaxPages)
+            return fail(KVQ_EUNSUPPORTED, "the chunk reaches %lld pages; paged prefill addresses at most %d",
+                        (long long)pages, kvq::kPrefillMaxPages);
+    }
     if (pos0 + n_tokens > (int64_t)INT32_MAX)
         return fail(KVQ_EUNSUPPORTED, "prefill positions beyond 2^31 rows");
     if (n_q_heads <= 0 || n_q_heads % L->k.n_kv_heads != 0)
@@ -418,6 +429,7 @@ kvq_status kvq_attend_prefill(const kvq_layer *L, const uint16_t *q_bf16, int32_
     kvq::PrefillArgs a;
     a.k = view(L->k);
     a.v = view(L->v);
+    a.pt = pt;
     a.q = q_bf16;
     a.out = out;
     a.seq = seq;
@@ -428,6 +440,29 @@ kvq_status kvq_attend_prefill(const kvq_layer *L, const uint16_t *q_bf16, int32_
     a.scale_log2 = softmax_scale * 1.4426950408889634f;
     return hip_status(kvq::launch_prefill(a, static_cast<hipStream_t>(hip_stream)),
                       "prefill launch");
+}
+
+}  // namespace
+
+kvq_status kvq_attend_prefill(const kvq_layer *L, const uint16_t *q_bf16, int32_t seq, int64_t pos0,
+                              int32_t n_tokens, int32_t n_q_heads, float softmax_scale, float *out,
+                              void *workspace, size_t ws_bytes, void *hip_stream) {
+    (void)workspace;
+    (void)ws_bytes;
+    kvq_status st = check_layer(L);
+    if (st != KVQ_OK) return st;
+    return attend_prefill(L, no_pages(), q_bf16, seq, pos0, n_tokens, n_q_heads, softmax_scale, out, hip_stream);
+}
+
+kvq_status kvq_paged_attend_prefill(const kvq_paged_layer *P, const uint16_t *q_bf16, int32_t seq, int64_t pos0,
+                                    int32_t n_tokens, int32_t n_q_heads, float softmax_scale, float *out,
+                                    void *workspace, size_t ws_bytes, void *hip_stream) {
+    (void)workspace;
+    (void)ws_bytes;
+    kvq::PageTable pt;
+    kvq_status st = check_paged(P, &pt);
+    if (st != KVQ_OK) return st;
+    return attend_prefill(&P->pool, pt, q_bf16, seq, pos0, n_tokens, n_q_heads, softmax_scale, out, hip_stream);
 }
 
 kvq_status kvq_dequant(const kvq_plane *P, int32_t seq, int64_t row0, int64_t n_rows, float *out,

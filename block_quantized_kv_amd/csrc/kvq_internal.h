@@ -84,6 +84,7 @@ struct DecodeArgs {
 
 struct PrefillArgs {
     PlaneView k, v;
+    PageTable pt;            // table null: contiguous planes
     const uint16_t *q;       // [T][Hq][D] bf16 bits
     float *out;              // [T][Hq][D]
     int seq;
@@ -120,6 +121,9 @@ hipError_t launch_dequant(const DequantArgs &a, hipStream_t s);
 bool decode_supported(int k_codec, int v_codec, int head_dim);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t s);
 bool prefill_supported(int k_codec, int v_codec, int head_dim);
+// Pages of one sequence a paged prefill can address (its workgroups keep the
+// sequence's page numbers in LDS).
+constexpr int kPrefillMaxPages = 4096;
 hipError_t launch_prefill(const PrefillArgs &a, hipStream_t s);
 
 }  // namespace kvq

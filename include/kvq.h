@@ -302,6 +302,17 @@ kvq_status kvq_attend_prefill(const kvq_layer *L, const uint16_t *q_bf16, int32_
                               int32_t n_tokens, int32_t n_q_heads, float softmax_scale, float *out,
                               void *workspace, size_t ws_bytes, void *hip_stream);
 
+/* kvq_attend_prefill over paged planes (den_llama.cpp, "Adaptive KV streaming
+ * (contributed)": the device pool of resident KV pages, read through the
+ * sequence's block table): the same result as on contiguous planes holding
+ * the same rows.  seq in [0, P->n_seqs); pos0 + n_tokens <= max_pages *
+ * page_rows; the pages that the chunk's rows rounded up to a multiple of 64
+ * reach must number at most 4096 (else KVQ_EUNSUPPORTED).  Rows whose table
+ * entry lies outside the pool read as zeros (key and value 0). */
+kvq_status kvq_paged_attend_prefill(const kvq_paged_layer *P, const uint16_t *q_bf16, int32_t seq, int64_t pos0,
+                                    int32_t n_tokens, int32_t n_q_heads, float softmax_scale, float *out,
+                                    void *workspace, size_t ws_bytes, void *hip_stream);
+
 /* ---- dequant (den_llama.cpp, "What's in the fork": convert; "Results":
  * dequant bit-identical to the CPU reference) ----------------------------- */
 

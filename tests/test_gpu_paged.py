@@ -12,7 +12,8 @@ larger than needed; ragged lengths (a length inside a page, on a page
 boundary, shorter than a page); several sequences; one and two queries per
 sequence; the fused append + decode through the table; a table entry outside
 the pool (the append reports KVQ_ERANGE and skips the row, the attention
-stays finite); and the 64K-context Q4_G64 step on 256-row pages.
+stays finite); the 64K-context Q4_G64 step on 256-row pages; and chunked
+prefill through the table (below).
 """
 import numpy as np
 import pytest
@@ -201,3 +202,91 @@ def test_workload_64k_on_256_row_pages(gpu):
     _same_pages(pl, contig, [n // 256])
     assert torch.isfinite(out).all()
     assert rel_err(out.cpu().numpy(), ref.cpu().numpy()) <= SAME
+
+
+# ---- chunked prefill through the table ---------------------------------------------
+# The prefill kernel reads a tile's blocks in a fixed order, so over paged
+# planes holding the same rows it must return exactly what it returns over
+# contiguous planes (bit for bit), and within the prefill bar of the oracle,
+# 1e-2 of max|oracle|.
+
+PTOL = 1e-2
+
+
+def _prefill_case(gpu, kc, vc, d, hq, hkv, P, T, page_rows, seed, seqs=1, seq=0, bad_page=None):
+    from block_quantized_kv_amd import kvq_attend_prefill, kvq_paged_attend_prefill
+    n = P + T
+    max_pages = (n + page_rows - 1) // page_rows + 1
+    pl = _pool_for(kc, vc, d, hkv, seqs, max_pages, page_rows, gpu, seed)
+    contig = Layer.create(kc, vc, d, hkv, seqs, max_pages * page_rows, device=gpu)
+    rows = {}
+    for s in range(seqs):
+        q, k, v = workloads.prefill_inputs(gpu, seed_layer=seed + s, prefix=P, chunk=T, n_q_heads=hq,
+                                           n_kv_heads=hkv, head_dim=d)
+        _paged_rows(pl, s, k, v)
+        append_rows(contig, k, v, s, 0)
+        rows[s] = (q, k, v)
+    q, k, v = rows[seq]
+    kh = oracle.quant_dequant(kc, k.cpu().numpy().transpose(1, 0, 2).copy())
+    vh = oracle.quant_dequant(vc, v.cpu().numpy().transpose(1, 0, 2).copy())
+    if bad_page is not None:
+        # a table entry outside the pool: those rows read as zeros
+        table = pl.block_table.clone()
+        table[seq, bad_page] = pl.pool.k.n_seqs + 5
+        pl = PagedLayer(pl.pool, table)
+        lo, hi = bad_page * page_rows, min(n, (bad_page + 1) * page_rows)
+        kh[:, lo:hi] = 0.0
+        vh[:, lo:hi] = 0.0
+    scale = 1.0 / np.sqrt(d)
+    out = kvq_paged_attend_prefill(pl, q, seq, P, scale).cpu().numpy()
+    assert np.isfinite(out).all()
+    if bad_page is None:
+        ref_c = kvq_attend_prefill(contig, q, seq, P, scale).cpu().numpy()
+        assert np.array_equal(out, ref_c)
+    ref = oracle.attend_prefill(q.float().cpu().numpy(), kh, vh, P, scale)
+    err = rel_err(out, ref)
+    assert err <= PTOL, (kc, vc, d, P, T, page_rows, err)
+
+
+@pytest.mark.parametrize("page_rows", [32, 64, 256])
+@pytest.mark.parametrize("kc,vc,d", [("q8_0", "q4_0", 128), ("q4_g64", "q4_g64", 256), ("q4_0", "q8_0", 64)])
+def test_paged_prefill_matches_contiguous(gpu, kc, vc, d, page_rows):
+    _prefill_case(gpu, kc, vc, d, 8, 2, 300, 77, page_rows, seed=page_rows + d)
+
+
+@pytest.mark.parametrize("P,T", [(0, 1), (31, 33), (64, 64), (500, 260)])
+def test_paged_prefill_ragged(gpu, P, T):
+    _prefill_case(gpu, "q8_0", "q4_g64", 128, 6, 1, P, T, 64, seed=P + T)
+
+
+def test_paged_prefill_middle_sequence(gpu):
+    _prefill_case(gpu, "q4_0", "q4_0", 128, 8, 2, 200, 150, 32, seed=3, seqs=3, seq=1)
+
+
+def test_paged_prefill_entry_outside_pool_reads_zeros(gpu):
+    _prefill_case(gpu, "q8_0", "q4_0", 128, 8, 2, 300, 70, 64, seed=8, bad_page=2)
+
+
+def test_paged_prefill_workload_2048_over_32768(gpu):
+    """The chunked-prefill workload on 256-row pages shuffled over the pool:
+    bit for bit what the contiguous planes give; 256 rows against the oracle."""
+    from block_quantized_kv_amd import kvq_attend_prefill, kvq_paged_attend_prefill
+    W = workloads.PREFILL
+    P, T, hq, hkv, d = W["prefix"], W["chunk"], W["n_q_heads"], W["n_kv_heads"], W["head_dim"]
+    kc, vc = W["k_codec"], W["v_codec"]
+    page_rows = 256
+    max_pages = (P + T) // page_rows
+    pl = _pool_for(kc, vc, d, hkv, 1, max_pages, page_rows, gpu, seed=21)
+    contig = Layer.create(kc, vc, d, hkv, 1, P + T, device=gpu)
+    q, k, v = workloads.prefill_inputs(gpu)
+    _paged_rows(pl, 0, k, v)
+    append_rows(contig, k, v, 0, 0)
+    scale = 1.0 / np.sqrt(d)
+    out = kvq_paged_attend_prefill(pl, q, 0, P, scale).cpu().numpy()
+    assert np.array_equal(out, kvq_attend_prefill(contig, q, 0, P, scale).cpu().numpy())
+    rng = np.random.default_rng(4)
+    toks, heads = rng.integers(0, T, 256).astype(np.int32), rng.integers(0, hq, 256).astype(np.int32)
+    kh = oracle.quant_dequant(kc, k.cpu().numpy().transpose(1, 0, 2).copy())
+    vh = oracle.quant_dequant(vc, v.cpu().numpy().transpose(1, 0, 2).copy())
+    ref = oracle.attend_prefill(q.float().cpu().numpy(), kh, vh, P, scale, tokens=toks, heads=heads)
+    assert rel_err(out[toks, heads], ref) <= PTOL

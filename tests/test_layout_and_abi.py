@@ -223,3 +223,24 @@ def test_noalloc_size_check_runs_before_the_device():
     # argument errors are still reported first
     assert lib.kvq_append_attend_decode_noalloc(ctypes.byref(big), None, 0x6000, 0x1000, 0x2000, 1, 32, 64, 0.1,
                                                 0x3000, None) == 1
+
+
+def test_paged_prefill_validation():
+    lib = B.load_library()
+    pool = B._Layer(_fake_plane(cap=64, seqs=8), _fake_plane(codec="q4_0", role=1, cap=64, seqs=8, codes=0x30000,
+                                                             scales=0x40000))
+    P = B._PagedLayer(pool, 0x7000, 2, 4)   # 2 sequences x 4 pages of 64 rows
+    call = lambda seq=0, pos0=0, T=16, hq=4, q=0x1000, out=0x3000: lib.kvq_paged_attend_prefill(
+        ctypes.byref(P), q, seq, pos0, T, hq, 0.1, out, None, 0, None)
+    assert call(seq=2) == 1                      # only 2 sequences in the table
+    assert call(pos0=250, T=7) == 3              # past 4 pages x 64 rows
+    assert call(q=0) == 1
+    assert call(hq=3) == 1
+    assert call(T=0) == 0                        # nothing to do
+    bad = B._PagedLayer(pool, 0, 2, 4)
+    assert lib.kvq_paged_attend_prefill(ctypes.byref(bad), 0x1000, 0, 0, 16, 4, 0.1, 0x3000, None, 0, None) == 1
+    # more pages than a paged prefill addresses
+    big = B._PagedLayer(B._Layer(_fake_plane(cap=32, seqs=8), _fake_plane(codec="q4_0", role=1, cap=32, seqs=8,
+                                                                          codes=0x30000, scales=0x40000)),
+                        0x7000, 1, 10000)
+    assert lib.kvq_paged_attend_prefill(ctypes.byref(big), 0x1000, 0, 200000, 16, 4, 0.1, 0x3000, None, 0, None) == 2
