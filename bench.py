@@ -448,7 +448,7 @@ def main():
         u1.record()
         torch.cuda.synchronize()
         unfused_ms = round(u0.elapsed_time(u1) / (reps * ROTATE), 5)
-        # attention alone (no append), for the baselines below
+        # attention alone (no append)
         u0.record()
         for _ in range(reps):
             attend_graph.replay()
@@ -511,13 +511,7 @@ def main():
     if speak is not None:
         result["stream_read_peak"] = speak
     if not args.no_baselines:
-        bl = run_baselines(torch, dev, cfg, caches, q, seq_len, cfg.scale, max(8, min(args.steps, 64)))
-        bl["direct_quantized_attend_ms"] = round(attend_only_ms, 4)
-        bl["speedup_vs_f16_control"] = round(bl["f16_control"]["ms_per_attend"] / attend_only_ms, 2)
-        bl["speedup_vs_dequant_once"] = round(bl["dequant_once"]["ms_per_attend"] / attend_only_ms, 2)
-        # no f16 decode, however good, can move its 4x larger K/V faster than HBM peak
-        bl["f16_hbm_floor_ms"] = round(bl["f16_control"]["kv_bytes"] / (HBM_PEAK_GBS * 1e9) * 1e3, 4)
-        result["baselines"] = bl
+        result["f16_control"] = run_f16_control(torch, dev, args)
     if not args.no_prefill:
         result["prefill"] = run_prefill(torch, dev, args)
     if not args.no_quality:
@@ -847,59 +841,77 @@ def mfma_peak(torch, dev) -> dict:
     return {"tflops": max(by.values()), "by_workgroups_of_8_waves": by, "instruction": "v_mfma_f32_16x16x32_f16"}
 
 
-def run_baselines(torch, dev, cfg, caches, q, seq_len, scale, steps):
-    """What reading the quantized blocks directly saves, on the same 64K
-    decode: (1) an f16 control -- the K/V kept unquantized in binary16 and
-    attended with PyTorch's batched matrix products (rocBLAS/hipBLASLt) and
-    softmax; (2) dequant-once -- kvq_dequant of the quantized cache to fp32,
-    cast to binary16, then the same attention.  Both are vendor baselines,
-    not this library's kernels; K/V rotate over independent copies (>= 1 GB)."""
-    from block_quantized_kv_amd import kvq_dequant
-    n, H, d, hq = cfg.ctx, cfg.n_kv_heads, cfg.head_dim, cfg.n_q_heads
-    G = hq // H
-    qg = q[0].view(H, G, d).half().transpose(1, 2).contiguous()   # [H][d][G]
-
-    def attend_f16(kh, vh):
-        s = torch.bmm(kh, qg).float() * scale                       # [H][n][G]
-        p = torch.softmax(s, dim=1).half().transpose(1, 2).contiguous()  # [H][G][n]
-        return torch.bmm(p, vh)                                    # [H][G][d]
-
-    rot = 4  # 4 x 268 MB of f16 K/V
-    gen = torch.Generator(device=dev).manual_seed(11)
-    kv16 = [(torch.randn(H, n, d, device=dev, generator=gen).half(),
-             torch.randn(H, n, d, device=dev, generator=gen).half()) for _ in range(rot)]
-    for i in range(4):
-        attend_f16(*kv16[i % rot])
+def _time_attend(torch, caches, q, lens, max_len, scale, reps: int) -> float:
+    """ms per kvq_attend_decode call, as HIP-graph replays of one call per
+    cache in turn (the caches rotate so the last-level cache cannot serve
+    the K/V)."""
+    from block_quantized_kv_amd import decode_workspace, kvq_attend_decode
+    out = torch.empty_like(q)
+    ws = decode_workspace(caches[0], q.shape[1], q.shape[0], max_len)
+    per_graph = max(4, len(caches))
+    cap = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cap):
+        for i in range(per_graph):
+            kvq_attend_decode(caches[i % len(caches)], q, lens, max_len, scale, out=out, workspace=ws, stream=cap)
+        with torch.cuda.graph(g, stream=cap):
+            for i in range(per_graph):
+                kvq_attend_decode(caches[i % len(caches)], q, lens, max_len, scale, out=out, workspace=ws,
+                                  stream=cap)
     torch.cuda.synchronize()
+    g.replay()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
-    for i in range(steps):
-        attend_f16(*kv16[i % rot])
+    for _ in range(reps):
+        g.replay()
     e1.record()
     torch.cuda.synchronize()
-    f16_ms = e0.elapsed_time(e1) / steps
-    del kv16
+    return e0.elapsed_time(e1) / (reps * per_graph)
 
-    def dequant_once(L):
-        kh = kvq_dequant(L.k, 0, 0, n).half()
-        vh = kvq_dequant(L.v, 0, 0, n).half()
-        return attend_f16(kh, vh)
 
-    for i in range(2):
-        dequant_once(caches[i % len(caches)])
-    torch.cuda.synchronize()
-    e0.record()
-    for i in range(steps):
-        dequant_once(caches[i % len(caches)])
-    e1.record()
-    torch.cuda.synchronize()
-    dq_ms = e0.elapsed_time(e1) / steps
-    f16_bytes = 2 * H * n * d * 2
-    return {"f16_control": {"ms_per_attend": round(f16_ms, 4), "kv_bytes": f16_bytes,
-                            "gbs": round(f16_bytes / (f16_ms * 1e-3) / 1e9, 1),
-                            "how": "binary16 K/V, torch.bmm + softmax + torch.bmm"},
-            "dequant_once": {"ms_per_attend": round(dq_ms, 4),
-                             "how": "kvq_dequant (fp32) -> binary16 -> the f16 control's attention"}}
+def run_f16_control(torch, dev, args) -> dict:
+    """The pages' comparison through this library's own decode kernel: a
+    q8_0 K / q4_0 V cache read directly against the f16 K / f16 V control
+    (the fallback the quantized pair replaced), same kernel, same rows (the
+    32K workload's outlier-channel rows), 32/8 heads, head_dim 128, at 32K
+    and 65K context.  Beside it, the HBM bytes any dequant-once step moves
+    (read the quantized cache, write a binary16 copy, read the copy) and the
+    time they take at the 8 TB/s peak."""
+    import dataclasses
+
+    import workloads
+    from block_quantized_kv_amd import Layer, kvq_append
+    base = workloads.DECODE_32K
+    res = {}
+    for ctx in (32768, 65536):
+        cfg = dataclasses.replace(base, ctx=ctx, name=f"decode_ctx{ctx // 1024}k_32q_8kv_d128")
+        q = workloads.queries(cfg, 0, dev)
+        lens = torch.tensor([ctx], dtype=torch.int64, device=dev)
+        entry = {}
+        for kc, vc in (("q8_0", "q4_0"), ("f16", "f16")):
+            L = Layer.create(kc, vc, cfg.head_dim, cfg.n_kv_heads, 1, ctx, device=dev)
+            for a in range(0, ctx, 16384):
+                b = min(ctx, a + 16384)
+                kvq_append(L, workloads.kv_rows(cfg, 0, 0, "k", a, b - a, dev),
+                           workloads.kv_rows(cfg, 0, 0, "v", a, b - a, dev),
+                           torch.zeros(b - a, dtype=torch.int32, device=dev),
+                           torch.arange(a, b, dtype=torch.int64, device=dev))
+            rot = max(2, -(-(1 << 30) // L.nbytes))
+            caches = [L] + [L.clone() for _ in range(rot - 1)]
+            ms = _time_attend(torch, caches, q, lens, ctx, cfg.scale, max(4, args.steps // 40))
+            entry[f"{kc}/{vc}"] = {"us_per_call": round(ms * 1e3, 2), "kv_bytes": L.nbytes,
+                                   "gbs": round(L.nbytes / (ms * 1e-3) / 1e9, 1), "rotated_caches": rot}
+            if kc == "q8_0":
+                quant_bytes = L.nbytes
+            del caches, L
+        f16_bytes = entry["f16/f16"]["kv_bytes"]
+        entry["speedup_q8_0_q4_0_over_f16"] = round(entry["f16/f16"]["us_per_call"] /
+                                                    entry["q8_0/q4_0"]["us_per_call"], 3)
+        floor = quant_bytes + 2 * f16_bytes
+        entry["dequant_once_hbm_floor"] = {"bytes": floor, "us_at_8tbs": round(floor / (HBM_PEAK_GBS * 1e9) * 1e6, 2)}
+        res[cfg.name] = entry
+    res["step"] = "kvq_attend_decode over the whole cache, HIP-graph replay, both caches through the same kernel"
+    return res
 
 
 def run_quality(torch, dev, args):

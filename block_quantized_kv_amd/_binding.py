@@ -10,7 +10,7 @@ import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 BLOCK_ROWS = 32
-CODECS = {"q8_0": 0, "q4_0": 1, "q4_g64": 2}
+CODECS = {"q8_0": 0, "q4_0": 1, "q4_g64": 2, "f16": 3}   # f16: the control codec (no scales)
 GROUP = {"q8_0": 32, "q4_0": 32, "q4_g64": 64}
 ROLE_K, ROLE_V = 0, 1
 

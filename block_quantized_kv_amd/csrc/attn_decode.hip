@@ -83,11 +83,15 @@ constexpr int dma_count(int B) { return B / 1024 + (B % 1024) / 256 + ((B % 256)
 template <int D, int KC, int VC>
 struct Cfg {
     static constexpr int KSTEPS = D / 32;
-    static constexpr int KG = group_size(KC);
+    // f16 K has no scales: one "group" spans the row (scale 1)
+    static constexpr int KG = is16(KC) ? D : group_size(KC);
     static constexpr int KNG = D / KG;
     static constexpr int STEPS_PER_KGROUP = KG / 32;
     static constexpr int VG = group_size(VC);
-    static constexpr int VNG = D / VG;
+    static constexpr int VNG = is16(VC) ? 0 : D / VG;
+    // words per k-step (K) and per 16-channel block (V) of one lane
+    static constexpr int K_WPS = is16(KC) ? 4 : is8(KC) ? 2 : 1;
+    static constexpr int V_WPC = is16(VC) ? 4 : is8(VC) ? 2 : 1;
     static constexpr int CB = D / 16;
     static constexpr int K_LB = k_lane_bytes(KC, D);      // bytes per lane per K tile
     static constexpr int V_LB = v_lane_bytes(VC, D);      // bytes per lane per V block
@@ -111,7 +115,7 @@ struct Cfg {
     static constexpr int N_DMA = N_DMA_K + N_DMA_V;
     // per-lane scale words of one block: K (4 rows x KNG groups per tile),
     // V (8 rows x VNG groups)
-    static constexpr int KS_LANE_BYTES = 8 * KNG;   // per tile
+    static constexpr int KS_LANE_BYTES = is16(KC) ? 0 : 8 * KNG;   // per tile
     static constexpr int VS_LANE_BYTES = 16 * VNG;
     // head_dim 256: the query operand is read from LDS at every channel step,
     // leaving the registers to the output accumulator and one block
@@ -756,8 +760,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
                 const int t = g * C::STEPS_PER_KGROUP + st2;
                 const h8 qh = C::Q_LDS ? qg[2 * st2] : qreg[2 * t];
                 const h8 ql = C::Q_LDS ? qg[2 * st2 + 1] : qreg[2 * t + 1];
-                const h8 k0 = k_operand<KC>(&pl.k(0)[is8(KC) ? 2 * t : t]);
-                const h8 k1 = k_operand<KC>(&pl.k(1)[is8(KC) ? 2 * t : t]);
+                const h8 k0 = k_operand<KC>(&pl.k(0)[C::K_WPS * t]);
+                const h8 k1 = k_operand<KC>(&pl.k(1)[C::K_WPS * t]);
                 acc0 = mfma16x16x32(k0, qh, acc0);
                 acc1 = mfma16x16x32(k1, qh, acc1);
                 acc0 = mfma16x16x32(k0, ql, acc0);
@@ -765,8 +769,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                S[0][r] = fmaf(acc0[r], (float)ksc0[g * 4 + r], S[0][r]);
-                S[1][r] = fmaf(acc1[r], (float)ksc1[g * 4 + r], S[1][r]);
+                if constexpr (is16(KC)) {  // binary16 keys: no scale
+                    S[0][r] = acc0[r];
+                    S[1][r] = acc1[r];
+                } else {
+                    S[0][r] = fmaf(acc0[r], (float)ksc0[g * 4 + r], S[0][r]);
+                    S[1][r] = fmaf(acc1[r], (float)ksc1[g * 4 + r], S[1][r]);
+                }
             }
         }
 #pragma unroll
@@ -818,7 +827,23 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     auto process_v = [&](Payload<D, KC, VC> &pl, int idx, const h8 &P) {
         uint32_t *vsw = pl.vs();
         const int rend = rows_to_end(idx);
-        if (rend < kBlockRows) {
+        if (is16(VC) && rend < kBlockRows) {
+            // binary16 values of rows past the sequence end (never written:
+            // any bits) are zeroed, as the block codecs zero their scales;
+            // word 4 cb + m holds the values of slots (2m, 2m + 1)
+            const int vlim = rend - 4 * q4;
+#pragma unroll
+            for (int cb = 0; cb < C::CB; ++cb)
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const int j0 = (m >> 1) * 16 + 2 * (m & 1);
+                    uint32_t word = pl.v()[4 * cb + m];
+                    if (j0 >= vlim) word &= 0xFFFF0000u;
+                    if (j0 + 1 >= vlim) word &= 0x0000FFFFu;
+                    pl.v()[4 * cb + m] = word;
+                }
+        }
+        if (!is16(VC) && rend < kBlockRows) {
             const int vlim = rend - 4 * q4;  // rows past the sequence end
             // rows past the end get a zero V scale, so that bytes that were
             // never written cannot turn 0 * V into NaN; word g*4+m holds the
@@ -839,8 +864,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
         // ---- O^T += V^T P^T, one 16-channel block at a time
 #pragma unroll
         for (int cb = 0; cb < C::CB; ++cb) {
-            const int gv = cb * 16 / C::VG;
-            const h8 vop = v_operand<VC>(&pl.v()[is8(VC) ? 2 * cb : cb], svb + gv * 4);
+            const int gv = is16(VC) ? 0 : cb * 16 / C::VG;
+            const h8 vop = v_operand<VC>(&pl.v()[C::V_WPC * cb], svb + gv * 4);
             O[cb] = mfma16x16x32(vop, P, O[cb]);
         }
     };
@@ -1170,6 +1195,9 @@ hipError_t launch_d(const DecodeArgs &a, hipStream_t s) {
         case Q4_G64 * 3 + Q8_0: return launch_typed<D, Q4_G64, Q8_0>(a, s);
         case Q4_G64 * 3 + Q4_0: return launch_typed<D, Q4_G64, Q4_0>(a, s);
         case Q4_G64 * 3 + Q4_G64: return launch_typed<D, Q4_G64, Q4_G64>(a, s);
+        case F16 * 3 + F16:
+            if constexpr (D <= 128) return launch_typed<D, F16, F16>(a, s);
+            return hipErrorInvalidValue;
         default: return hipErrorInvalidValue;
     }
 }
@@ -1237,6 +1265,8 @@ hipError_t static_scratch(hipStream_t s, void **ptr) {
 }
 
 bool decode_supported(int k_codec, int v_codec, int head_dim) {
+    if (k_codec == F16 || v_codec == F16)  // the f16 control: f16/f16 at head_dim 64 and 128
+        return k_codec == F16 && v_codec == F16 && (head_dim == 64 || head_dim == 128);
     return k_codec >= 0 && k_codec <= 2 && v_codec >= 0 && v_codec <= 2 &&
            (head_dim == 64 || head_dim == 128 || head_dim == 256);
 }

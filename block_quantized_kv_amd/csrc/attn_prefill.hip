@@ -689,6 +689,7 @@ hipError_t launch_pd(const PrefillArgs &a, hipStream_t s) {
 }  // namespace
 
 bool prefill_supported(int k_codec, int v_codec, int head_dim) {
+    // the block codecs (the f16 control codec is a decode-only baseline)
     return k_codec >= 0 && k_codec <= 2 && v_codec >= 0 && v_codec <= 2 &&
            (head_dim == 64 || head_dim == 128 || head_dim == 256);
 }

@@ -94,12 +94,15 @@ __device__ __forceinline__ void append_v(const AppendArgs &a, int tb, int head) 
     } else {
         ok = 0;
     }
+    // f16 values are whole 2-byte stores of their own: never the tile
+    if (is16(VC)) ok = 0;
     if (!__syncthreads_and(ok)) {
         for (int it = tid; it < ((rows * chunks + 255) / 256) * 256; it += 256)
             append_one<VC, ROLE_V>(a, pl, a.x[1], t0 + it / chunks, head, it % chunks, it < rows * chunks);
         return;
     }
 
+    if constexpr (is16(VC)) return;
     // quantize: codes into the tile [row][channel], scales straight to the block
     const int64_t blk_idx = prow0 / kBlockRows;
     uint8_t *blk = pl.codes + head_lin * pl.head_code_stride + blk_idx * block_code_bytes(VC, d);
@@ -187,6 +190,10 @@ __global__ __launch_bounds__(256) void dequant_kernel(DequantArgs a) {
     for (int s = 0; s < 8; ++s) {
         const int c = chunk * 8 + s;
         const CodePos p = ROLE == ROLE_K ? k_code_pos(CODEC, d, j, c) : v_code_pos(CODEC, d, j, c);
+        if constexpr (is16(CODEC)) {  // the stored binary16 value, exact in fp32
+            o[s] = (float)__builtin_bit_cast(_Float16, *reinterpret_cast<const uint16_t *>(blk + p.byte));
+            continue;
+        }
         int qi;
         if constexpr (is8(CODEC)) {
             qi = (int8_t)blk[p.byte];
@@ -226,9 +233,14 @@ hipError_t launch_append(const AppendArgs &a, hipStream_t s) {
         case Q4_G64 * 3 + Q8_0: append_kernel<Q4_G64, Q8_0><<<grid, block, 0, s>>>(a); break;
         case Q4_G64 * 3 + Q4_0: append_kernel<Q4_G64, Q4_0><<<grid, block, 0, s>>>(a); break;
         case Q4_G64 * 3 + Q4_G64: append_kernel<Q4_G64, Q4_G64><<<grid, block, 0, s>>>(a); break;
+        case F16 * 3 + F16: append_kernel<F16, F16><<<grid, block, 0, s>>>(a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+bool append_supported(int k_codec, int v_codec) {
+    return (k_codec == F16) == (v_codec == F16) && k_codec >= 0 && k_codec <= 3 && v_codec >= 0 && v_codec <= 3;
 }
 
 hipError_t launch_dequant(const DequantArgs &a, hipStream_t s) {
@@ -242,6 +254,8 @@ hipError_t launch_dequant(const DequantArgs &a, hipStream_t s) {
         case Q4_0 * 2 + ROLE_V: dequant_kernel<Q4_0, ROLE_V><<<grid, block, 0, s>>>(a); break;
         case Q4_G64 * 2 + ROLE_K: dequant_kernel<Q4_G64, ROLE_K><<<grid, block, 0, s>>>(a); break;
         case Q4_G64 * 2 + ROLE_V: dequant_kernel<Q4_G64, ROLE_V><<<grid, block, 0, s>>>(a); break;
+        case F16 * 2 + ROLE_K: dequant_kernel<F16, ROLE_K><<<grid, block, 0, s>>>(a); break;
+        case F16 * 2 + ROLE_V: dequant_kernel<F16, ROLE_V><<<grid, block, 0, s>>>(a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -28,7 +28,7 @@ kvq_status ok() {
     return KVQ_OK;
 }
 
-bool codec_valid(int32_t c) { return c == KVQ_Q8_0 || c == KVQ_Q4_0 || c == KVQ_Q4_G64; }
+bool codec_valid(int32_t c) { return c == KVQ_Q8_0 || c == KVQ_Q4_0 || c == KVQ_Q4_G64 || c == KVQ_F16; }
 bool head_dim_valid(int32_t d) { return d == 64 || d == 128 || d == 256; }
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
@@ -47,7 +47,7 @@ kvq_status check_plane(const kvq_plane *P, const char *name, int32_t role) {
         return fail(KVQ_EINVAL, "%s: capacity %lld not a positive multiple of %d", name,
                     (long long)P->capacity, KVQ_BLOCK_ROWS);
     if (P->reserved != 0) return fail(KVQ_EINVAL, "%s: reserved field must be 0", name);
-    if (!P->codes || !P->scales) return fail(KVQ_EINVAL, "%s: null codes/scales", name);
+    if (!P->codes || (!P->scales && P->codec != KVQ_F16)) return fail(KVQ_EINVAL, "%s: null codes/scales", name);
     if (!aligned(P->codes, 256) || !aligned(P->scales, 256))
         return fail(KVQ_EINVAL, "%s: codes/scales not 256-byte aligned", name);
     return KVQ_OK;
@@ -143,6 +143,8 @@ kvq_status append_impl(const kvq_layer *L, const kvq::PageTable &pt, const float
     if (n_tokens > 0 && (!seq_idx || !pos)) return fail(KVQ_EINVAL, "null seq_idx/pos");
     if ((k_new && !aligned(k_new, 16)) || (v_new && !aligned(v_new, 16)))
         return fail(KVQ_EINVAL, "k_new/v_new not 16-byte aligned");
+    if (!kvq::append_supported(L->k.codec, L->v.codec))
+        return fail(KVQ_EUNSUPPORTED, "codec pair %d/%d: f16 pairs only with f16", L->k.codec, L->v.codec);
     if (n_tokens == 0) return ok();
     kvq::AppendArgs a;
     a.plane[0] = view(L->k);

@@ -69,7 +69,10 @@ __device__ __forceinline__ u2 byte_magic(uint32_t w) {
 // code plus a known per-slot bias (removed through the accumulator init).
 template <int CODEC>
 __device__ __forceinline__ h8 k_operand(const uint32_t *w) {
-    if constexpr (is8(CODEC)) {
+    if constexpr (is16(CODEC)) {  // the stored binary16 values themselves
+        const u4 r = {w[0], w[1], w[2], w[3]};
+        return __builtin_bit_cast(h8, r);
+    } else if constexpr (is8(CODEC)) {
         const u2 a = byte_magic(w[0]), b = byte_magic(w[1]);
         const u4 r = {a.x, a.y, b.x, b.y};
         return __builtin_bit_cast(h8, r);
@@ -82,11 +85,11 @@ __device__ __forceinline__ h8 k_operand(const uint32_t *w) {
 // in that slot so that slot * factor = (code + bias) * query.
 template <int CODEC>
 __device__ __forceinline__ constexpr float k_slot_bias(int s) {
-    return is8(CODEC) ? 1152.0f : (((s >> 1) & 1) ? 1152.0f : 1032.0f);
+    return is16(CODEC) ? 0.0f : is8(CODEC) ? 1152.0f : (((s >> 1) & 1) ? 1152.0f : 1032.0f);
 }
 template <int CODEC>
 __device__ __forceinline__ constexpr float k_slot_factor(int s) {
-    return is8(CODEC) ? 1.0f : (((s >> 1) & 1) ? 0.0625f : 1.0f);
+    return (is16(CODEC) || is8(CODEC)) ? 1.0f : (((s >> 1) & 1) ? 0.0625f : 1.0f);
 }
 
 // V operand (A of O^T = V^T P^T) for one 16-channel block: binary16 of
@@ -94,6 +97,10 @@ __device__ __forceinline__ constexpr float k_slot_factor(int s) {
 // eight slot rows.  dq2[m] holds the scales of slots (2m, 2m+1).
 template <int CODEC>
 __device__ __forceinline__ h8 v_operand(const uint32_t *w, const h2_alias *dq2) {
+    if constexpr (is16(CODEC)) {  // the stored binary16 values themselves (no scale)
+        const u4 r = {w[0], w[1], w[2], w[3]};
+        return __builtin_bit_cast(h8, r);
+    }
     h2 v0, v1, v2, v3;
     if constexpr (is8(CODEC)) {
         const u2 a = byte_magic(w[0]), b = byte_magic(w[1]);

@@ -115,6 +115,7 @@ constexpr size_t kStaticScratchBytes = (size_t)16 << 20;
 hipError_t static_scratch(hipStream_t s, void **ptr);
 
 hipError_t launch_append(const AppendArgs &a, hipStream_t s);
+bool append_supported(int k_codec, int v_codec);
 hipError_t launch_dequant(const DequantArgs &a, hipStream_t s);
 // Returns hipErrorInvalidValue when no kernel instance exists for the codec
 // pair / head_dim (the API maps that to KVQ_EUNSUPPORTED before calling).

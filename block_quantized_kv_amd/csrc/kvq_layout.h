@@ -24,6 +24,10 @@
 //   and the same chunk-major layout as K.
 //   Scales: [kq][group][s] for those eight rows.
 //
+//  F16 (no scales): the same lane order with one binary16 value (2 bytes) per
+//   slot: 16 bytes per k-step (K) or per channel block (V) and lane, so a
+//   lane's 16-byte run is exactly its 8-value matrix-core operand.
+//
 // The 4-bit slot order (0,4,1,5,2,6,3,7 in nibble positions) is the one in
 // which a word splits into binary16 pairs with two masks and one shift.
 #pragma once
@@ -37,21 +41,26 @@
 
 namespace kvq {
 
-enum : int { Q8_0 = 0, Q4_0 = 1, Q4_G64 = 2 };
+// F16: the f16 control codec (each value its binary16 rounding, 2 bytes, no
+// scales), the cache the quantized codecs are measured against.
+enum : int { Q8_0 = 0, Q4_0 = 1, Q4_G64 = 2, F16 = 3 };
 enum : int { ROLE_K = 0, ROLE_V = 1 };
 constexpr int kBlockRows = 32;
 
+// group_size: values per binary16 scale (F16 has no scales; its "group" is
+// taken as 32 values so that divisions stay defined, with 0 scales per row)
 KVQ_HD constexpr int group_size(int codec) { return codec == Q4_G64 ? 64 : 32; }
 KVQ_HD constexpr int qmax(int codec) { return codec == Q8_0 ? 127 : 7; }
 KVQ_HD constexpr bool is8(int codec) { return codec == Q8_0; }
-KVQ_HD constexpr int row_bytes(int codec, int d) { return is8(codec) ? d : d / 2; }
-KVQ_HD constexpr int n_groups(int codec, int d) { return d / group_size(codec); }
+KVQ_HD constexpr bool is16(int codec) { return codec == F16; }
+KVQ_HD constexpr int row_bytes(int codec, int d) { return is16(codec) ? 2 * d : is8(codec) ? d : d / 2; }
+KVQ_HD constexpr int n_groups(int codec, int d) { return is16(codec) ? 0 : d / group_size(codec); }
 KVQ_HD constexpr int block_code_bytes(int codec, int d) { return kBlockRows * row_bytes(codec, d); }
 KVQ_HD constexpr int block_scales(int codec, int d) { return kBlockRows * n_groups(codec, d); }
 
 // Bytes one lane owns per K tile / per V block.
-KVQ_HD constexpr int k_lane_bytes(int codec, int d) { return is8(codec) ? d / 4 : d / 8; }
-KVQ_HD constexpr int v_lane_bytes(int codec, int d) { return is8(codec) ? d / 2 : d / 4; }
+KVQ_HD constexpr int k_lane_bytes(int codec, int d) { return is16(codec) ? d / 2 : is8(codec) ? d / 4 : d / 8; }
+KVQ_HD constexpr int v_lane_bytes(int codec, int d) { return is16(codec) ? d : is8(codec) ? d / 2 : d / 4; }
 KVQ_HD constexpr int chunk_width(int lane_bytes) { return lane_bytes < 16 ? lane_bytes : 16; }
 
 // Nibble position (0..7 within a 32-bit word) of MFMA slot s.
@@ -74,6 +83,7 @@ KVQ_HD CodePos k_code_pos(int codec, int d, int j, int c) {
     const int t = c >> 5, kq = (c & 31) >> 3, s = c & 7;
     const int lane = i + 16 * kq;
     const int tile = tau * 16 * row_bytes(codec, d);
+    if (is16(codec)) return {tile + lane_byte_offset(k_lane_bytes(codec, d), lane, 16 * t + 2 * s), 0};
     if (is8(codec)) return {tile + lane_byte_offset(k_lane_bytes(codec, d), lane, 8 * t + s), 0};
     const int p = slot_nibble(s);
     return {tile + lane_byte_offset(k_lane_bytes(codec, d), lane, 4 * t + (p >> 1)), 4 * (p & 1)};
@@ -93,6 +103,7 @@ KVQ_HD constexpr int v_slot(int j) { return 4 * (j >> 4) + (j & 3); }
 KVQ_HD CodePos v_code_pos(int codec, int d, int j, int c) {
     const int cb = c >> 4, c16 = c & 15;
     const int lane = c16 + 16 * v_kq(j), s = v_slot(j);
+    if (is16(codec)) return {lane_byte_offset(v_lane_bytes(codec, d), lane, 16 * cb + 2 * s), 0};
     if (is8(codec)) return {lane_byte_offset(v_lane_bytes(codec, d), lane, 8 * cb + s), 0};
     const int p = slot_nibble(s);
     return {lane_byte_offset(v_lane_bytes(codec, d), lane, 4 * cb + (p >> 1)), 4 * (p & 1)};

@@ -81,9 +81,38 @@ __device__ __forceinline__ _Float16 quantize8(const float (&x)[8], int (&q)[8]) 
     return d16;
 }
 
+// The f16 control codec: each value's binary16 nearest-even rounding
+// (v_cvt_f16_f32), saturated at +-65504; no scales.  K role: the 8 values are
+// one 16-byte slot run of one lane, stored whole; V role: each value is a
+// 2-byte store of its own (no other row shares its bytes).
+template <int ROLE>
+__device__ __forceinline__ void store_f16(const PlaneView &pl, int64_t head_lin, int64_t pos, int chunk,
+                                          const float (&x)[8]) {
+    const int d = pl.head_dim;
+    _Float16 h[8];
+    for (int s = 0; s < 8; ++s) h[s] = (_Float16)fminf(fmaxf(x[s], -65504.0f), 65504.0f);
+    const int j = (int)(pos % kBlockRows);
+    uint8_t *blk = pl.codes + head_lin * pl.head_code_stride + (pos / kBlockRows) * block_code_bytes(F16, d);
+    if constexpr (ROLE == ROLE_K) {
+        u4 w;
+        for (int m = 0; m < 4; ++m)
+            w[m] = (uint32_t)__builtin_bit_cast(uint16_t, h[2 * m]) |
+                   ((uint32_t)__builtin_bit_cast(uint16_t, h[2 * m + 1]) << 16);
+        *reinterpret_cast<u4 *>(blk + k_code_pos(F16, d, j, chunk * 8).byte) = w;
+    } else {
+        for (int s = 0; s < 8; ++s)
+            *reinterpret_cast<uint16_t *>(blk + v_code_pos(F16, d, j, chunk * 8 + s).byte) =
+                __builtin_bit_cast(uint16_t, h[s]);
+    }
+}
+
 template <int CODEC, int ROLE>
 __device__ __forceinline__ void quantize_store(const PlaneView &pl, int64_t head_lin, int64_t pos, int chunk,
                                                const float (&x)[8], bool store) {
+    if constexpr (is16(CODEC)) {
+        if (store) store_f16<ROLE>(pl, head_lin, pos, chunk, x);
+        return;
+    }
     const int d = pl.head_dim;
     constexpr int lanes_per_group = group_size(CODEC) / 8;
     int q[8];

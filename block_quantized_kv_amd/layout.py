@@ -9,7 +9,7 @@ from __future__ import annotations
 import numpy as np
 
 BLOCK_ROWS = 32
-GROUP = {"q8_0": 32, "q4_0": 32, "q4_g64": 64}
+GROUP = {"q8_0": 32, "q4_0": 32, "q4_g64": 64}   # f16: no scales
 
 
 def _is8(codec):
@@ -17,7 +17,11 @@ def _is8(codec):
 
 
 def row_bytes(codec, d):
-    return d if _is8(codec) else d // 2
+    return 2 * d if codec == "f16" else d if _is8(codec) else d // 2
+
+
+def n_scales(codec, d):
+    return 0 if codec == "f16" else d // GROUP[codec]
 
 
 def _lane_byte_offset(LB, lane, b):
@@ -45,6 +49,8 @@ def _code_positions(codec: str, role: str, d: int):
         t, kq, s = c >> 5, (c & 31) >> 3, c & 7
         lane = i + 16 * kq
         tile = tau * 16 * row_bytes(codec, d)
+        if codec == "f16":   # byte position of the value's low byte
+            return tile + _lane_byte_offset(d // 2, lane, 16 * t + 2 * s), np.zeros_like(lane + tile)
         if _is8(codec):
             LB = d // 4
             return tile + _lane_byte_offset(LB, lane, 8 * t + s), np.zeros_like(lane + tile)
@@ -54,6 +60,8 @@ def _code_positions(codec: str, role: str, d: int):
     cb, c16 = c >> 4, c & 15
     kq, s = (j & 15) >> 2, 4 * (j >> 4) + (j & 3)
     lane = c16 + 16 * kq
+    if codec == "f16":
+        return _lane_byte_offset(d, lane, 16 * cb + 2 * s), np.zeros_like(lane)
     if _is8(codec):
         LB = d // 2
         return _lane_byte_offset(LB, lane, 8 * cb + s), np.zeros_like(lane)
@@ -64,7 +72,7 @@ def _code_positions(codec: str, role: str, d: int):
 
 def scale_positions(codec: str, role: str, d: int):
     """Index (binary16 units) of the scale of block row j, group g: [32][ng]."""
-    ng = d // GROUP[codec]
+    ng = n_scales(codec, d)
     j = np.arange(BLOCK_ROWS)[:, None]
     g = np.arange(ng)[None, :]
     if role == "k":
@@ -81,6 +89,11 @@ def unpack_codes(codec: str, role: str, d: int, blocks: np.ndarray) -> np.ndarra
     lead = blocks.shape[:-2]
     nb = blocks.shape[-2]
     byte, shift = code_positions(codec, role, d)
+    if codec == "f16":
+        # each value's two bytes (little-endian) in channel order
+        lo, hi = blocks[..., byte], blocks[..., byte + 1]
+        rows = np.stack([lo, hi], axis=-1).reshape(lead + (nb * BLOCK_ROWS, 2 * d))
+        return rows
     vals = (blocks[..., byte] >> shift.astype(np.uint8)) if not _is8(codec) else blocks[..., byte]
     if _is8(codec):
         rows = vals
@@ -107,7 +120,8 @@ def plane_to_rows(plane, seq: int | None = None):
     nb = cap // BLOCK_ROWS
     role = "k" if plane.role == 0 else "v"
     codes = plane.codes.cpu().numpy().reshape(plane.n_seqs, plane.n_kv_heads, nb, -1)
-    scales = plane.scales.cpu().numpy().view(np.uint16).reshape(plane.n_seqs, plane.n_kv_heads, nb, -1)
+    scales = plane.scales.cpu().numpy().view(np.uint16).reshape(plane.n_seqs, plane.n_kv_heads, nb,
+                                                                32 * n_scales(plane.codec, d))
     if seq is not None:
         codes, scales = codes[seq:seq + 1], scales[seq:seq + 1]
     return (unpack_codes(plane.codec, role, d, codes), unpack_scales(plane.codec, role, d, scales))

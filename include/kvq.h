@@ -62,7 +62,14 @@ extern "C" {
 #define KVQ_MAX_GQA 16 /* q-heads per kv-head supported by the attention kernels */
 #define KVQ_MAX_QUERIES 64 /* queries per sequence in one kvq_attend_decode_mq call */
 
-typedef enum { KVQ_Q8_0 = 0, KVQ_Q4_0 = 1, KVQ_Q4_G64 = 2 } kvq_codec;
+/* KVQ_F16 is the control the block codecs are measured against (den_llama.cpp,
+ * "What this fork is" / "Results": without the quantized FlashAttention pair
+ * the fork falls back to an f16 K / f16 V cache): each value stored as its
+ * binary16 nearest-even rounding, saturated at +-65504, 16 bits per value,
+ * no scales (the scales pointer of an F16 plane may be NULL).  It pairs only
+ * with itself (K and V both KVQ_F16), and decode reads it at head_dim 64 and
+ * 128; prefill does not read it.  Anything else returns KVQ_EUNSUPPORTED. */
+typedef enum { KVQ_Q8_0 = 0, KVQ_Q4_0 = 1, KVQ_Q4_G64 = 2, KVQ_F16 = 3 } kvq_codec;
 
 typedef enum { KVQ_ROLE_K = 0, KVQ_ROLE_V = 1 } kvq_role;
 
@@ -99,8 +106,8 @@ typedef struct {
 
 /* ---- sizing (host only, never touches the GPU) ------------------------- */
 
-/* Code bytes per row: head_dim (8-bit codec) or head_dim/2 (4-bit codecs);
- * 0 for an invalid codec/head_dim. */
+/* Code bytes per row: 2*head_dim (KVQ_F16), head_dim (8-bit codec) or
+ * head_dim/2 (4-bit codecs); 0 for an invalid codec/head_dim. */
 size_t kvq_row_code_bytes(int32_t codec, int32_t head_dim);
 
 /* Bytes of the codes and scales buffers of a plane of the given shape

@@ -27,10 +27,10 @@ SRC = os.path.join(HERE, "kvq_oracle.c")
 LIB = os.path.join(HERE, "libkvq_oracle.so")
 
 # Codec names -> the oracle's own codec numbers (see kvq_oracle.c).
-CODECS = {"q8_0": 0, "q4_0": 1, "q4_g64": 2}
-GROUP = {"q8_0": 32, "q4_0": 32, "q4_g64": 64}
+CODECS = {"q8_0": 0, "q4_0": 1, "q4_g64": 2, "f16": 3}
+GROUP = {"q8_0": 32, "q4_0": 32, "q4_g64": 64}        # f16: no groups, no scales
 QMAX = {"q8_0": 127, "q4_0": 7, "q4_g64": 7}
-BITS = {"q8_0": 8, "q4_0": 4, "q4_g64": 4}
+BITS = {"q8_0": 8, "q4_0": 4, "q4_g64": 4, "f16": 16}
 
 _lib = None
 
@@ -113,7 +113,12 @@ def f16_bits_to_f32(h: int) -> float:
 # --------------------------------------------------------------------------
 
 def row_code_bytes(codec: str, d: int) -> int:
-    return d if BITS[codec] == 8 else d // 2
+    return d * BITS[codec] // 8
+
+
+def n_scales(codec: str, d: int) -> int:
+    """binary16 scales per row (none for the f16 codec)."""
+    return d // GROUP[codec] if codec in GROUP else 0
 
 
 def quantize_group(codec: str, x) -> tuple[int, np.ndarray]:
@@ -128,13 +133,13 @@ def quantize_group(codec: str, x) -> tuple[int, np.ndarray]:
 
 
 def quantize_rows(codec: str, x) -> tuple[np.ndarray, np.ndarray]:
-    """fp32 [..., d] rows -> (codes uint8 [..., row_bytes], scales uint16 [..., d/G])."""
+    """fp32 [..., d] rows -> (codes uint8 [..., row_bytes], scales uint16 [..., d/G]; f16: [..., 0])."""
     x = np.ascontiguousarray(x, dtype=np.float32)
     d = x.shape[-1]
     lead = x.shape[:-1]
     n = int(np.prod(lead)) if lead else 1
     codes = np.zeros(lead + (row_code_bytes(codec, d),), np.uint8)
-    scales = np.zeros(lead + (d // GROUP[codec],), np.uint16)
+    scales = np.zeros(lead + (n_scales(codec, d),), np.uint16)
     _check(_load().kvq_oracle_quantize_rows(CODECS[codec], d, n, _ptr(x), _ptr(codes),
                                             _ptr(scales)), "quantize_rows")
     return codes, scales

@@ -34,7 +34,7 @@
 #include <string.h>
 
 /* Codec identifiers used by this file's entry points (its own numbering). */
-enum { OR_Q8_0 = 0, OR_Q4_0 = 1, OR_Q4_G64 = 2 };
+enum { OR_Q8_0 = 0, OR_Q4_0 = 1, OR_Q4_G64 = 2, OR_F16 = 3 };
 
 /* Status codes returned by the entry points. */
 enum { OR_OK = 0, OR_BAD_ARG = 1, OR_NONFINITE = 2 };
@@ -123,12 +123,37 @@ static int codec_group(int codec)
     return codec == OR_Q4_G64 ? 64 : (codec == OR_Q8_0 || codec == OR_Q4_0) ? 32 : 0;
 }
 static int codec_qmax(int codec) { return codec == OR_Q8_0 ? 127 : 7; }
-static int codec_bits(int codec) { return codec == OR_Q8_0 ? 8 : 4; }
+static int codec_bits(int codec) { return codec == OR_F16 ? 16 : codec == OR_Q8_0 ? 8 : 4; }
 
 /* Bytes of codes per row of d values. */
 int64_t kvq_oracle_row_code_bytes(int codec, int d)
 {
-    return codec_bits(codec) == 8 ? d : d / 2;
+    return (int64_t)d * codec_bits(codec) / 8;
+}
+
+/* ------------------------------------------------------------------------- */
+/* The f16 control codec ([den] "What this fork is" / "Results": without the */
+/* quantized FlashAttention pair compiled in, the fork's golden build falls   */
+/* back to an f16 K / f16 V cache, the control the q8_0 K / q4_0 V build is   */
+/* measured against).  Each value is stored as its binary16 nearest-even      */
+/* rounding, two bytes little-endian, with no scales.  Reading where the      */
+/* pages are silent: values beyond the binary16 range saturate at +-65504     */
+/* (the rule the block codecs apply to their scales), so the cache stays      */
+/* finite.                                                                   */
+/* ------------------------------------------------------------------------- */
+
+static int f16_rows(int d, int64_t n_rows, const float *x, uint8_t *codes)
+{
+    for (int64_t i = 0; i < n_rows * (int64_t)d; ++i) {
+        float v = x[i];
+        if (!isfinite(v)) return OR_NONFINITE;
+        if (v > 65504.0f) v = 65504.0f;
+        if (v < -65504.0f) v = -65504.0f;
+        uint16_t h = kvq_oracle_f32_to_f16(v);
+        codes[2 * i] = (uint8_t)(h & 0xFFu);
+        codes[2 * i + 1] = (uint8_t)(h >> 8);
+    }
+    return OR_OK;
 }
 
 /* ------------------------------------------------------------------------- */
@@ -186,6 +211,7 @@ int kvq_oracle_quantize_group(int codec, const float *x, uint16_t *scale_bits, i
 int kvq_oracle_quantize_rows(int codec, int d, int64_t n_rows, const float *x,
                              uint8_t *codes, uint16_t *scales)
 {
+    if (codec == OR_F16) return d > 0 && n_rows >= 0 ? f16_rows(d, n_rows, x, codes) : OR_BAD_ARG;
     int G = codec_group(codec);
     if (G == 0 || d <= 0 || d % G != 0 || n_rows < 0) return OR_BAD_ARG;
     int ng = d / G;
@@ -218,6 +244,12 @@ int kvq_oracle_quantize_rows(int codec, int d, int64_t n_rows, const float *x,
 int kvq_oracle_dequant_rows(int codec, int d, int64_t n_rows, const uint8_t *codes,
                             const uint16_t *scales, float *out)
 {
+    if (codec == OR_F16) {
+        if (d <= 0 || n_rows < 0) return OR_BAD_ARG;
+        for (int64_t i = 0; i < n_rows * (int64_t)d; ++i)
+            out[i] = kvq_oracle_f16_to_f32((uint16_t)(codes[2 * i] | (codes[2 * i + 1] << 8)));
+        return OR_OK;
+    }
     int G = codec_group(codec);
     if (G == 0 || d <= 0 || d % G != 0 || n_rows < 0) return OR_BAD_ARG;
     int ng = d / G;

@@ -180,3 +180,43 @@ def test_append_full_workload_plane_bit_exact(gpu):
         wc, ws = oracle.quantize_rows("q4_g64", xn)
         assert np.array_equal(codes[0], wc)
         assert np.array_equal(scales[0], ws)
+
+
+def _f16_rows(rng, n, H, d):
+    """fp32 rows for the f16 control codec: magnitudes over 1e-8..1e5, with
+    per-row values at a binary16 tie, beyond the range (saturation) and in the
+    binary16 subnormal range."""
+    x = rng.standard_normal((n, H, d)) * 10.0 ** rng.uniform(-8, 5, (n, H, 1))
+    x[..., 0] = 1 + 2.0 ** -11
+    x[..., 1] = 7e4
+    x[..., 2] = -1e6
+    x[..., 3] = 2.0 ** -25
+    x[..., 4] = 3 * 2.0 ** -26
+    return x.astype(np.float32)
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_append_f16_control_bit_exact(gpu, d):
+    """The f16 control codec: every stored value is the oracle's (binary16
+    nearest-even, saturated), in both plane roles; nothing else written;
+    dequant returns it exactly."""
+    rng = np.random.default_rng(d + 16)
+    H, S, cap, n = 3, 2, 96, 110
+    flat = rng.choice(S * cap, size=n, replace=False)
+    seq, pos = flat // cap, flat % cap
+    xk, xv = _f16_rows(rng, n, H, d), _f16_rows(rng, n, H, d)
+    layer = Layer.create("f16", "f16", d, H, S, cap, device=gpu)
+    kvq_append(layer, torch.from_numpy(xk).to(gpu), torch.from_numpy(xv).to(gpu),
+               torch.from_numpy(seq.astype(np.int32)).to(gpu), torch.from_numpy(pos.astype(np.int64)).to(gpu))
+    for plane, x in ((layer.k, xk), (layer.v, xv)):
+        codes, _ = layout.plane_to_rows(plane)
+        want_c, want_s = oracle.quantize_rows("f16", x)
+        assert np.array_equal(codes[seq, :, pos], want_c)
+        untouched = np.ones((S, cap), bool)
+        untouched[seq, pos] = False
+        assert not codes.transpose(0, 2, 1, 3)[untouched].any()
+        want_hat = oracle.dequant_rows("f16", want_c, want_s, d)
+        for s in range(S):
+            got = kvq_dequant(plane, s, 0, cap).cpu().numpy()
+            m = seq == s
+            assert np.array_equal(got[:, pos[m]].transpose(1, 0, 2).view(np.uint32), want_hat[m].view(np.uint32))

@@ -3,7 +3,7 @@ oracle's own quantization of the same fp32 rows).
 
 Bar: max|gpu - oracle| / max|oracle| <= 1e-3 over the outputs of one call
 (per layer), the decode tolerance.  Covered: all
-9 codec pairs, head_dim 64/128/256, GQA 1..16, lengths 0, 1, ragged tails and
+9 codec pairs, the f16 control codec (head_dim 64/128), head_dim 64/128/256, GQA 1..16, lengths 0, 1, ragged tails and
 several tiles, split-count sweeps, softmax invariants, and the tiny workload
 configuration in full (the others, every head, in test_gpu_fullsize.py).
 """
@@ -85,6 +85,37 @@ def test_split_sweep(gpu, max_len_factor):
 def test_large_and_small_magnitudes(gpu):
     _run_case(gpu, "q8_0", "q4_g64", 64, hq=4, hkv=1, lens=[500], kv_scale=1e-5, seed=3)
     _run_case(gpu, "q8_0", "q4_g64", 64, hq=4, hkv=1, lens=[500], kv_scale=300.0, seed=4)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("gqa", [1, 4, 16])
+def test_f16_control_codec(gpu, d, gqa):
+    # the f16 control: binary16 K and V through the same decode kernel
+    _run_case(gpu, "f16", "f16", d, hq=2 * gqa, hkv=2, lens=[3001, 33, 0, 1], seed=d * 3 + gqa)
+
+
+def test_f16_control_split_sweep_and_magnitudes(gpu):
+    _run_case(gpu, "f16", "f16", 128, hq=8, hkv=2, lens=[3000], cap=24032, max_len=24000, seed=12)
+    _run_case(gpu, "f16", "f16", 64, hq=4, hkv=1, lens=[500], kv_scale=1e-3, seed=13)
+    _run_case(gpu, "f16", "f16", 64, hq=4, hkv=1, lens=[500], kv_scale=300.0, seed=14)
+
+
+def test_f16_garbage_rows_past_length_are_ignored(gpu):
+    """f16 planes have no scales to zero: binary16 NaN/Inf patterns in rows past
+    the length (never appended) must not reach the output."""
+    d, H, n = 128, 1, 45
+    layer = Layer.create("f16", "f16", d, H, 1, 64, device=gpu)
+    layer.k.codes.fill_(0xFF)  # 0xFFFF: NaN
+    layer.v.codes.fill_(0x7C)  # 0x7C7C: NaN
+    rng = np.random.default_rng(2)
+    k = rng.standard_normal((n, H, d)).astype(np.float32)
+    v = rng.standard_normal((n, H, d)).astype(np.float32)
+    append_rows(layer, torch.from_numpy(k).to(gpu), torch.from_numpy(v).to(gpu), 0, 0)
+    q = rng.standard_normal((1, 4, d)).astype(np.float32)
+    out = kvq_attend_decode(layer, torch.from_numpy(q).to(gpu), torch.tensor([n], device=gpu), n,
+                            0.1).cpu().numpy()
+    ref = _oracle_decode("f16", "f16", q[0], k, v, n, 0.1)
+    assert np.isfinite(out).all() and rel_err(out[0], ref) <= TOL
 
 
 def test_invariants_constant_v_and_single_row(gpu):

@@ -116,6 +116,12 @@ def test_codec_pairs(gpu, kc, vc):
     _case(gpu, kc, vc, d, hq=8, hkv=2, lens=[300, 33], seed=CODECS.index(kc) * 3 + CODECS.index(vc))
 
 
+@pytest.mark.parametrize("q_len", [1, 3])
+def test_f16_control_codec(gpu, q_len):
+    # the f16 control codec through the fused append + decode
+    _case(gpu, "f16", "f16", 128, hq=8, hkv=2, lens=[300, 33, 1], q_len=q_len, seed=16 + q_len)
+
+
 @pytest.mark.parametrize("n", [1, 31, 32, 33, 255, 256, 257, 511, 513, 2000])
 def test_new_row_positions(gpu, n):
     # small caches split every 256 rows: 256 ends a split, 257 opens one

@@ -176,18 +176,56 @@ def test_decode_workspace_grows_with_length():
     assert 0 < a <= b
 
 
-@pytest.mark.parametrize("codec", ["q8_0", "q4_0", "q4_g64"])
+@pytest.mark.parametrize("codec", ["q8_0", "q4_0", "q4_g64", "f16"])
 @pytest.mark.parametrize("role", ["k", "v"])
 @pytest.mark.parametrize("d", [64, 128, 256])
 def test_block_permutation_is_a_bijection(codec, role, d):
     byte, shift = layout.code_positions(codec, role, d)
     rb = layout.row_bytes(codec, d)
-    slot = byte * 2 + shift // 4 if codec != "q8_0" else byte
-    n_slots = 32 * rb * (2 if codec != "q8_0" else 1)
+    if codec == "f16":  # a value's two bytes: its low byte sits at an even offset
+        assert (byte % 2 == 0).all()
+        slot = byte // 2
+        n_slots = 32 * rb // 2
+    else:
+        slot = byte * 2 + shift // 4 if codec != "q8_0" else byte
+        n_slots = 32 * rb * (2 if codec != "q8_0" else 1)
     assert slot.min() == 0 and slot.max() == n_slots - 1
     assert np.unique(slot).size == slot.size == n_slots
     sidx = layout.scale_positions(codec, role, d)
-    assert np.unique(sidx).size == sidx.size == 32 * (d // layout.GROUP[codec])
+    assert np.unique(sidx).size == sidx.size == 32 * layout.n_scales(codec, d)
+
+
+def test_unpack_inverts_a_scatter_f16():
+    d, nb = 128, 2
+    rng = np.random.default_rng(1)
+    for role in ("k", "v"):
+        rows = rng.integers(0, 256, size=(nb * 32, 2 * d), dtype=np.uint8)
+        byte, _ = layout.code_positions("f16", role, d)
+        blocks = np.zeros((nb, 32 * 2 * d), np.uint8)
+        for bi in range(nb):
+            for j in range(32):
+                for c in range(d):
+                    blocks[bi, byte[j, c]] = rows[bi * 32 + j, 2 * c]
+                    blocks[bi, byte[j, c] + 1] = rows[bi * 32 + j, 2 * c + 1]
+        assert np.array_equal(layout.unpack_codes("f16", role, d, blocks), rows)
+
+
+def test_f16_control_codec_sizes_and_pairing():
+    # 16 bits per value, no scales
+    c, sc = B.kvq_plane_bytes("f16", 128, 8, 1, 1024)
+    assert sc == 0 and c * 8 == 16 * 8 * 1024 * 128 and B.kvq_row_code_bytes("f16", 256) == 512
+    lib = B.load_library()
+    f16 = lambda role, d=128, codes=0x10000: _fake_plane(codec="f16", role=role, d=d, codes=codes, scales=0)
+    both = B._Layer(f16(0), f16(1, codes=0x30000))
+    # an f16 plane needs no scales pointer: validation passes up to the workspace check
+    assert _call_decode(both, ws_bytes=16) == 4
+    # f16 pairs only with f16 (append, decode); decode reads it at head_dim <= 128; prefill not at all
+    mixed = B._Layer(f16(0), _fake_plane(codec="q4_0", role=1, codes=0x30000, scales=0x40000))
+    assert _call_decode(mixed) == 2
+    assert lib.kvq_append(ctypes.byref(mixed), 0x5000, 0x6000, 0x1000, 0x2000, 4, None, None) == 2
+    wide = B._Layer(f16(0, d=256), f16(1, d=256, codes=0x30000))
+    assert _call_decode(wide) == 2
+    assert lib.kvq_attend_prefill(ctypes.byref(both), 0x1000, 0, 0, 16, 4, 0.1, 0x3000, None, 0, None) == 2
 
 
 @pytest.mark.parametrize("codec", ["q8_0", "q4_0", "q4_g64"])

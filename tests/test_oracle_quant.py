@@ -235,3 +235,43 @@ def test_nonfinite_input_rejected():
     x[3] = np.nan
     with pytest.raises(ValueError):
         oracle.quantize_group("q8_0", x)
+
+
+# ---- the f16 control codec ---------------------------------------------------------
+
+def _f16_inputs():
+    rng = np.random.default_rng(16)
+    x = rng.standard_normal(4096) * 10.0 ** rng.uniform(-9, 6, 4096)
+    one = 1.0
+    specials = [0.0, -0.0, 1.0, -1.0, 65504.0, -65504.0, 65519.99, 65520.0, -65520.0, 1e6, -3e38,
+                6.1e-5, 2.0 ** -14, 2.0 ** -24, 2.0 ** -25, 3 * 2.0 ** -26, 2.0 ** -26,
+                one + 2.0 ** -11, one + 3 * 2.0 ** -11, -(one + 2.0 ** -11), 2049.0, 2051.0, 1e-8]
+    return np.concatenate([x, specials, np.zeros(64 - (4096 + len(specials)) % 64)]).astype(np.float32)
+
+
+def test_f16_codec_is_the_binary16_cast_with_saturation():
+    """The f16 control codec stores each value as torch's binary16 cast (a
+    library routine, round to nearest even) of the value clamped to +-65504,
+    little-endian, with no scales; dequantization returns that binary16 value."""
+    import torch
+    x = _f16_inputs()
+    codes, scales = oracle.quantize_rows("f16", x.reshape(-1, 64))
+    assert codes.shape == (x.size // 64, 128) and scales.shape == (x.size // 64, 0)
+    bits = codes.reshape(-1, 2)
+    got = bits[:, 0].astype(np.uint16) | (bits[:, 1].astype(np.uint16) << 8)
+    want = torch.from_numpy(np.clip(x, -65504, 65504)).half().view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got, want)
+    back = oracle.dequant_rows("f16", codes, scales, 64).reshape(-1)
+    assert np.array_equal(back, want.view(np.float16).astype(np.float32))
+    # round-trip error at most half a binary16 unit in the last place inside the range
+    inside = np.abs(x) < 65504
+    ulp = np.spacing(np.abs(back[inside]).astype(np.float16)).astype(np.float64)
+    assert (np.abs(back[inside].astype(np.float64) - x[inside]) <= ulp / 2).all()
+    assert oracle.row_code_bytes("f16", 128) == 256
+
+
+def test_f16_codec_rejects_non_finite():
+    x = np.zeros(64, np.float32)
+    x[3] = np.inf
+    with pytest.raises(ValueError):
+        oracle.quantize_rows("f16", x)
