@@ -10,6 +10,7 @@ library raises.
 from ._binding import (  # noqa: F401
     BLOCK_ROWS,
     CODECS,
+    KVQ_EOVERFLOW,
     KvqError,
     Plane,
     Layer,

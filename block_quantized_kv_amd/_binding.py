@@ -15,7 +15,8 @@ GROUP = {"q8_0": 32, "q4_0": 32, "q4_g64": 64}
 ROLE_K, ROLE_V = 0, 1
 
 STATUS = {0: "KVQ_OK", 1: "KVQ_EINVAL", 2: "KVQ_EUNSUPPORTED", 3: "KVQ_ERANGE",
-          4: "KVQ_EWORKSPACE", 5: "KVQ_EHIP"}
+          4: "KVQ_EWORKSPACE", 5: "KVQ_EHIP", 6: "KVQ_EOVERFLOW"}
+KVQ_EOVERFLOW = 6
 
 
 class KvqError(RuntimeError):
@@ -65,21 +66,21 @@ def load_library():
         "kvq_plane_bytes": (i32, [i32, i32, i32, i32, i64, ctypes.POINTER(sz), ctypes.POINTER(sz)]),
         "kvq_append": (i32, [LY, P, P, P, P, i32, P, P]),
         "kvq_decode_workspace_bytes": (sz, [LY, i32, i32, i64]),
-        "kvq_attend_decode": (i32, [LY, P, P, i32, i32, i64, f32, P, P, sz, P]),
+        "kvq_attend_decode": (i32, [LY, P, P, i32, i32, i64, f32, P, P, sz, P, P]),
         "kvq_decode_mq_workspace_bytes": (sz, [LY, i32, i32, i32, i64]),
-        "kvq_attend_decode_mq": (i32, [LY, P, P, i32, i32, i32, i64, f32, P, P, sz, P]),
-        "kvq_append_attend_decode": (i32, [LY, P, P, P, P, i32, i32, i64, f32, P, P, sz, P]),
-        "kvq_append_attend_decode_mq": (i32, [LY, P, P, P, P, i32, i32, i32, i64, f32, P, P, sz, P]),
-        "kvq_append_attend_decode_noalloc": (i32, [LY, P, P, P, P, i32, i32, i64, f32, P, P]),
+        "kvq_attend_decode_mq": (i32, [LY, P, P, i32, i32, i32, i64, f32, P, P, sz, P, P]),
+        "kvq_append_attend_decode": (i32, [LY, P, P, P, P, i32, i32, i64, f32, P, P, sz, P, P]),
+        "kvq_append_attend_decode_mq": (i32, [LY, P, P, P, P, i32, i32, i32, i64, f32, P, P, sz, P, P]),
+        "kvq_append_attend_decode_noalloc": (i32, [LY, P, P, P, P, i32, i32, i64, f32, P, P, P]),
         "kvq_noalloc_scratch_bytes": (sz, []),
         "kvq_prefill_workspace_bytes": (sz, [LY, i32, i32]),
-        "kvq_attend_prefill": (i32, [LY, P, i32, i64, i32, i32, f32, P, P, sz, P]),
+        "kvq_attend_prefill": (i32, [LY, P, i32, i64, i32, i32, f32, P, P, sz, P, P]),
         "kvq_dequant": (i32, [PL, i32, i64, i64, P, P]),
         "kvq_paged_append": (i32, [PG, P, P, P, P, i32, P, P]),
         "kvq_paged_decode_workspace_bytes": (sz, [PG, i32, i32, i32, i64]),
-        "kvq_paged_attend_decode_mq": (i32, [PG, P, P, i32, i32, i32, i64, f32, P, P, sz, P]),
-        "kvq_paged_append_attend_decode_mq": (i32, [PG, P, P, P, P, i32, i32, i32, i64, f32, P, P, sz, P]),
-        "kvq_paged_attend_prefill": (i32, [PG, P, i32, i64, i32, i32, f32, P, P, sz, P]),
+        "kvq_paged_attend_decode_mq": (i32, [PG, P, P, i32, i32, i32, i64, f32, P, P, sz, P, P]),
+        "kvq_paged_append_attend_decode_mq": (i32, [PG, P, P, P, P, i32, i32, i32, i64, f32, P, P, sz, P, P]),
+        "kvq_paged_attend_prefill": (i32, [PG, P, i32, i64, i32, i32, f32, P, P, sz, P, P]),
         "kvq_status_str": (ctypes.c_char_p, [i32]),
         "kvq_last_error": (ctypes.c_char_p, []),
     }
@@ -106,6 +107,13 @@ def _check(status: int) -> None:
 
 def _ptr(t) -> int | None:
     return None if t is None else t.data_ptr()
+
+
+def _status(dev_status):
+    """The optional device status word (int32 [1]) of an attention call."""
+    if dev_status is not None:
+        _need(dev_status, "dev_status", torch.int32, (1,))
+    return _ptr(dev_status)
 
 
 def _stream(stream) -> int | None:
@@ -210,7 +218,7 @@ def decode_workspace(layer: Layer, n_q_heads: int, n_seqs: int, max_len: int):
 
 
 def kvq_attend_decode(layer: Layer, q, seq_len, max_len: int, softmax_scale: float, out=None,
-                      workspace=None, stream=None):
+                      workspace=None, dev_status=None, stream=None):
     """q fp32 [n_seqs][n_q_heads][head_dim]; seq_len int64 [n_seqs] (device)."""
     n_seqs, hq, d = q.shape
     _need(q, "q", torch.float32, (n_seqs, hq, layer.k.head_dim))
@@ -225,7 +233,7 @@ def kvq_attend_decode(layer: Layer, q, seq_len, max_len: int, softmax_scale: flo
     L = layer.struct()
     _check(load_library().kvq_attend_decode(ctypes.byref(L), _ptr(q), _ptr(seq_len), n_seqs, hq,
                                             max_len, softmax_scale, _ptr(out), _ptr(workspace),
-                                            workspace.numel(), _stream(stream)))
+                                            workspace.numel(), _status(dev_status), _stream(stream)))
     return out
 
 
@@ -241,7 +249,7 @@ def decode_mq_workspace(layer: Layer, n_q_heads: int, n_seqs: int, q_len: int, m
 
 
 def kvq_attend_decode_mq(layer: Layer, q, seq_len, max_len: int, softmax_scale: float, out=None,
-                         workspace=None, stream=None):
+                         workspace=None, dev_status=None, stream=None):
     """q fp32 [n_seqs][q_len][n_q_heads][head_dim]; query i of sequence b sits at
     row seq_len[b] - q_len + i (already appended) and attends rows up to it."""
     n_seqs, q_len, hq, d = q.shape
@@ -257,12 +265,12 @@ def kvq_attend_decode_mq(layer: Layer, q, seq_len, max_len: int, softmax_scale: 
     L = layer.struct()
     _check(load_library().kvq_attend_decode_mq(ctypes.byref(L), _ptr(q), _ptr(seq_len), n_seqs, q_len, hq,
                                                max_len, softmax_scale, _ptr(out), _ptr(workspace),
-                                               workspace.numel(), _stream(stream)))
+                                               workspace.numel(), _status(dev_status), _stream(stream)))
     return out
 
 
 def kvq_append_attend_decode(layer: Layer, k_new, v_new, q, seq_len, max_len: int, softmax_scale: float,
-                             out=None, workspace=None, stream=None):
+                             out=None, workspace=None, dev_status=None, stream=None):
     """k_new, v_new fp32 [n_seqs][n_kv_heads][head_dim] become row seq_len[b] - 1
     of sequence b; then q fp32 [n_seqs][n_q_heads][head_dim] attends as
     kvq_attend_decode (one launch does both)."""
@@ -283,7 +291,7 @@ def kvq_append_attend_decode(layer: Layer, k_new, v_new, q, seq_len, max_len: in
     _check(load_library().kvq_append_attend_decode(ctypes.byref(L), _ptr(k_new), _ptr(v_new), _ptr(q),
                                                    _ptr(seq_len), n_seqs, hq, max_len, softmax_scale,
                                                    _ptr(out), _ptr(workspace), workspace.numel(),
-                                                   _stream(stream)))
+                                                   _status(dev_status), _stream(stream)))
     return out
 
 
@@ -292,7 +300,7 @@ def kvq_noalloc_scratch_bytes() -> int:
 
 
 def kvq_append_attend_decode_noalloc(layer: Layer, k_new, v_new, q, seq_len, max_len: int, softmax_scale: float,
-                                     out, stream=None):
+                                     out, dev_status=None, stream=None):
     """kvq_append_attend_decode without a workspace: the library's own device
     scratch holds the split partials (the call allocates nothing; `out` must
     be given)."""
@@ -306,12 +314,12 @@ def kvq_append_attend_decode_noalloc(layer: Layer, k_new, v_new, q, seq_len, max
     L = layer.struct()
     _check(load_library().kvq_append_attend_decode_noalloc(ctypes.byref(L), _ptr(k_new), _ptr(v_new), _ptr(q),
                                                            _ptr(seq_len), n_seqs, hq, max_len, softmax_scale,
-                                                           _ptr(out), _stream(stream)))
+                                                           _ptr(out), _status(dev_status), _stream(stream)))
     return out
 
 
 def kvq_append_attend_decode_mq(layer: Layer, k_new, v_new, q, seq_len, max_len: int, softmax_scale: float,
-                                out=None, workspace=None, stream=None):
+                                out=None, workspace=None, dev_status=None, stream=None):
     """k_new, v_new fp32 [n_seqs][q_len][n_kv_heads][head_dim] become rows
     seq_len[b] - q_len + i; then q fp32 [n_seqs][q_len][n_q_heads][head_dim]
     attends as kvq_attend_decode_mq (the first launch appends)."""
@@ -332,7 +340,7 @@ def kvq_append_attend_decode_mq(layer: Layer, k_new, v_new, q, seq_len, max_len:
     _check(load_library().kvq_append_attend_decode_mq(ctypes.byref(L), _ptr(k_new), _ptr(v_new), _ptr(q),
                                                       _ptr(seq_len), n_seqs, q_len, hq, max_len,
                                                       softmax_scale, _ptr(out), _ptr(workspace),
-                                                      workspace.numel(), _stream(stream)))
+                                                      workspace.numel(), _status(dev_status), _stream(stream)))
     return out
 
 
@@ -342,7 +350,7 @@ def kvq_prefill_workspace_bytes(layer: Layer, n_q_heads: int, n_tokens: int) -> 
 
 
 def kvq_attend_prefill(layer: Layer, q_bf16, seq: int, pos0: int, softmax_scale: float, out=None,
-                       workspace=None, stream=None):
+                       workspace=None, dev_status=None, stream=None):
     """q_bf16 bfloat16 [n_tokens][n_q_heads][head_dim] (device); rows of the chunk
     must already be appended at positions pos0..pos0+n_tokens-1."""
     T, hq, d = q_bf16.shape
@@ -357,7 +365,7 @@ def kvq_attend_prefill(layer: Layer, q_bf16, seq: int, pos0: int, softmax_scale:
     _check(load_library().kvq_attend_prefill(ctypes.byref(L), _ptr(q_bf16), seq, pos0, T, hq,
                                              softmax_scale, _ptr(out), _ptr(workspace),
                                              0 if workspace is None else workspace.numel(),
-                                             _stream(stream)))
+                                             _status(dev_status), _stream(stream)))
     return out
 
 
@@ -415,7 +423,8 @@ def paged_decode_workspace(pl: PagedLayer, n_q_heads: int, n_seqs: int, q_len: i
     return torch.zeros(nbytes, dtype=torch.uint8, device=pl.pool.k.codes.device)
 
 
-def _paged_decode(pl: PagedLayer, k_new, v_new, q, seq_len, max_len, softmax_scale, out, workspace, stream):
+def _paged_decode(pl: PagedLayer, k_new, v_new, q, seq_len, max_len, softmax_scale, out, workspace, dev_status,
+                  stream):
     n_seqs, q_len, hq, d = q.shape
     H, D = pl.pool.k.n_kv_heads, pl.pool.k.head_dim
     _need(q, "q", torch.float32, (n_seqs, q_len, hq, D))
@@ -435,30 +444,31 @@ def _paged_decode(pl: PagedLayer, k_new, v_new, q, seq_len, max_len, softmax_sca
     if k_new is None:
         st = lib.kvq_paged_attend_decode_mq(ctypes.byref(P), _ptr(q), _ptr(seq_len), n_seqs, q_len, hq, max_len,
                                             softmax_scale, _ptr(out), _ptr(workspace), workspace.numel(),
-                                            _stream(stream))
+                                            _status(dev_status), _stream(stream))
     else:
         st = lib.kvq_paged_append_attend_decode_mq(ctypes.byref(P), _ptr(k_new), _ptr(v_new), _ptr(q),
                                                    _ptr(seq_len), n_seqs, q_len, hq, max_len, softmax_scale,
-                                                   _ptr(out), _ptr(workspace), workspace.numel(), _stream(stream))
+                                                   _ptr(out), _ptr(workspace), workspace.numel(),
+                                                   _status(dev_status), _stream(stream))
     _check(st)
     return out
 
 
 def kvq_paged_attend_decode_mq(pl: PagedLayer, q, seq_len, max_len: int, softmax_scale: float, out=None,
-                               workspace=None, stream=None):
+                               workspace=None, dev_status=None, stream=None):
     """q fp32 [n_seqs][q_len][n_q_heads][head_dim]: kvq_attend_decode_mq over paged planes."""
-    return _paged_decode(pl, None, None, q, seq_len, max_len, softmax_scale, out, workspace, stream)
+    return _paged_decode(pl, None, None, q, seq_len, max_len, softmax_scale, out, workspace, dev_status, stream)
 
 
 def kvq_paged_append_attend_decode_mq(pl: PagedLayer, k_new, v_new, q, seq_len, max_len: int,
-                                      softmax_scale: float, out=None, workspace=None, stream=None):
+                                      softmax_scale: float, out=None, workspace=None, dev_status=None, stream=None):
     """kvq_append_attend_decode_mq over paged planes (k_new, v_new fp32
     [n_seqs][q_len][n_kv_heads][head_dim])."""
-    return _paged_decode(pl, k_new, v_new, q, seq_len, max_len, softmax_scale, out, workspace, stream)
+    return _paged_decode(pl, k_new, v_new, q, seq_len, max_len, softmax_scale, out, workspace, dev_status, stream)
 
 
 def kvq_paged_attend_prefill(pl: PagedLayer, q_bf16, seq: int, pos0: int, softmax_scale: float, out=None,
-                             stream=None):
+                             dev_status=None, stream=None):
     """kvq_attend_prefill over paged planes: q_bf16 bfloat16 [n_tokens][n_q_heads][head_dim];
     the chunk's rows must already be appended (through the table) at pos0..pos0+n_tokens-1."""
     T, hq, d = q_bf16.shape
@@ -468,5 +478,5 @@ def kvq_paged_attend_prefill(pl: PagedLayer, q_bf16, seq: int, pos0: int, softma
     _need(out, "out", torch.float32, (T, hq, pl.pool.k.head_dim))
     P = pl.struct()
     _check(load_library().kvq_paged_attend_prefill(ctypes.byref(P), _ptr(q_bf16), seq, pos0, T, hq, softmax_scale,
-                                                   _ptr(out), None, 0, _stream(stream)))
+                                                   _ptr(out), None, 0, _status(dev_status), _stream(stream)))
     return out

@@ -971,8 +971,16 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     l_run = quad_sum(l_run, x32);
     constexpr int D4 = D / 4;
     // writes item (col, c) of the merged result: the output when the call has
-    // one split, else this split's partial (unnormalized O, max, sum)
+    // one split, else this split's partial (unnormalized O, max, sum).  A
+    // V_hat beyond the binary16 range (|code * dq| > 65504) became an
+    // infinity in the operand, which reaches the sums it enters as an
+    // infinity or a NaN (0 * inf included); a non-finite item marks the call
+    // as outside the operand range (finite queries assumed), and the
+    // combine of finite partials stays finite.
     auto emit = [&](int col, int c, const f4 &o, float M, float L) {
+        if (a.dev_status && !(__builtin_isfinite(o[0]) && __builtin_isfinite(o[1]) && __builtin_isfinite(o[2]) &&
+                              __builtin_isfinite(o[3])))
+            *a.dev_status = kStatusOverflow;
         const int cq = col / G, ch = col % G;
         if (a.max_splits == 1) {
             const float r = L > 0.0f ? 1.0f / L : 0.0f;

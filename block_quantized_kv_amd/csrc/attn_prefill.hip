@@ -633,7 +633,13 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
     }
     if (have_p) pv(ntiles - 1);
 
-    // ---- normalize and store: lane (column h16, q4) holds channels 16cb+4q4..+3
+    // ---- normalize and store: lane (column h16, q4) holds channels 16cb+4q4..+3.
+    // A K_hat or V_hat beyond the binary16 range (|code * dq| > 65504) became
+    // an infinity in LDS, which reaches every output it can affect as an
+    // infinity or a NaN (0 * inf included); only a causally masked row drops
+    // out, and then the result is right.  So a non-finite output marks the
+    // call as outside the operand range (finite queries assumed).
+    bool bad = false;
 #pragma unroll
     for (int nt = 0; nt < C::NT; ++nt) {
         float L = l_run[nt];
@@ -645,9 +651,14 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
         float *dst = a.out + ((int64_t)t * a.n_q_heads + (int64_t)kvh * G + hh) * D;
         const float inv = 1.0f / L;
 #pragma unroll
-        for (int cb = 0; cb < C::CB; ++cb)
-            *reinterpret_cast<f4 *>(dst + 16 * cb + 4 * q4) = O[nt][cb] * inv;
+        for (int cb = 0; cb < C::CB; ++cb) {
+            const f4 o = O[nt][cb] * inv;
+            bad |= !(__builtin_isfinite(o[0]) && __builtin_isfinite(o[1]) && __builtin_isfinite(o[2]) &&
+                     __builtin_isfinite(o[3]));
+            *reinterpret_cast<f4 *>(dst + 16 * cb + 4 * q4) = o;
+        }
     }
+    if (a.dev_status && __any(bad) && lane == 0) *a.dev_status = kStatusOverflow;
 }
 
 template <int D, int KC, int VC, bool PAGED>

@@ -208,7 +208,7 @@ size_t decode_ws_bytes(const kvq_layer *L, int32_t n_q_heads, int32_t n_seqs, in
 kvq_status attend_decode(const kvq_layer *L, const kvq::PageTable &pt, const float *app_k, const float *app_v,
                          const float *q, const int64_t *seq_len, int32_t n_seqs, int32_t q_len, int32_t n_q_heads,
                          int64_t max_len, float softmax_scale, float *out, void *workspace, size_t ws_bytes,
-                         void *hip_stream, bool static_ws = false) {
+                         int32_t *dev_status, void *hip_stream, bool static_ws = false) {
     kvq_status st = KVQ_OK;
     const int32_t seq_limit = pt.table ? pt.n_seqs : L->k.n_seqs;
     const int64_t cap = pt.table ? (int64_t)pt.table_stride * pt.page_rows : L->k.capacity;
@@ -271,6 +271,7 @@ kvq_status attend_decode(const kvq_layer *L, const kvq::PageTable &pt, const flo
     a.split_rows = p.split_rows;
     a.max_splits = p.max_splits;
     a.scale_log2 = softmax_scale * 1.4426950408889634f;
+    a.dev_status = dev_status;
     const int64_t qstride = (int64_t)n_q_heads * L->k.head_dim;  // floats per query
     a.q_seq_stride = (int64_t)q_len * qstride;
     // launches of `per` queries each, in order on the stream (they share the
@@ -301,11 +302,11 @@ size_t kvq_decode_workspace_bytes(const kvq_layer *L, int32_t n_q_heads, int32_t
 kvq_status kvq_attend_decode(const kvq_layer *L, const float *q, const int64_t *seq_len,
                              int32_t n_seqs, int32_t n_q_heads, int64_t max_len,
                              float softmax_scale, float *out, void *workspace, size_t ws_bytes,
-                             void *hip_stream) {
+                             int32_t *dev_status, void *hip_stream) {
     kvq_status st = check_layer(L);
     if (st != KVQ_OK) return st;
     return attend_decode(L, no_pages(), nullptr, nullptr, q, seq_len, n_seqs, 1, n_q_heads, max_len, softmax_scale,
-                         out, workspace, ws_bytes, hip_stream);
+                         out, workspace, ws_bytes, dev_status, hip_stream);
 }
 
 size_t kvq_decode_mq_workspace_bytes(const kvq_layer *L, int32_t n_q_heads, int32_t n_seqs,
@@ -316,33 +317,33 @@ size_t kvq_decode_mq_workspace_bytes(const kvq_layer *L, int32_t n_q_heads, int3
 kvq_status kvq_attend_decode_mq(const kvq_layer *L, const float *q, const int64_t *seq_len,
                                 int32_t n_seqs, int32_t q_len, int32_t n_q_heads, int64_t max_len,
                                 float softmax_scale, float *out, void *workspace, size_t ws_bytes,
-                                void *hip_stream) {
+                                int32_t *dev_status, void *hip_stream) {
     kvq_status st = check_layer(L);
     if (st != KVQ_OK) return st;
     return attend_decode(L, no_pages(), nullptr, nullptr, q, seq_len, n_seqs, q_len, n_q_heads, max_len,
-                         softmax_scale, out, workspace, ws_bytes, hip_stream);
+                         softmax_scale, out, workspace, ws_bytes, dev_status, hip_stream);
 }
 
 kvq_status kvq_append_attend_decode(const kvq_layer *L, const float *k_new, const float *v_new, const float *q,
                                     const int64_t *seq_len, int32_t n_seqs, int32_t n_q_heads, int64_t max_len,
                                     float softmax_scale, float *out, void *workspace, size_t ws_bytes,
-                                    void *hip_stream) {
+                                    int32_t *dev_status, void *hip_stream) {
     if (!k_new || !v_new) return fail(KVQ_EINVAL, "null k_new/v_new");
     kvq_status st = check_layer(L);
     if (st != KVQ_OK) return st;
     return attend_decode(L, no_pages(), k_new, v_new, q, seq_len, n_seqs, 1, n_q_heads, max_len, softmax_scale,
-                         out, workspace, ws_bytes, hip_stream);
+                         out, workspace, ws_bytes, dev_status, hip_stream);
 }
 
 kvq_status kvq_append_attend_decode_noalloc(const kvq_layer *L, const float *k_new, const float *v_new,
                                             const float *q, const int64_t *seq_len, int32_t n_seqs,
                                             int32_t n_q_heads, int64_t max_len, float softmax_scale, float *out,
-                                            void *hip_stream) {
+                                            int32_t *dev_status, void *hip_stream) {
     if (!k_new || !v_new) return fail(KVQ_EINVAL, "null k_new/v_new");
     kvq_status st = check_layer(L);
     if (st != KVQ_OK) return st;
     return attend_decode(L, no_pages(), k_new, v_new, q, seq_len, n_seqs, 1, n_q_heads, max_len, softmax_scale,
-                         out, nullptr, 0, hip_stream, true);
+                         out, nullptr, 0, dev_status, hip_stream, true);
 }
 
 size_t kvq_noalloc_scratch_bytes(void) { return kvq::kStaticScratchBytes; }
@@ -350,12 +351,12 @@ size_t kvq_noalloc_scratch_bytes(void) { return kvq::kStaticScratchBytes; }
 kvq_status kvq_append_attend_decode_mq(const kvq_layer *L, const float *k_new, const float *v_new,
                                        const float *q, const int64_t *seq_len, int32_t n_seqs, int32_t q_len,
                                        int32_t n_q_heads, int64_t max_len, float softmax_scale, float *out,
-                                       void *workspace, size_t ws_bytes, void *hip_stream) {
+                                       void *workspace, size_t ws_bytes, int32_t *dev_status, void *hip_stream) {
     if (!k_new || !v_new) return fail(KVQ_EINVAL, "null k_new/v_new");
     kvq_status st = check_layer(L);
     if (st != KVQ_OK) return st;
     return attend_decode(L, no_pages(), k_new, v_new, q, seq_len, n_seqs, q_len, n_q_heads, max_len,
-                         softmax_scale, out, workspace, ws_bytes, hip_stream);
+                         softmax_scale, out, workspace, ws_bytes, dev_status, hip_stream);
 }
 
 size_t kvq_paged_decode_workspace_bytes(const kvq_paged_layer *P, int32_t n_q_heads, int32_t n_seqs,
@@ -366,24 +367,24 @@ size_t kvq_paged_decode_workspace_bytes(const kvq_paged_layer *P, int32_t n_q_he
 kvq_status kvq_paged_attend_decode_mq(const kvq_paged_layer *P, const float *q, const int64_t *seq_len,
                                       int32_t n_seqs, int32_t q_len, int32_t n_q_heads, int64_t max_len,
                                       float softmax_scale, float *out, void *workspace, size_t ws_bytes,
-                                      void *hip_stream) {
+                                      int32_t *dev_status, void *hip_stream) {
     kvq::PageTable pt;
     kvq_status st = check_paged(P, &pt);
     if (st != KVQ_OK) return st;
     return attend_decode(&P->pool, pt, nullptr, nullptr, q, seq_len, n_seqs, q_len, n_q_heads, max_len,
-                         softmax_scale, out, workspace, ws_bytes, hip_stream);
+                         softmax_scale, out, workspace, ws_bytes, dev_status, hip_stream);
 }
 
 kvq_status kvq_paged_append_attend_decode_mq(const kvq_paged_layer *P, const float *k_new, const float *v_new,
                                              const float *q, const int64_t *seq_len, int32_t n_seqs, int32_t q_len,
                                              int32_t n_q_heads, int64_t max_len, float softmax_scale, float *out,
-                                             void *workspace, size_t ws_bytes, void *hip_stream) {
+                                             void *workspace, size_t ws_bytes, int32_t *dev_status, void *hip_stream) {
     if (!k_new || !v_new) return fail(KVQ_EINVAL, "null k_new/v_new");
     kvq::PageTable pt;
     kvq_status st = check_paged(P, &pt);
     if (st != KVQ_OK) return st;
     return attend_decode(&P->pool, pt, k_new, v_new, q, seq_len, n_seqs, q_len, n_q_heads, max_len,
-                         softmax_scale, out, workspace, ws_bytes, hip_stream);
+                         softmax_scale, out, workspace, ws_bytes, dev_status, hip_stream);
 }
 
 size_t kvq_prefill_workspace_bytes(const kvq_layer *L, int32_t n_q_heads, int32_t n_tokens) {
@@ -399,7 +400,7 @@ namespace {
 // caller has checked L).
 kvq_status attend_prefill(const kvq_layer *L, const kvq::PageTable &pt, const uint16_t *q_bf16, int32_t seq,
                           int64_t pos0, int32_t n_tokens, int32_t n_q_heads, float softmax_scale, float *out,
-                          void *hip_stream) {
+                          int32_t *dev_status, void *hip_stream) {
     const int32_t seq_limit = pt.table ? pt.n_seqs : L->k.n_seqs;
     const int64_t cap = pt.table ? (int64_t)pt.table_stride * pt.page_rows : L->k.capacity;
     if (!q_bf16 || !out) return fail(KVQ_EINVAL, "null q/out");
@@ -440,6 +441,7 @@ kvq_status attend_prefill(const kvq_layer *L, const kvq::PageTable &pt, const ui
     a.n_q_heads = n_q_heads;
     a.gqa = gqa;
     a.scale_log2 = softmax_scale * 1.4426950408889634f;
+    a.dev_status = dev_status;
     return hip_status(kvq::launch_prefill(a, static_cast<hipStream_t>(hip_stream)),
                       "prefill launch");
 }
@@ -448,23 +450,23 @@ kvq_status attend_prefill(const kvq_layer *L, const kvq::PageTable &pt, const ui
 
 kvq_status kvq_attend_prefill(const kvq_layer *L, const uint16_t *q_bf16, int32_t seq, int64_t pos0,
                               int32_t n_tokens, int32_t n_q_heads, float softmax_scale, float *out,
-                              void *workspace, size_t ws_bytes, void *hip_stream) {
+                              void *workspace, size_t ws_bytes, int32_t *dev_status, void *hip_stream) {
     (void)workspace;
     (void)ws_bytes;
     kvq_status st = check_layer(L);
     if (st != KVQ_OK) return st;
-    return attend_prefill(L, no_pages(), q_bf16, seq, pos0, n_tokens, n_q_heads, softmax_scale, out, hip_stream);
+    return attend_prefill(L, no_pages(), q_bf16, seq, pos0, n_tokens, n_q_heads, softmax_scale, out, dev_status, hip_stream);
 }
 
 kvq_status kvq_paged_attend_prefill(const kvq_paged_layer *P, const uint16_t *q_bf16, int32_t seq, int64_t pos0,
                                     int32_t n_tokens, int32_t n_q_heads, float softmax_scale, float *out,
-                                    void *workspace, size_t ws_bytes, void *hip_stream) {
+                                    void *workspace, size_t ws_bytes, int32_t *dev_status, void *hip_stream) {
     (void)workspace;
     (void)ws_bytes;
     kvq::PageTable pt;
     kvq_status st = check_paged(P, &pt);
     if (st != KVQ_OK) return st;
-    return attend_prefill(&P->pool, pt, q_bf16, seq, pos0, n_tokens, n_q_heads, softmax_scale, out, hip_stream);
+    return attend_prefill(&P->pool, pt, q_bf16, seq, pos0, n_tokens, n_q_heads, softmax_scale, out, dev_status, hip_stream);
 }
 
 kvq_status kvq_dequant(const kvq_plane *P, int32_t seq, int64_t row0, int64_t n_rows, float *out,
@@ -497,6 +499,7 @@ const char *kvq_status_str(int32_t status) {
         case KVQ_ERANGE: return "KVQ_ERANGE: position or length outside the capacity";
         case KVQ_EWORKSPACE: return "KVQ_EWORKSPACE: workspace missing or too small";
         case KVQ_EHIP: return "KVQ_EHIP: HIP runtime error";
+        case KVQ_EOVERFLOW: return "KVQ_EOVERFLOW: a dequantized value beyond the binary16 operand range";
         default: return "unknown kvq_status";
     }
 }

@@ -9,6 +9,10 @@
 
 namespace kvq {
 
+// Stored in a call's dev_status by the attention kernels when a dequantized
+// K or V value they read exceeds the binary16 range (KVQ_EOVERFLOW).
+constexpr int32_t kStatusOverflow = 6;
+
 // Device view of one plane for one sequence-major layout.
 struct PlaneView {
     uint8_t *codes;
@@ -80,6 +84,7 @@ struct DecodeArgs {
     const float *app_k;
     const float *app_v;
     int app_rows;
+    int32_t *dev_status;     // nullable: kStatusOverflow when a V_hat beyond binary16 is met
 };
 
 struct PrefillArgs {
@@ -93,6 +98,7 @@ struct PrefillArgs {
     int n_q_heads;
     int gqa;
     float scale_log2;
+    int32_t *dev_status;     // nullable: kStatusOverflow when a K_hat / V_hat beyond binary16 is met
 };
 
 // Decode split size (rows per workgroup) and split count for a call.

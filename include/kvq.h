@@ -35,6 +35,19 @@
  * KVQ_EUNSUPPORTED: there is no fallback path.  A failed kernel launch returns
  * KVQ_EHIP.
  *
+ * Operand range of the attention calls.  Their matrix-core operands are
+ * binary16: decode rounds each dequantized V value x_hat = code * dq to
+ * binary16, prefill each K and V value, so |x_hat| must stay within 65504.
+ * The block codecs keep every finite input within that unless a group's
+ * largest magnitude reaches about 57000 (4-bit codecs) or 65000 (q8_0).  A
+ * value beyond it becomes an infinity in the operand and makes every result
+ * it can affect non-finite.  Every attention call takes an optional device
+ * status word (dev_status, int32, may be NULL): a kernel that writes a
+ * non-finite result stores KVQ_EOVERFLOW there (queries must be finite, so a
+ * non-finite result can only come from such a value); nothing is stored
+ * otherwise, so the caller initializes it.  The status is written by the
+ * device, after the call returns.
+ *
  * Cache layout (one "plane" = the K or the V cache of one layer).  Rows are
  * grouped in blocks of KVQ_BLOCK_ROWS = 32 consecutive positions of one
  * (sequence, kv-head):
@@ -79,7 +92,9 @@ typedef enum {
     KVQ_EUNSUPPORTED = 2, /* valid but unsupported combination (no fallback exists)   */
     KVQ_ERANGE = 3,       /* a position/length outside the plane's capacity           */
     KVQ_EWORKSPACE = 4,   /* workspace missing or smaller than required               */
-    KVQ_EHIP = 5          /* the HIP runtime reported an error                        */
+    KVQ_EHIP = 5,         /* the HIP runtime reported an error                        */
+    KVQ_EOVERFLOW = 6     /* (device status word) a dequantized K or V value the call  */
+                          /* read lies beyond the binary16 range of its operands       */
 } kvq_status;
 
 /* One K or V cache plane of one layer.  head_dim must be 64, 128 or 256 and a
@@ -159,11 +174,12 @@ size_t kvq_decode_workspace_bytes(const kvq_layer *L, int32_t n_q_heads, int32_t
  * n_q_heads / n_kv_heads must be an integer in [1, KVQ_MAX_GQA].
  * Precision: fp32 statistics and accumulation; the matrix-core operands are
  * binary16 (query as a hi+lo pair, probabilities and dequantized V rounded to
- * nearest-even).  |v_hat| must stay below 65504. */
+ * nearest-even); |v_hat| beyond 65504 is reported through dev_status (see
+ * "Operand range" above). */
 kvq_status kvq_attend_decode(const kvq_layer *L, const float *q, const int64_t *seq_len,
                              int32_t n_seqs, int32_t n_q_heads, int64_t max_len,
                              float softmax_scale, float *out, void *workspace, size_t ws_bytes,
-                             void *hip_stream);
+                             int32_t *dev_status, void *hip_stream);
 
 /* ---- multi-query decode (den_llama.cpp, "Ship command": the server drafts
  * up to two tokens per step with multi-token prediction, so a verifying decode
@@ -188,7 +204,7 @@ size_t kvq_decode_mq_workspace_bytes(const kvq_layer *L, int32_t n_q_heads, int3
 kvq_status kvq_attend_decode_mq(const kvq_layer *L, const float *q, const int64_t *seq_len,
                                 int32_t n_seqs, int32_t q_len, int32_t n_q_heads, int64_t max_len,
                                 float softmax_scale, float *out, void *workspace, size_t ws_bytes,
-                                void *hip_stream);
+                                int32_t *dev_status, void *hip_stream);
 
 /* ---- fused append + decode (den_llama.cpp, "What's in the fork": the
  * quantize-on-write path and the FlashAttention reader of the same codec,
@@ -205,7 +221,7 @@ kvq_status kvq_attend_decode_mq(const kvq_layer *L, const float *q, const int64_
 kvq_status kvq_append_attend_decode(const kvq_layer *L, const float *k_new, const float *v_new,
                                     const float *q, const int64_t *seq_len, int32_t n_seqs,
                                     int32_t n_q_heads, int64_t max_len, float softmax_scale, float *out,
-                                    void *workspace, size_t ws_bytes, void *hip_stream);
+                                    void *workspace, size_t ws_bytes, int32_t *dev_status, void *hip_stream);
 
 /* For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid allocation):
@@ -222,7 +238,7 @@ kvq_status kvq_append_attend_decode(const kvq_layer *L, const float *k_new, cons
 kvq_status kvq_append_attend_decode_noalloc(const kvq_layer *L, const float *k_new, const float *v_new,
                                             const float *q, const int64_t *seq_len, int32_t n_seqs,
                                             int32_t n_q_heads, int64_t max_len, float softmax_scale, float *out,
-                                            void *hip_stream);
+                                            int32_t *dev_status, void *hip_stream);
 /* The scratch size of kvq_append_attend_decode_noalloc (host only). */
 size_t kvq_noalloc_scratch_bytes(void);
 
@@ -235,7 +251,7 @@ kvq_status kvq_append_attend_decode_mq(const kvq_layer *L, const float *k_new, c
                                        const float *q, const int64_t *seq_len, int32_t n_seqs,
                                        int32_t q_len, int32_t n_q_heads, int64_t max_len,
                                        float softmax_scale, float *out, void *workspace, size_t ws_bytes,
-                                       void *hip_stream);
+                                       int32_t *dev_status, void *hip_stream);
 
 /* ---- paged planes (den_llama.cpp, "Adaptive KV streaming (contributed)": a
  * bounded device pool of resident KV pages; here the pool itself, addressed
@@ -277,7 +293,7 @@ size_t kvq_paged_decode_workspace_bytes(const kvq_paged_layer *P, int32_t n_q_he
 kvq_status kvq_paged_attend_decode_mq(const kvq_paged_layer *P, const float *q, const int64_t *seq_len,
                                       int32_t n_seqs, int32_t q_len, int32_t n_q_heads, int64_t max_len,
                                       float softmax_scale, float *out, void *workspace, size_t ws_bytes,
-                                      void *hip_stream);
+                                      int32_t *dev_status, void *hip_stream);
 
 /* kvq_append_attend_decode_mq over paged planes (the new rows go through
  * the table too). */
@@ -285,7 +301,7 @@ kvq_status kvq_paged_append_attend_decode_mq(const kvq_paged_layer *P, const flo
                                              const float *q, const int64_t *seq_len, int32_t n_seqs,
                                              int32_t q_len, int32_t n_q_heads, int64_t max_len,
                                              float softmax_scale, float *out, void *workspace, size_t ws_bytes,
-                                             void *hip_stream);
+                                             int32_t *dev_status, void *hip_stream);
 
 /* ---- chunked-prefill attention (den_llama.cpp, "Results": prefill with the
  * quantized cache and 2048-token micro-batches; Llaminar, "GPU Graph
@@ -303,11 +319,11 @@ size_t kvq_prefill_workspace_bytes(const kvq_layer *L, int32_t n_q_heads, int32_
  * rounded once to binary16 for the matrix cores; each (token, head) query
  * column is scaled by a power of two (largest value in [1, 2)) before its
  * binary16 rounding, so any bfloat16 magnitude is accepted; accumulation and
- * softmax are fp32.  K and V values must lie within the binary16 range
- * (|x| <= 65504). */
+ * softmax are fp32.  K and V values beyond the binary16 range are reported
+ * through dev_status (see "Operand range" above). */
 kvq_status kvq_attend_prefill(const kvq_layer *L, const uint16_t *q_bf16, int32_t seq, int64_t pos0,
                               int32_t n_tokens, int32_t n_q_heads, float softmax_scale, float *out,
-                              void *workspace, size_t ws_bytes, void *hip_stream);
+                              void *workspace, size_t ws_bytes, int32_t *dev_status, void *hip_stream);
 
 /* kvq_attend_prefill over paged planes (den_llama.cpp, "Adaptive KV streaming
  * (contributed)": the device pool of resident KV pages, read through the
@@ -318,7 +334,7 @@ kvq_status kvq_attend_prefill(const kvq_layer *L, const uint16_t *q_bf16, int32_
  * entry lies outside the pool read as zeros (key and value 0). */
 kvq_status kvq_paged_attend_prefill(const kvq_paged_layer *P, const uint16_t *q_bf16, int32_t seq, int64_t pos0,
                                     int32_t n_tokens, int32_t n_q_heads, float softmax_scale, float *out,
-                                    void *workspace, size_t ws_bytes, void *hip_stream);
+                                    void *workspace, size_t ws_bytes, int32_t *dev_status, void *hip_stream);
 
 /* ---- dequant (den_llama.cpp, "What's in the fork": convert; "Results":
  * dequant bit-identical to the CPU reference) ----------------------------- */

@@ -70,14 +70,14 @@ def _call_decode(L, q=0x1000, seq_len=0x2000, n_seqs=1, hq=4, max_len=64, out=0x
                  ws_bytes=1 << 30):
     lib = B.load_library()
     return lib.kvq_attend_decode(ctypes.byref(L), q, seq_len, n_seqs, hq, max_len, 0.1, out, ws,
-                                 ws_bytes, None)
+                                 ws_bytes, None, None)
 
 
 def test_validation_errors_return_before_launch():
     lib = B.load_library()
     good = B._Layer(_fake_plane(role=0), _fake_plane(codec="q4_0", role=1, codes=0x30000, scales=0x40000))
     # decode: every failing argument -> exact status, nothing enqueued (no GPU here)
-    assert lib.kvq_attend_decode(None, 1, 1, 1, 4, 64, 0.1, 1, 1, 1, None) == 1
+    assert lib.kvq_attend_decode(None, 1, 1, 1, 4, 64, 0.1, 1, 1, 1, None, None) == 1
     assert _call_decode(good, q=0) == 1
     assert _call_decode(good, q=0x1004) == 1                      # misaligned q
     assert _call_decode(good, hq=3) == 1                          # not a multiple of Hkv
@@ -103,8 +103,8 @@ def test_validation_errors_return_before_launch():
     assert lib.kvq_append(ctypes.byref(good), 0x7000, 0, 0, 0x6000, 4, None, None) == 1
     assert lib.kvq_append(ctypes.byref(good), 0x7000, 0, 0x5000, 0x6000, 0, None, None) == 0
     # prefill
-    assert lib.kvq_attend_prefill(ctypes.byref(good), 0x1000, 0, 60, 8, 4, 0.1, 0x3000, 0, 0, None) == 3
-    assert lib.kvq_attend_prefill(ctypes.byref(good), 0x1000, 1, 0, 8, 4, 0.1, 0x3000, 0, 0, None) == 1
+    assert lib.kvq_attend_prefill(ctypes.byref(good), 0x1000, 0, 60, 8, 4, 0.1, 0x3000, 0, 0, None, None) == 3
+    assert lib.kvq_attend_prefill(ctypes.byref(good), 0x1000, 1, 0, 8, 4, 0.1, 0x3000, 0, 0, None, None) == 1
     # dequant
     p = _fake_plane()
     assert lib.kvq_dequant(ctypes.byref(p), 0, 60, 8, 0x3000, None) == 3
@@ -119,7 +119,7 @@ def test_multi_query_decode_validation():
 
     def call(q_len, hq=4, ws_bytes=1 << 30):
         return lib.kvq_attend_decode_mq(ctypes.byref(good), 0x1000, 0x2000, 1, q_len, hq, 64, 0.1, 0x3000,
-                                        0x4000, ws_bytes, None)
+                                        0x4000, ws_bytes, None, None)
     assert call(0) == 1                 # no query
     assert call(65) == 1                # above KVQ_MAX_QUERIES
     assert call(2, hq=3) == 1           # not a multiple of Hkv
@@ -138,11 +138,11 @@ def test_fused_append_decode_validation():
 
     def call(k, v, ws_bytes=1 << 30, q=0x1000):
         return lib.kvq_append_attend_decode(ctypes.byref(good), k, v, q, 0x2000, 1, 4, 64, 0.1, 0x3000,
-                                            0x4000, ws_bytes, None)
+                                            0x4000, ws_bytes, None, None)
 
     def call_mq(k, v, q_len):
         return lib.kvq_append_attend_decode_mq(ctypes.byref(good), k, v, 0x1000, 0x2000, 1, q_len, 4, 64, 0.1,
-                                               0x3000, 0x4000, 1 << 30, None)
+                                               0x3000, 0x4000, 1 << 30, None, None)
     assert call(None, 0x5000) == 1          # k_new missing
     assert call(0x5000, None) == 1          # v_new missing
     assert call(0x5004, 0x6000) == 1        # k_new not 16-byte aligned
@@ -225,7 +225,7 @@ def test_f16_control_codec_sizes_and_pairing():
     assert lib.kvq_append(ctypes.byref(mixed), 0x5000, 0x6000, 0x1000, 0x2000, 4, None, None) == 2
     wide = B._Layer(f16(0, d=256), f16(1, d=256, codes=0x30000))
     assert _call_decode(wide) == 2
-    assert lib.kvq_attend_prefill(ctypes.byref(both), 0x1000, 0, 0, 16, 4, 0.1, 0x3000, None, 0, None) == 2
+    assert lib.kvq_attend_prefill(ctypes.byref(both), 0x1000, 0, 0, 16, 4, 0.1, 0x3000, None, 0, None, None) == 2
 
 
 @pytest.mark.parametrize("codec", ["q8_0", "q4_0", "q4_g64"])
@@ -256,11 +256,11 @@ def test_noalloc_size_check_runs_before_the_device():
     big = B._Layer(_fake_plane(heads=8, seqs=64, cap=131072),
                    _fake_plane(codec="q4_0", role=1, heads=8, seqs=64, cap=131072, codes=0x30000, scales=0x40000))
     st = lib.kvq_append_attend_decode_noalloc(ctypes.byref(big), 0x5000, 0x6000, 0x1000, 0x2000, 64, 32, 131072,
-                                              0.1, 0x3000, None)
+                                              0.1, 0x3000, None, None)
     assert st == 4 and b"no-allocation" in lib.kvq_last_error()
     # argument errors are still reported first
     assert lib.kvq_append_attend_decode_noalloc(ctypes.byref(big), None, 0x6000, 0x1000, 0x2000, 1, 32, 64, 0.1,
-                                                0x3000, None) == 1
+                                                0x3000, None, None) == 1
 
 
 def test_paged_prefill_validation():
@@ -269,16 +269,18 @@ def test_paged_prefill_validation():
                                                              scales=0x40000))
     P = B._PagedLayer(pool, 0x7000, 2, 4)   # 2 sequences x 4 pages of 64 rows
     call = lambda seq=0, pos0=0, T=16, hq=4, q=0x1000, out=0x3000: lib.kvq_paged_attend_prefill(
-        ctypes.byref(P), q, seq, pos0, T, hq, 0.1, out, None, 0, None)
+        ctypes.byref(P), q, seq, pos0, T, hq, 0.1, out, None, 0, None, None)
     assert call(seq=2) == 1                      # only 2 sequences in the table
     assert call(pos0=250, T=7) == 3              # past 4 pages x 64 rows
     assert call(q=0) == 1
     assert call(hq=3) == 1
     assert call(T=0) == 0                        # nothing to do
     bad = B._PagedLayer(pool, 0, 2, 4)
-    assert lib.kvq_paged_attend_prefill(ctypes.byref(bad), 0x1000, 0, 0, 16, 4, 0.1, 0x3000, None, 0, None) == 1
+    assert lib.kvq_paged_attend_prefill(ctypes.byref(bad), 0x1000, 0, 0, 16, 4, 0.1, 0x3000, None, 0, None,
+                                        None) == 1
     # more pages than a paged prefill addresses
     big = B._PagedLayer(B._Layer(_fake_plane(cap=32, seqs=8), _fake_plane(codec="q4_0", role=1, cap=32, seqs=8,
                                                                           codes=0x30000, scales=0x40000)),
                         0x7000, 1, 10000)
-    assert lib.kvq_paged_attend_prefill(ctypes.byref(big), 0x1000, 0, 200000, 16, 4, 0.1, 0x3000, None, 0, None) == 2
+    assert lib.kvq_paged_attend_prefill(ctypes.byref(big), 0x1000, 0, 200000, 16, 4, 0.1, 0x3000, None, 0, None,
+                                        None) == 2
