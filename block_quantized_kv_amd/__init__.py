@@ -11,6 +11,7 @@ from ._binding import (  # noqa: F401
     BLOCK_ROWS,
     CODECS,
     KVQ_EOVERFLOW,
+    KVQ_EWAIT,
     KvqError,
     Plane,
     Layer,
@@ -24,6 +25,7 @@ from ._binding import (  # noqa: F401
     kvq_attend_decode_mq,
     kvq_attend_prefill,
     kvq_dequant,
+    kvq_debug_append_wait,
     kvq_decode_workspace_bytes,
     decode_workspace,
     decode_mq_workspace,

@@ -15,8 +15,8 @@ GROUP = {"q8_0": 32, "q4_0": 32, "q4_g64": 64}
 ROLE_K, ROLE_V = 0, 1
 
 STATUS = {0: "KVQ_OK", 1: "KVQ_EINVAL", 2: "KVQ_EUNSUPPORTED", 3: "KVQ_ERANGE",
-          4: "KVQ_EWORKSPACE", 5: "KVQ_EHIP", 6: "KVQ_EOVERFLOW"}
-KVQ_EOVERFLOW = 6
+          4: "KVQ_EWORKSPACE", 5: "KVQ_EHIP", 6: "KVQ_EOVERFLOW", 7: "KVQ_EWAIT"}
+KVQ_EOVERFLOW, KVQ_EWAIT = 6, 7
 
 
 class KvqError(RuntimeError):
@@ -81,6 +81,7 @@ def load_library():
         "kvq_paged_attend_decode_mq": (i32, [PG, P, P, i32, i32, i32, i64, f32, P, P, sz, P, P]),
         "kvq_paged_append_attend_decode_mq": (i32, [PG, P, P, P, P, i32, i32, i32, i64, f32, P, P, sz, P, P]),
         "kvq_paged_attend_prefill": (i32, [PG, P, i32, i64, i32, i32, f32, P, P, sz, P, P]),
+        "kvq_debug_append_wait": (i32, [i32, i32]),
         "kvq_status_str": (ctypes.c_char_p, [i32]),
         "kvq_last_error": (ctypes.c_char_p, []),
     }
@@ -90,6 +91,12 @@ def load_library():
         fn.argtypes = args
     _lib = lib
     return lib
+
+
+def kvq_debug_append_wait(polls: int, hold_flag: bool = False) -> None:
+    """The fused append's wait bound (polls) and, for tests only, a switch
+    that keeps the appending wave from signalling."""
+    _check(load_library().kvq_debug_append_wait(polls, 1 if hold_flag else 0))
 
 
 def kvq_status_str(status: int) -> str:

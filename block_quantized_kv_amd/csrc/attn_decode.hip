@@ -882,15 +882,18 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     // NS - 1 other slots: waiting until at most that many remain is exact.
     // Waits until wave 0 has raised the flag (its stores of the new rows are
     // complete).  Wave 0 raises it without waiting for any other wave, so the
-    // wait ends; the iteration cap only bounds it.
+    // wait ends; the poll count only bounds it (a.append_wait_polls).  A wait
+    // that runs out goes on, so the kernel always ends, and reports it: the
+    // block it then reads may hold the new rows' old bytes.
     auto wait_appended = [&]() {
-        for (int it = 0; it < (1 << 20); ++it) {
+        for (int it = 0; it < a.append_wait_polls; ++it) {
             uint32_t f;
             ds_rd(f, lds0, C::OFF_CNT + 4);
             lds_wait<1>(&f);
-            if (__builtin_amdgcn_readfirstlane(f) != 0u) break;
+            if (__builtin_amdgcn_readfirstlane(f) != 0u) return;
             __builtin_amdgcn_s_sleep(2);
         }
+        if (a.dev_status && lane == 0) *a.dev_status = kStatusWaitExpired;
     };
     auto grab = [&]() -> int {
         uint32_t v = 0;
@@ -915,7 +918,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
             vm_wait<0>();
             // in flag mode wave 0 always gets here (its second block exists),
             // and this complete wait covered its stores of the new rows
-            if (flag_mode && wave == 0) ds_wr(lds0, 1u, C::OFF_CNT + 4);
+            if (flag_mode && wave == 0 && !a.hold_append_flag) ds_wr(lds0, 1u, C::OFF_CNT + 4);
             Payload<D, KC, VC> pl;
             read_slot<D, KC, VC>(pl, a16, a8, a4, aks, avs, C::SLOT);
             const int nxt = grab();

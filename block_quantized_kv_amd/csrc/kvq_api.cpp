@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -65,6 +66,10 @@ kvq_status check_layer(const kvq_layer *L) {
     return KVQ_OK;
 }
 
+// the fused append's wait bound (polls) and its test switch
+std::atomic<int> g_append_wait_polls{1 << 20};
+std::atomic<int> g_hold_append_flag{0};
+
 kvq::PlaneView view(const kvq_plane &P) {
     kvq::PlaneView v;
     v.codes = static_cast<uint8_t *>(P.codes);
@@ -87,7 +92,24 @@ kvq_status hip_status(hipError_t e, const char *what) {
 
 }  // namespace
 
+namespace kvq {
+void set_append_wait(int polls, int hold_flag) {
+    g_append_wait_polls.store(polls);
+    g_hold_append_flag.store(hold_flag);
+}
+void get_append_wait(int *polls, int *hold_flag) {
+    *polls = g_append_wait_polls.load();
+    *hold_flag = g_hold_append_flag.load();
+}
+}  // namespace kvq
+
 extern "C" {
+
+kvq_status kvq_debug_append_wait(int32_t polls, int32_t hold_flag) {
+    if (polls < 0) return fail(KVQ_EINVAL, "polls %d < 0", polls);
+    kvq::set_append_wait(polls, hold_flag ? 1 : 0);
+    return ok();
+}
 
 size_t kvq_row_code_bytes(int32_t codec, int32_t head_dim) {
     if (!codec_valid(codec) || head_dim <= 0 || head_dim % kvq::group_size(codec) != 0) return 0;
@@ -272,6 +294,7 @@ kvq_status attend_decode(const kvq_layer *L, const kvq::PageTable &pt, const flo
     a.max_splits = p.max_splits;
     a.scale_log2 = softmax_scale * 1.4426950408889634f;
     a.dev_status = dev_status;
+    kvq::get_append_wait(&a.append_wait_polls, &a.hold_append_flag);
     const int64_t qstride = (int64_t)n_q_heads * L->k.head_dim;  // floats per query
     a.q_seq_stride = (int64_t)q_len * qstride;
     // launches of `per` queries each, in order on the stream (they share the
@@ -500,6 +523,7 @@ const char *kvq_status_str(int32_t status) {
         case KVQ_EWORKSPACE: return "KVQ_EWORKSPACE: workspace missing or too small";
         case KVQ_EHIP: return "KVQ_EHIP: HIP runtime error";
         case KVQ_EOVERFLOW: return "KVQ_EOVERFLOW: a dequantized value beyond the binary16 operand range";
+        case KVQ_EWAIT: return "KVQ_EWAIT: the fused append's bounded wait ran out";
         default: return "unknown kvq_status";
     }
 }

@@ -12,6 +12,9 @@ namespace kvq {
 // Stored in a call's dev_status by the attention kernels when a dequantized
 // K or V value they read exceeds the binary16 range (KVQ_EOVERFLOW).
 constexpr int32_t kStatusOverflow = 6;
+// Stored by the fused append + decode when a wave's bounded wait for the
+// appending wave's stores ran out (KVQ_EWAIT).
+constexpr int32_t kStatusWaitExpired = 7;
 
 // Device view of one plane for one sequence-major layout.
 struct PlaneView {
@@ -84,8 +87,16 @@ struct DecodeArgs {
     const float *app_k;
     const float *app_v;
     int app_rows;
-    int32_t *dev_status;     // nullable: kStatusOverflow when a V_hat beyond binary16 is met
+    int32_t *dev_status;     // nullable: kStatusOverflow / kStatusWaitExpired
+    // bounded wait of the fused append (polls of the appending wave's flag),
+    // and, for tests of its expiry only, a switch that keeps the flag down
+    int append_wait_polls;
+    int hold_append_flag;
 };
+
+// The fused append's wait bound and its test switch (kvq_debug_append_wait).
+void set_append_wait(int polls, int hold_flag);
+void get_append_wait(int *polls, int *hold_flag);
 
 struct PrefillArgs {
     PlaneView k, v;

@@ -93,8 +93,11 @@ typedef enum {
     KVQ_ERANGE = 3,       /* a position/length outside the plane's capacity           */
     KVQ_EWORKSPACE = 4,   /* workspace missing or smaller than required               */
     KVQ_EHIP = 5,         /* the HIP runtime reported an error                        */
-    KVQ_EOVERFLOW = 6     /* (device status word) a dequantized K or V value the call  */
+    KVQ_EOVERFLOW = 6,    /* (device status word) a dequantized K or V value the call  */
                           /* read lies beyond the binary16 range of its operands       */
+    KVQ_EWAIT = 7         /* (device status word) a fused append + decode wave's       */
+                          /* bounded wait for the appending wave ran out: it went on   */
+                          /* and may have read the new rows' old bytes                 */
 } kvq_status;
 
 /* One K or V cache plane of one layer.  head_dim must be 64, 128 or 256 and a
@@ -345,6 +348,16 @@ kvq_status kvq_dequant(const kvq_plane *P, int32_t seq, int64_t row0, int64_t n_
                        void *hip_stream);
 
 /* ---- diagnostics --------------------------------------------------------- */
+
+/* The fused append + decode calls (kvq_append_attend_decode and its
+ * variants) let the waves that read the block holding a new row wait, in
+ * LDS, for the wave that stores it, at most `polls` polls (default 2^20,
+ * far beyond any real delay); a wait that runs out goes on and stores
+ * KVQ_EWAIT in the call's dev_status, so no kernel can hang on it.
+ * hold_flag != 0 keeps the storing wave from signalling, so that tests can
+ * drive that path; it is for tests only.  Applies to calls made after it
+ * (process-wide).  KVQ_EINVAL for polls < 0. */
+kvq_status kvq_debug_append_wait(int32_t polls, int32_t hold_flag);
 
 const char *kvq_status_str(int32_t status);
 /* Message of the last failing call on this thread ("" if none). */

@@ -179,3 +179,42 @@ def test_workload_64k_step_matches_unfused(gpu):
     _same_cache(fused, plain)
     assert np.isfinite(out).all()
     assert rel_err(out, ref) <= SAME
+
+
+def test_bounded_wait_that_runs_out_is_reported(gpu):
+    """The fused append's wait for the appending wave is bounded: with the
+    appending wave held from signalling (a test switch) and a 16-poll bound,
+    the waves that read the new row's block give up, go on, and store
+    KVQ_EWAIT; the kernel ends normally and the new row is still stored as
+    kvq_append stores it."""
+    from block_quantized_kv_amd import KVQ_EWAIT, kvq_debug_append_wait
+    cfg = workloads.DECODE_64K  # 1024-row splits: the new row's block is read late in its split
+    n, H, d = cfg.ctx, cfg.n_kv_heads, cfg.head_dim
+    kc, vc = cfg.layers[0]
+    L = Layer.create(kc, vc, d, H, 1, cfg.capacity, device=gpu)
+    k = workloads.kv_rows(cfg, 0, 0, "k", 0, n, gpu)
+    v = workloads.kv_rows(cfg, 0, 0, "v", 0, n, gpu)
+    append_rows(L, k[: n - 1], v[: n - 1], 0, 0)
+    q = workloads.queries(cfg, 0, gpu)
+    lens = torch.tensor([n], dtype=torch.int64, device=gpu)
+    st = torch.zeros(1, dtype=torch.int32, device=gpu)
+    kvq_debug_append_wait(16, hold_flag=True)
+    try:
+        out = kvq_append_attend_decode(L, k[n - 1:].contiguous(), v[n - 1:].contiguous(), q, lens, n, cfg.scale,
+                                       dev_status=st)
+        torch.cuda.synchronize()
+    finally:
+        kvq_debug_append_wait(1 << 20, hold_flag=False)
+    assert st.item() == KVQ_EWAIT
+    assert out.shape == q.shape
+    from block_quantized_kv_amd import layout
+    for plane, rows in ((L.k, k), (L.v, v)):
+        codes, scales = layout.plane_to_rows(plane, seq=0)
+        want_c, want_s = oracle.quantize_rows(plane.codec, rows[n - 1].cpu().numpy())
+        assert np.array_equal(codes[0, :, n - 1], want_c) and np.array_equal(scales[0, :, n - 1], want_s)
+    # with the default bound the same call stores nothing
+    st.zero_()
+    kvq_append_attend_decode(L, k[n - 1:].contiguous(), v[n - 1:].contiguous(), q, lens, n, cfg.scale,
+                             dev_status=st)
+    torch.cuda.synchronize()
+    assert st.item() == 0

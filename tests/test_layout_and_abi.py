@@ -284,3 +284,9 @@ def test_paged_prefill_validation():
                         0x7000, 1, 10000)
     assert lib.kvq_paged_attend_prefill(ctypes.byref(big), 0x1000, 0, 200000, 16, 4, 0.1, 0x3000, None, 0, None,
                                         None) == 2
+
+
+def test_debug_append_wait_validation():
+    lib = B.load_library()
+    assert lib.kvq_debug_append_wait(-1, 0) == 1
+    assert lib.kvq_debug_append_wait(1 << 20, 0) == 0
