@@ -46,7 +46,9 @@ _lib = None
 
 
 def library_path() -> str:
-    return os.path.join(HERE, "libkvq.so")
+    """libkvq.so beside this file, or the file KVQ_LIBRARY names (another
+    build of the same library, e.g. one with host sanitizers)."""
+    return os.environ.get("KVQ_LIBRARY") or os.path.join(HERE, "libkvq.so")
 
 
 def load_library():

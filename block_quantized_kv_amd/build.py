@@ -76,5 +76,41 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
     return LIB
 
 
+# Host sanitizers for the C ABI's host side (argument validation, sizing,
+# dispatch): every -fsanitize= reaches the host compiler only (-Xarch_host),
+# the device code is built as usual.  The library then expects the clang
+# sanitizer runtime to be preloaded (LD_PRELOAD=sanitizer_runtime()).
+SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+            "-Xarch_host", "-g"]
+
+
+def sanitizer_runtime() -> str:
+    return subprocess.run(["/opt/rocm/llvm/bin/clang", "--print-file-name=libclang_rt.asan-x86_64.so"],
+                          capture_output=True, text=True, check=True).stdout.strip()
+
+
+def build_sanitized(out_dir: str, jobs: int | None = None) -> str:
+    """libkvq.so with sanitized host code, in out_dir (not in place)."""
+    os.makedirs(out_dir, exist_ok=True)
+    jobs = jobs or min(len(SOURCES), max(1, os.cpu_count() or 1))
+
+    def one(src):
+        obj = os.path.join(out_dir, src.replace("/", "_").replace(".", "_") + ".o")
+        lang = ["-x", "hip"] if src.endswith(".hip") else []
+        cmd = [hipcc()] + _common_flags() + SANITIZE + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+        r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+        if r.returncode != 0:
+            raise subprocess.CalledProcessError(r.returncode, cmd, r.stdout)
+        return obj
+
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(one, SOURCES))
+    lib = os.path.join(out_dir, "libkvq.so")
+    subprocess.run([hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-Xarch_host", "-fsanitize=address",
+                    "-Xarch_host", "-fsanitize=undefined", "-o", lib] + objs, check=True)
+    return lib
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))

@@ -50,9 +50,10 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+    override = os.environ.get("KVQ_ORACLE_LIBRARY")
+    if not override and (not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC)):
         build(force=True)
-    lib = ctypes.CDLL(LIB)
+    lib = ctypes.CDLL(override or LIB)
     P = ctypes.c_void_p
     lib.kvq_oracle_f32_to_f16.argtypes = [ctypes.c_float]
     lib.kvq_oracle_f32_to_f16.restype = ctypes.c_uint16
