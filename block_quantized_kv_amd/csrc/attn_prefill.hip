@@ -23,7 +23,13 @@
 //  * The bf16 query is widened and scaled by a power of two per (token,
 //    head) column so that its largest value lies in [1, 2), then rounded to
 //    binary16 (exact for every value within 2^-14 of that maximum); the power
-//    of two is folded into the column's score scale.
+//    of two is folded into the column's score scale.  The softmax scale's
+//    sign goes into the query as well, so the column's factor is positive:
+//    the maximum is taken over the raw scores, and the factor multiplies a
+//    score inside the FMA that subtracts the running maximum before exp2.
+//  * The 8 XCDs each have their own L2 and receive workgroups round-robin;
+//    the column groups of one kv-head are placed on one XCD, so the K/V rows
+//    they all sweep come from HBM about once per kv-head.
 //  * Each wave computes S^T = K_hat Q^T (A = K_hat rows from LDS, B = its
 //    query columns held in registers) and O^T += V_hat^T P^T on
 //    v_mfma_f32_16x16x32_f16.  The S^T accumulator layout is the P^T operand
@@ -36,6 +42,8 @@
 //    the products of tile k; tile k+2's codes are loaded into registers and
 //    its scales staged in LDS during iteration k, so the dequant never waits
 //    for memory.
+#include <cfloat>
+
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -237,9 +245,18 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
     f16bits *lds = reinterpret_cast<f16bits *>(smem);
 
     const int G = a.gqa;
-    const int kvh = blockIdx.y;
     const int ncols = a.n_tokens * G;
-    const int col0 = blockIdx.x * C::COLS;
+    // Workgroups are dealt to the 8 XCDs, each with its own L2, round-robin
+    // by id.  Every column group of a kv-head sweeps the same K/V rows in the
+    // same order, so where the count allows, the groups of one kv-head share
+    // an XCD: workgroup L takes entry (L % 8) * (n / 8) + L / 8 of the
+    // kv-head-major list of (kv-head, column group) pairs, and its rows come
+    // from that XCD's L2 after the first group has read them.
+    const int ncg = (ncols + C::COLS - 1) / C::COLS;
+    const int nwg = (int)gridDim.x, L = (int)blockIdx.x;
+    const int pair = nwg % 8 == 0 ? (L % 8) * (nwg / 8) + L / 8 : L;
+    const int kvh = pair / ncg;
+    const int col0 = (pair % ncg) * C::COLS;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int h16 = lane & 15, q4 = lane >> 4;
 
@@ -275,14 +292,18 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
         mx = fmaxf(mx, shfl_xor(mx, 16));
         mx = fmaxf(mx, shfl_xor(mx, 32));
         const int e = mx > 0.0f ? ilogbf(mx) : 0;
-        const float nrm = ldexpf(1.0f, -e);
-        cscale[nt] = a.scale_log2 * ldexpf(1.0f, e);
+        // the scale's sign goes into the operand, so the column's factor is
+        // positive (at least FLT_MIN: a zero scale still weighs every visible
+        // row alike) and the largest raw score gives the largest scaled one
+        cscale[nt] = fmaxf(ldexpf(fabsf(a.scale_log2), e), FLT_MIN);
+        const bool neg = a.scale_log2 < 0.0f;
 #pragma unroll
         for (int ks = 0; ks < C::KSTEPS; ++ks)
 #pragma unroll
             for (int s2 = 0; s2 < 8; ++s2) {
                 const uint32_t wd = raw[ks][s2 >> 1];
-                qop[nt][ks][s2] = (_Float16)(__builtin_bit_cast(float, (s2 & 1) ? (wd & 0xFFFF0000u) : (wd << 16)) * nrm);
+                const float x = __builtin_bit_cast(float, (s2 & 1) ? (wd & 0xFFFF0000u) : (wd << 16));
+                qop[nt][ks][s2] = (_Float16)ldexpf(neg ? -x : x, -e);
             }
     }
 
@@ -499,7 +520,7 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
                 f4 acc = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ks = 0; ks < C::KSTEPS; ++ks) acc = mfma16x16x32(kop[ks], qop[nt][ks], acc);
-                S[nt][mt] = acc * cscale[nt];
+                S[nt][mt] = acc;  // unscaled: the column's factor enters with the exponent
             }
         }
     };
@@ -526,6 +547,7 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
                 for (int r = 0; r < 4; ++r) mx = fmaxf(mx, S[nt][mt][r]);
             mx = fmaxf(mx, shfl_xor(mx, 16));
             mx = fmaxf(mx, shfl_xor(mx, 32));
+            mx *= cscale[nt];  // -inf stays -inf (the factor is positive)
             // a column with every row of this tile masked keeps its state
             const bool raise = mx > m_run[nt] + kPRescaleThreshold;
             if (__any(raise)) {
@@ -540,7 +562,7 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
             for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const float p = fast_exp2(S[nt][mt][r] - m_run[nt]);  // 0 when masked
+                    const float p = fast_exp2(fmaf(S[nt][mt][r], cscale[nt], -m_run[nt]));  // 0 when masked
                     l_run[nt] += p;
                     P[nt][mt >> 1][4 * (mt & 1) + r] = (_Float16)p;
                 }
@@ -671,7 +693,7 @@ hipError_t launch_ptyped_p(const PrefillArgs &a, hipStream_t s) {
         if (e != hipSuccess) return e;
     }
     const int ncols = a.n_tokens * a.gqa;
-    const dim3 grid((unsigned)((ncols + C::COLS - 1) / C::COLS), (unsigned)a.k.n_kv_heads);
+    const dim3 grid((unsigned)((ncols + C::COLS - 1) / C::COLS * a.k.n_kv_heads));
     prefill_kernel<D, KC, VC, PAGED><<<grid, dim3(kPThreads), lds, s>>>(a);
     return hipGetLastError();
 }

@@ -5,7 +5,7 @@ Bar: max|gpu - oracle| / max|oracle| <= 1e-2, the prefill tolerance (the
 matrix cores see K_hat, V_hat, the scaled query and P rounded to binary16).
 Covered: the tiny prefill enumerated in full, ragged prefix/chunk lengths,
 every codec pair, head_dim 64/128/256, several GQA ratios, a chunk at
-position 0, queries far outside the binary16 range, the chunk of a middle sequence of a three-sequence
+position 0, queries far outside the binary16 range, negative and zero softmax scales, the chunk of a middle sequence of a three-sequence
 cache over several workgroups at every head_dim, and the 2048-token chunk over a 32768-token prefix on 4096
 (token, head) rows: every head of the first and last 32 tokens and 2048 random
 pairs.
@@ -24,7 +24,7 @@ TOL = 1e-2
 CODECS = ["q8_0", "q4_0", "q4_g64"]
 
 
-def _run(gpu, kc, vc, d, hq, hkv, P, T, seed=0, sample=None, cap_extra=0, qmul=1.0, capsys=None):
+def _run(gpu, kc, vc, d, hq, hkv, P, T, seed=0, sample=None, cap_extra=0, qmul=1.0, capsys=None, scale_mul=1.0):
     q, k, v = workloads.prefill_inputs(gpu, seed_layer=seed, prefix=P, chunk=T, n_q_heads=hq,
                                        n_kv_heads=hkv, head_dim=d)
     if qmul != 1.0:  # a power of two: exact in bf16
@@ -32,7 +32,7 @@ def _run(gpu, kc, vc, d, hq, hkv, P, T, seed=0, sample=None, cap_extra=0, qmul=1
     cap = (P + T + 31) // 32 * 32 + cap_extra
     layer = Layer.create(kc, vc, d, hkv, 1, cap, device=gpu)
     append_rows(layer, k, v, 0, 0)                      # prefix and chunk rows
-    scale = 1.0 / np.sqrt(d) / qmul
+    scale = 1.0 / np.sqrt(d) / qmul * scale_mul
     out = kvq_attend_prefill(layer, q, 0, P, scale).cpu().numpy()
     kh = oracle.quant_dequant(kc, k.cpu().numpy().transpose(1, 0, 2).copy())
     vh = oracle.quant_dequant(vc, v.cpu().numpy().transpose(1, 0, 2).copy())
@@ -84,6 +84,13 @@ def test_query_outside_binary16_range(gpu, qmul):
     # column is scaled by a power of two before the binary16 rounding, and the
     # softmax scale divided by qmul makes the exact result the unscaled one
     _run(gpu, "q8_0", "q4_g64", 128, 8, 2, 70, 45, seed=11, qmul=qmul)
+
+
+@pytest.mark.parametrize("scale_mul", [-1.0, 0.0, -0.0, 3.0])
+def test_softmax_scale_sign_and_zero(gpu, scale_mul):
+    # any non-NaN scale: a negative one favours the smallest scores, a zero
+    # one weighs every visible row alike (the mean of V_hat up to the diagonal)
+    _run(gpu, "q8_0", "q4_0", 128, 8, 2, 70, 45, seed=13, scale_mul=scale_mul)
 
 
 def test_capacity_slack_rows_ignored(gpu):
