@@ -448,6 +448,12 @@ kvq_status attend_prefill(const kvq_layer *L, const kvq::PageTable &pt, const ui
         return fail(KVQ_EINVAL, "n_q_heads %d not a multiple of n_kv_heads %d", n_q_heads,
                     L->k.n_kv_heads);
     const int gqa = n_q_heads / L->k.n_kv_heads;
+    // (token, head) columns are int on the device, and one workgroup per 128
+    // or more of them per kv-head must fit a one-dimensional grid
+    const int64_t ncols = (int64_t)n_tokens * gqa;
+    if (ncols > (int64_t)1 << 30 || (ncols + 127) / 128 * L->k.n_kv_heads > (int64_t)INT32_MAX)
+        return fail(KVQ_EUNSUPPORTED, "%d tokens x %d q-heads per kv-head x %d kv-heads exceed one launch",
+                    n_tokens, gqa, L->k.n_kv_heads);
     if (!(softmax_scale == softmax_scale)) return fail(KVQ_EINVAL, "softmax_scale is NaN");
     if (!kvq::prefill_supported(L->k.codec, L->v.codec, L->k.head_dim))
         return fail(KVQ_EUNSUPPORTED, "no prefill kernel for this codec pair/head_dim");

@@ -105,6 +105,11 @@ def test_validation_errors_return_before_launch():
     # prefill
     assert lib.kvq_attend_prefill(ctypes.byref(good), 0x1000, 0, 60, 8, 4, 0.1, 0x3000, 0, 0, None, None) == 3
     assert lib.kvq_attend_prefill(ctypes.byref(good), 0x1000, 1, 0, 8, 4, 0.1, 0x3000, 0, 0, None, None) == 1
+    # more (token, head) columns than one launch holds: 2^21 tokens x 1024 q-heads per kv-head
+    wide = B._Layer(_fake_plane(cap=1 << 22), _fake_plane(codec="q4_0", role=1, cap=1 << 22, codes=0x30000,
+                                                          scales=0x40000))
+    assert lib.kvq_attend_prefill(ctypes.byref(wide), 0x1000, 0, 0, 1 << 21, 2048, 0.1, 0x3000, 0, 0, None,
+                                  None) == 2
     # dequant
     p = _fake_plane()
     assert lib.kvq_dequant(ctypes.byref(p), 0, 60, 8, 0x3000, None) == 3
