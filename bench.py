@@ -180,10 +180,11 @@ def read_traffic(which: str = "decode"):
 # (--prefill-only) or over the decode step (--step-only).  MFMA busy fraction =
 # SQ_VALU_MFMA_BUSY_CYCLES / (SIMDs x cycles), where GRBM_GUI_ACTIVE reads the
 # sum of the 8 XCDs' busy cycles; SQ_INSTS_VALU includes the MFMA
-# instructions.  A summary records a hash of the kernel's sources and is used
+# instructions; the L2 hit rate comes from TCC_HIT / TCC_MISS summed over the
+# channels of every XCD.  A summary records a hash of the kernel's sources and is used
 # only while they are unchanged.
 BUSY_COUNTERS = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA",
-                 "SQ_INSTS_LDS", "SQ_WAVES", "GRBM_GUI_ACTIVE"]
+                 "SQ_INSTS_LDS", "SQ_WAVES", "GRBM_GUI_ACTIVE", "TCC_HIT_sum", "TCC_MISS_sum"]
 N_SIMDS, N_XCDS = 1024, 8
 BUSY_FILES = {
     "prefill": (os.path.join(ROOT, "profiles", "prefill2k_over32k_counters.txt"), "prefill_kernel", PREFILL_SOURCES,
@@ -209,6 +210,7 @@ def write_busy_summary(which: str, pmc_dir: str):
         f"#   rocprofv3 --pmc {' '.join(BUSY_COUNTERS)} -d <dir> -o run --output-format csv -- {cmd}",
         f"#   python bench.py --write-busy-summary {which} <dir>",
         "# mfma_busy_frac = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8 XCDs)",
+        "# tcc_hit_rate = TCC_HIT_sum / (TCC_HIT_sum + TCC_MISS_sum) (L2 requests of all 8 XCDs)",
         f"source_hash: {source_hash(sources)}",
         f"dispatches: {n}",
     ] + [f"{c}: {vals[c]:.6g}" for c in BUSY_COUNTERS] + [
@@ -217,6 +219,7 @@ def write_busy_summary(which: str, pmc_dir: str):
         f"valu_insts_per_wave: {vals['SQ_INSTS_VALU'] / waves:.6g}",
         f"mfma_insts_per_wave: {vals['SQ_INSTS_MFMA'] / waves:.6g}",
         f"lds_insts_per_wave: {vals['SQ_INSTS_LDS'] / waves:.6g}",
+        f"tcc_hit_rate: {vals['TCC_HIT_sum'] / max(1.0, vals['TCC_HIT_sum'] + vals['TCC_MISS_sum']):.4f}",
     ]
     with open(path, "w") as fh:
         fh.write("\n".join(lines) + "\n")
@@ -239,6 +242,7 @@ def read_busy(which: str):
         return {"mfma_busy_frac": float(kv["mfma_busy_frac"]),
                 "valu_insts_per_wave": float(kv["valu_insts_per_wave"]),
                 "mfma_insts_per_wave": float(kv["mfma_insts_per_wave"]),
+                "tcc_hit_rate": float(kv["tcc_hit_rate"]) if "tcc_hit_rate" in kv else None,
                 "source": os.path.relpath(path, ROOT)}
     except (OSError, KeyError, ValueError):
         return None

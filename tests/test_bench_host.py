@@ -82,7 +82,7 @@ def test_busy_summary_round_trip(tmp_path, monkeypatch):
     d = tmp_path / "busy"
     vals = {"SQ_VALU_MFMA_BUSY_CYCLES": 1024 * 300.0, "SQ_BUSY_CYCLES": 1.0, "SQ_WAVE_CYCLES": 1.0,
             "SQ_INSTS_VALU": 2048 * 500.0, "SQ_INSTS_MFMA": 2048 * 64.0, "SQ_INSTS_LDS": 2048 * 40.0,
-            "SQ_WAVES": 2048.0, "GRBM_GUI_ACTIVE": 8 * 1000.0}
+            "SQ_WAVES": 2048.0, "GRBM_GUI_ACTIVE": 8 * 1000.0, "TCC_HIT_sum": 900.0, "TCC_MISS_sum": 100.0}
     _csv(str(d / "run_counter_collection.csv"), [("prefill_kernel<128>", k, v) for k, v in vals.items()])
     path, kname, sources, cmd = bench.BUSY_FILES["prefill"]
     out = tmp_path / "prefill_counters.txt"
@@ -93,6 +93,7 @@ def test_busy_summary_round_trip(tmp_path, monkeypatch):
     assert got["mfma_busy_frac"] == pytest.approx(0.3)
     assert got["valu_insts_per_wave"] == pytest.approx(500.0)
     assert got["mfma_insts_per_wave"] == pytest.approx(64.0)
+    assert got["tcc_hit_rate"] == pytest.approx(0.9)
     out.write_text(out.read_text().replace(bench.source_hash(sources), "0000000000000000"))
     assert bench.read_busy("prefill") is None
 
