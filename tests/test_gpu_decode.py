@@ -4,7 +4,8 @@ oracle's own quantization of the same fp32 rows).
 Bar: max|gpu - oracle| / max|oracle| <= 1e-3 over the outputs of one call
 (per layer), the decode tolerance.  Covered: all
 9 codec pairs, the f16 control codec (head_dim 64/128), head_dim 64/128/256, GQA 1..16, lengths 0, 1, ragged tails and
-several tiles, split-count sweeps, softmax invariants, and the tiny workload
+several tiles, device lengths beyond the host bound (cut to it) and negative
+ones (empty), split-count sweeps, softmax invariants, and the tiny workload
 configuration in full (the others, every head, in test_gpu_fullsize.py).
 """
 import numpy as np
@@ -80,6 +81,35 @@ def test_split_sweep(gpu, max_len_factor):
     n = 3000
     _run_case(gpu, "q4_0", "q8_0", 128, hq=8, hkv=2, lens=[n], cap=n * 8 + 32,
               max_len=n * max_len_factor, seed=11)
+
+
+@pytest.mark.parametrize("lens,max_len", [([5000], 3000), ([5000, 100, -3, 2999], 3000), ([-1], 64)])
+def test_device_lengths_clamped_to_max_len(gpu, lens, max_len):
+    """The call attends rows [0, min(seq_len[b], max_len)) of every sequence, a
+    negative device length counting as 0: lengths past the host bound are cut
+    to it, in the one-sequence grid and in the batched work list alike."""
+    rng = np.random.default_rng(21)
+    d, hq, hkv = 128, 8, 2
+    S, cap = len(lens), 5024
+    layer = Layer.create("q8_0", "q4_0", d, hkv, S, cap, device=gpu)
+    q = rng.standard_normal((S, hq, d)).astype(np.float32)
+    ks, vs = [], []
+    for s in range(S):
+        k = rng.standard_normal((cap, hkv, d)).astype(np.float32)
+        v = rng.standard_normal((cap, hkv, d)).astype(np.float32)
+        append_rows(layer, torch.from_numpy(k).to(gpu), torch.from_numpy(v).to(gpu), s, 0)
+        ks.append(k)
+        vs.append(v)
+    scale = 1.0 / np.sqrt(d)
+    out = kvq_attend_decode(layer, torch.from_numpy(q).to(gpu), torch.tensor(lens, dtype=torch.int64, device=gpu),
+                            max_len, scale).cpu().numpy()
+    for s, n in enumerate(lens):
+        eff = min(max(n, 0), max_len)
+        if eff == 0:
+            assert np.array_equal(out[s], np.zeros_like(out[s]))
+            continue
+        ref = _oracle_decode("q8_0", "q4_0", q[s], ks[s], vs[s], eff, scale)
+        assert rel_err(out[s], ref) <= TOL, (s, n, eff)
 
 
 def test_large_and_small_magnitudes(gpu):

@@ -93,6 +93,13 @@ def test_softmax_scale_sign_and_zero(gpu, scale_mul):
     _run(gpu, "q8_0", "q4_0", 128, 8, 2, 70, 45, seed=13, scale_mul=scale_mul)
 
 
+def test_xcd_placement_of_column_groups(gpu):
+    # 8 kv-heads x 3 column groups of 256 (token, head) columns: 24 workgroups,
+    # dealt to the XCDs by a permutation that keeps each kv-head's groups
+    # together; every (kv-head, column group) pair must still be computed once
+    _run(gpu, "q8_0", "q4_0", 128, 16, 8, 500, 300, seed=17)
+
+
 def test_capacity_slack_rows_ignored(gpu):
     # capacity beyond the chunk: never-written rows after it must not matter
     _run(gpu, "q8_0", "q4_0", 128, 8, 2, 40, 30, cap_extra=64)
