@@ -84,7 +84,6 @@ TRAFFIC = {
                 "one kvq_attend_prefill call, 2048-token chunk over a 32768-row prefix (q8_0 K / q4_0 V, 32/8 "
                 "heads, head_dim 128)"),
 }
-TRAFFIC_FILE = TRAFFIC["decode"][0]
 
 
 def source_hash(sources) -> str:
@@ -94,10 +93,6 @@ def source_hash(sources) -> str:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
-
-
-def decode_source_hash() -> str:
-    return source_hash(DECODE_SOURCES)
 
 
 def _pmc_mean(path_glob: str, counter: str, name_pat: str):
