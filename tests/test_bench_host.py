@@ -103,3 +103,12 @@ def test_more_than_one_gpu_is_refused():
                        text=True, cwd=ROOT, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_committed_counter_summaries_match_the_kernel_sources():
+    """Every counter-backed summary under profiles/ was taken on the kernel
+    sources as they stand: a kernel change without new counters fails here
+    (bench.py would otherwise report traffic and busy fractions as null)."""
+    for which in ("decode", "prefill"):
+        assert bench.read_traffic(which) is not None, f"profiles traffic summary of {which} is stale or missing"
+        assert bench.read_busy(which) is not None, f"profiles counter summary of {which} is stale or missing"
