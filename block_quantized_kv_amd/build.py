@@ -3,6 +3,7 @@
   libkvq.so        the HIP kernels of the attention path and the C ABI (include/kvq.h)
   libkvq_probe.so  on-box measurement helpers (include/kvq_probe.h), used by the
                    benchmark only; not linked into libkvq.so
+  tests/c_abi/decode_step  a plain-C program over the C ABI (the GPU tests run it)
 
 Sources compile in parallel; each library is linked from its own objects."""
 from __future__ import annotations
@@ -63,8 +64,30 @@ def _link(objs: list, lib: str) -> str:
     return lib
 
 
+# A plain-C user of the C ABI (tests/c_abi/decode_step.c): host code only,
+# built with the system C compiler against include/kvq.h, libkvq.so and the
+# HIP runtime; the GPU tests run it.
+C_EXAMPLE_SRC = os.path.join(ROOT, "tests", "c_abi", "decode_step.c")
+C_EXAMPLE_BIN = os.path.join(ROOT, "tests", "c_abi", "decode_step")
+
+
+def build_c_example(verbose: bool = False) -> str:
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    cmd = ["gcc", "-std=c11", "-O2", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.join(rocm, "include"), "-I", os.path.join(ROOT, "include"), C_EXAMPLE_SRC,
+           "-L", HERE, "-lkvq", "-L", os.path.join(rocm, "lib"), "-lamdhip64",
+           "-Wl,-rpath,$ORIGIN/../../block_quantized_kv_amd", "-Wl,-rpath," + os.path.join(rocm, "lib"),
+           "-o", C_EXAMPLE_BIN + ".tmp"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(C_EXAMPLE_BIN + ".tmp", C_EXAMPLE_BIN)
+    return C_EXAMPLE_BIN
+
+
 def build(verbose: bool = False, jobs: int | None = None) -> str:
-    """Compile every source with hipcc and link libkvq.so and libkvq_probe.so."""
+    """Compile every source with hipcc and link libkvq.so and libkvq_probe.so,
+    then the plain-C example that links libkvq.so."""
     objdir = os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
     srcs = SOURCES + PROBE_SOURCES
@@ -73,6 +96,7 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
         objs = list(ex.map(lambda s: _compile(s, objdir, verbose), srcs))
     _link(objs[:len(SOURCES)], LIB)
     _link(objs[len(SOURCES):], PROBE_LIB)
+    build_c_example(verbose)
     return LIB
 
 

@@ -295,3 +295,14 @@ def test_debug_append_wait_validation():
     lib = B.load_library()
     assert lib.kvq_debug_append_wait(-1, 0) == 1
     assert lib.kvq_debug_append_wait(1 << 20, 0) == 0
+
+
+def test_plain_c_example_is_built_and_starts():
+    """The plain-C user of the C ABI (tests/c_abi/decode_step.c) is built with
+    the libraries and links against libkvq.so; without arguments it prints its
+    usage and exits before touching a GPU."""
+    import subprocess
+    from block_quantized_kv_amd import build
+    assert os.path.exists(build.C_EXAMPLE_BIN), "build it with block_quantized_kv_amd/build.py"
+    r = subprocess.run([build.C_EXAMPLE_BIN], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 1 and "usage" in r.stderr
