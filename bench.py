@@ -539,7 +539,7 @@ def main():
 
 
 def stream_peak(torch, dev, reps: int = 48) -> dict:
-    """On-box streaming-read rate: kvq_probe_stream_read over 64 MiB windows
+    """Measured streaming-read rate of this GPU: kvq_probe_stream_read over 64 MiB windows
     rotating through 1 GiB (so the 256 MB last-level cache cannot serve them),
     for 256, 512 and 1024 workgroups of 8 waves; the best is the practical
     ceiling the decode roofline is also quoted against."""
@@ -815,12 +815,12 @@ def run_prefill(torch, dev, args):
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
                          "traffic": read_traffic("prefill"), "kv_bytes": kv_bytes,
-                         "onbox_mfma_peak": mp, "frac_of_onbox_peak": round(tf / mp["tflops"], 4),
+                         "measured_mfma_peak": mp, "frac_of_measured_mfma_peak": round(tf / mp["tflops"], 4),
                          "counters": read_busy("prefill")}}
 
 
 def mfma_peak(torch, dev) -> dict:
-    """On-box matrix-core peak: kvq_probe_mfma_f16 (a register-only loop of
+    """Measured matrix-core peak of this GPU: kvq_probe_mfma_f16 (a register-only loop of
     v_mfma_f32_16x16x32_f16, the prefill kernel's product) for 256, 512 and
     1024 workgroups of 8 waves; the best is the practical ceiling the prefill
     roofline is also quoted against."""

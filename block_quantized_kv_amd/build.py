@@ -1,7 +1,7 @@
 """Builds the gfx950 libraries with hipcc, in place:
 
   libkvq.so        the HIP kernels of the attention path and the C ABI (include/kvq.h)
-  libkvq_probe.so  on-box measurement helpers (include/kvq_probe.h), used by the
+  libkvq_probe.so  measurement helpers (the GPU's own streaming-read and matrix-core rates) (include/kvq_probe.h), used by the
                    benchmark only; not linked into libkvq.so
   tests/c_abi/decode_step  a plain-C program over the C ABI (the GPU tests run it)
 

@@ -1,4 +1,4 @@
-// mfma_probe.hip -- on-box matrix-core throughput of v_mfma_f32_16x16x32_f16,
+// mfma_probe.hip -- measured matrix-core throughput of v_mfma_f32_16x16x32_f16,
 // the instruction the prefill kernel's products run on: the practical ceiling
 // its MFMA roofline is quoted against beside the published dense peak.  Not
 // part of the attention path.

@@ -1,4 +1,4 @@
-// stream_probe.hip -- on-box streaming-read rate, the practical ceiling that
+// stream_probe.hip -- measured streaming-read rate, the practical ceiling that
 // the decode kernel's HBM roofline is quoted against beside the published
 // peak.  Not part of the attention path.
 //

@@ -1,5 +1,5 @@
-"""ctypes binding of libkvq_probe.so (include/kvq_probe.h): the on-box
-streaming-read and matrix-core loop measurements the benchmark quotes its
+"""ctypes binding of libkvq_probe.so (include/kvq_probe.h): the GPU's own
+streaming-read and matrix-core loop rates, which the benchmark quotes its
 rooflines against.  Not part of the attention path."""
 from __future__ import annotations
 

@@ -1,4 +1,4 @@
-/* kvq_probe.h -- on-box measurement helpers, built as their own library
+/* kvq_probe.h -- measurement helpers (the GPU's own rates), built as their own library
  * (libkvq_probe.so), not part of the attention path and not linked into
  * libkvq.so.  The decode kernel's HBM roofline is reported against the
  * published 8 TB/s peak and against what a plain streaming read reaches on the
