@@ -5,7 +5,7 @@ quantization with length L - q_len + i + 1 (zero rows -> output 0).
 
 Bar: max|gpu - oracle| / max|oracle| <= 1e-3 per call, as for decode.
 Covered: q_len 1-4 on every head_dim, GQA ratios whose q_len * gqa exceeds
-one 16-column tile (several launches per call), sequences shorter than
+one 16-column tile (several launches per call), the largest q_len (64), sequences shorter than
 q_len, the newest rows alone in the last split, many splits, q_len = 1
 against kvq_attend_decode bit for bit (the 64K Q4_G64 workload with two
 queries per step, every head, is in test_gpu_fullsize.py).
@@ -70,6 +70,14 @@ def test_codec_pairs_two_queries(gpu, kc, vc):
 def test_more_columns_than_one_tile(gpu, gqa, q_len):
     # gqa * q_len > 16: the call runs several launches over the same K/V
     _case(gpu, "q8_0", "q4_0", 64, hq=2 * gqa, hkv=2, lens=[300], q_len=q_len, seed=gqa * 31 + q_len)
+
+
+@pytest.mark.parametrize("gqa", [1, 4])
+def test_the_largest_query_count(gpu, gqa):
+    # q_len at the limit (KVQ_MAX_QUERIES = 64): 4 or 16 launches of 16
+    # columns over the same K/V, the first queries of the shorter sequence
+    # seeing nothing
+    _case(gpu, "q8_0", "q4_g64", 128, hq=2 * gqa, hkv=2, lens=[900, 40], q_len=64, seed=64 + gqa)
 
 
 def test_sequences_shorter_than_the_queries(gpu):
