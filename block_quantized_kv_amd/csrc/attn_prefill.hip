@@ -624,10 +624,20 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
         // some column of this wave sees rows of this tile (false from some
         // tile on, for every later one)
         const bool act = tile * kTileRows <= wave_max_diag;
-        if (act) scores(tile);
-        if (have_p) {
+        if (act && have_p) {
+            // the usual case: the products of this tile's scores and of the
+            // previous tile's PV are independent, and in one block the
+            // scheduler can hide each stream's LDS operand reads behind the
+            // other's matrix products
+            scores(tile);
             pv(tile - 1);
             have_p = false;
+        } else {
+            if (act) scores(tile);
+            if (have_p) {
+                pv(tile - 1);
+                have_p = false;
+            }
         }
         if (act) {
             if (late) {
