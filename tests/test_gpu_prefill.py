@@ -6,8 +6,8 @@ matrix cores see K_hat, V_hat, the scaled query and P rounded to binary16).
 Covered: the tiny prefill enumerated in full, ragged prefix/chunk lengths,
 every codec pair, head_dim 64/128/256, several GQA ratios, a chunk at
 position 0, queries far outside the binary16 range, negative and zero softmax scales, the chunk of a middle sequence of a three-sequence
-cache over several workgroups at every head_dim, and the 2048-token chunk over a 32768-token prefix on every
-one of its 65536 (token, head) rows.
+cache over several workgroups at every head_dim, graph replays against the eager call, and the 2048-token
+chunk over a 32768-token prefix on every one of its 65536 (token, head) rows.
 """
 import numpy as np
 import pytest
@@ -140,3 +140,30 @@ def test_middle_sequence_over_several_workgroups(gpu, kc, vc, d):
     assert np.isfinite(out).all()
     err = rel_err(out, ref)
     assert err <= TOL, (kc, vc, d, err)
+
+
+def test_graph_replay_matches_eager(gpu):
+    """kvq_attend_prefill captured in a HIP graph: every replay equals the
+    eager call bit for bit (the call only enqueues its kernel), with eager
+    work on the device between the replays."""
+    d, hq, hkv, P, T = 128, 8, 2, 300, 130
+    q, k, v = workloads.prefill_inputs(gpu, seed_layer=23, prefix=P, chunk=T, n_q_heads=hq, n_kv_heads=hkv,
+                                       head_dim=d)
+    layer = Layer.create("q8_0", "q4_0", d, hkv, 1, (P + T + 31) // 32 * 32, device=gpu)
+    append_rows(layer, k, v, 0, 0)
+    out = torch.empty(T, hq, d, device=gpu)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        kvq_attend_prefill(layer, q, 0, P, d ** -0.5, out=out)
+    torch.cuda.synchronize()
+    eager = out.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        kvq_attend_prefill(layer, q, 0, P, d ** -0.5, out=out)
+    for i in range(4):
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), i
+        kvq_attend_prefill(layer, q, 0, P, 0.5 * d ** -0.5)  # eager work between replays
