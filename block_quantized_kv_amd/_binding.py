@@ -199,9 +199,20 @@ def _need(t, name, dtype, shape):
                          f"got {t.dtype} {tuple(t.shape)} on {t.device}")
 
 
+def _one_device(owner, **named):
+    """Every tensor (and stream) of a call must sit on the cache's device: a
+    pointer into another GPU's memory would reach the kernels unchecked."""
+    dev = owner.device
+    for name, t in named.items():
+        if t is not None and t.device != dev:
+            raise ValueError(f"{name} is on {t.device}; the cache is on {dev}")
+
+
 def kvq_append(layer: Layer, k_new, v_new, seq_idx, pos, dev_status=None, stream=None) -> None:
     """k_new/v_new fp32 [n_tokens][n_kv_heads][head_dim] (either may be None),
     seq_idx int32 [n_tokens], pos int64 [n_tokens] -- all device tensors."""
+    _one_device(layer.k.codes, v_planes=layer.v.codes, k_new=k_new, v_new=v_new, seq_idx=seq_idx, pos=pos,
+                dev_status=dev_status, stream=stream)
     n = int(seq_idx.numel())
     _need(seq_idx, "seq_idx", torch.int32, (n,))
     _need(pos, "pos", torch.int64, (n,))
@@ -229,6 +240,8 @@ def decode_workspace(layer: Layer, n_q_heads: int, n_seqs: int, max_len: int):
 def kvq_attend_decode(layer: Layer, q, seq_len, max_len: int, softmax_scale: float, out=None,
                       workspace=None, dev_status=None, stream=None):
     """q fp32 [n_seqs][n_q_heads][head_dim]; seq_len int64 [n_seqs] (device)."""
+    _one_device(layer.k.codes, v_planes=layer.v.codes, q=q, seq_len=seq_len, out=out, workspace=workspace,
+                dev_status=dev_status, stream=stream)
     n_seqs, hq, d = q.shape
     _need(q, "q", torch.float32, (n_seqs, hq, layer.k.head_dim))
     _need(seq_len, "seq_len", torch.int64, (n_seqs,))
@@ -261,6 +274,8 @@ def kvq_attend_decode_mq(layer: Layer, q, seq_len, max_len: int, softmax_scale: 
                          workspace=None, dev_status=None, stream=None):
     """q fp32 [n_seqs][q_len][n_q_heads][head_dim]; query i of sequence b sits at
     row seq_len[b] - q_len + i (already appended) and attends rows up to it."""
+    _one_device(layer.k.codes, v_planes=layer.v.codes, q=q, seq_len=seq_len, out=out, workspace=workspace,
+                dev_status=dev_status, stream=stream)
     n_seqs, q_len, hq, d = q.shape
     _need(q, "q", torch.float32, (n_seqs, q_len, hq, layer.k.head_dim))
     _need(seq_len, "seq_len", torch.int64, (n_seqs,))
@@ -283,6 +298,8 @@ def kvq_append_attend_decode(layer: Layer, k_new, v_new, q, seq_len, max_len: in
     """k_new, v_new fp32 [n_seqs][n_kv_heads][head_dim] become row seq_len[b] - 1
     of sequence b; then q fp32 [n_seqs][n_q_heads][head_dim] attends as
     kvq_attend_decode (one launch does both)."""
+    _one_device(layer.k.codes, v_planes=layer.v.codes, k_new=k_new, v_new=v_new, q=q, seq_len=seq_len, out=out,
+                workspace=workspace, dev_status=dev_status, stream=stream)
     n_seqs, hq, d = q.shape
     H = layer.k.n_kv_heads
     _need(q, "q", torch.float32, (n_seqs, hq, layer.k.head_dim))
@@ -313,6 +330,8 @@ def kvq_append_attend_decode_noalloc(layer: Layer, k_new, v_new, q, seq_len, max
     """kvq_append_attend_decode without a workspace: the library's own device
     scratch holds the split partials (the call allocates nothing; `out` must
     be given)."""
+    _one_device(layer.k.codes, v_planes=layer.v.codes, k_new=k_new, v_new=v_new, q=q, seq_len=seq_len, out=out,
+                dev_status=dev_status, stream=stream)
     n_seqs, hq, d = q.shape
     H = layer.k.n_kv_heads
     _need(q, "q", torch.float32, (n_seqs, hq, layer.k.head_dim))
@@ -332,6 +351,8 @@ def kvq_append_attend_decode_mq(layer: Layer, k_new, v_new, q, seq_len, max_len:
     """k_new, v_new fp32 [n_seqs][q_len][n_kv_heads][head_dim] become rows
     seq_len[b] - q_len + i; then q fp32 [n_seqs][q_len][n_q_heads][head_dim]
     attends as kvq_attend_decode_mq (the first launch appends)."""
+    _one_device(layer.k.codes, v_planes=layer.v.codes, k_new=k_new, v_new=v_new, q=q, seq_len=seq_len, out=out,
+                workspace=workspace, dev_status=dev_status, stream=stream)
     n_seqs, q_len, hq, d = q.shape
     H = layer.k.n_kv_heads
     _need(q, "q", torch.float32, (n_seqs, q_len, hq, layer.k.head_dim))
@@ -362,6 +383,8 @@ def kvq_attend_prefill(layer: Layer, q_bf16, seq: int, pos0: int, softmax_scale:
                        workspace=None, dev_status=None, stream=None):
     """q_bf16 bfloat16 [n_tokens][n_q_heads][head_dim] (device); rows of the chunk
     must already be appended at positions pos0..pos0+n_tokens-1."""
+    _one_device(layer.k.codes, v_planes=layer.v.codes, q_bf16=q_bf16, out=out, workspace=workspace,
+                dev_status=dev_status, stream=stream)
     T, hq, d = q_bf16.shape
     _need(q_bf16, "q_bf16", torch.bfloat16, (T, hq, layer.k.head_dim))
     if out is None:
@@ -380,6 +403,7 @@ def kvq_attend_prefill(layer: Layer, q_bf16, seq: int, pos0: int, softmax_scale:
 
 def kvq_dequant(plane: Plane, seq: int, row0: int, n_rows: int, out=None, stream=None):
     """-> fp32 [n_kv_heads][n_rows][head_dim] of x_hat = code * scale."""
+    _one_device(plane.codes, out=out, stream=stream)
     if out is None:
         out = torch.empty((plane.n_kv_heads, n_rows, plane.head_dim), dtype=torch.float32,
                           device=plane.codes.device)
@@ -409,6 +433,8 @@ class PagedLayer:
 
 def kvq_paged_append(pl: PagedLayer, k_new, v_new, seq_idx, pos, dev_status=None, stream=None) -> None:
     """kvq_append through the block table (pos is the row within the sequence)."""
+    _one_device(pl.pool.k.codes, v_planes=pl.pool.v.codes, block_table=pl.block_table, k_new=k_new, v_new=v_new,
+                seq_idx=seq_idx, pos=pos, dev_status=dev_status, stream=stream)
     n = int(seq_idx.numel())
     _need(seq_idx, "seq_idx", torch.int32, (n,))
     _need(pos, "pos", torch.int64, (n,))
@@ -434,6 +460,8 @@ def paged_decode_workspace(pl: PagedLayer, n_q_heads: int, n_seqs: int, q_len: i
 
 def _paged_decode(pl: PagedLayer, k_new, v_new, q, seq_len, max_len, softmax_scale, out, workspace, dev_status,
                   stream):
+    _one_device(pl.pool.k.codes, v_planes=pl.pool.v.codes, block_table=pl.block_table, k_new=k_new, v_new=v_new,
+                q=q, seq_len=seq_len, out=out, workspace=workspace, dev_status=dev_status, stream=stream)
     n_seqs, q_len, hq, d = q.shape
     H, D = pl.pool.k.n_kv_heads, pl.pool.k.head_dim
     _need(q, "q", torch.float32, (n_seqs, q_len, hq, D))
@@ -480,6 +508,8 @@ def kvq_paged_attend_prefill(pl: PagedLayer, q_bf16, seq: int, pos0: int, softma
                              dev_status=None, stream=None):
     """kvq_attend_prefill over paged planes: q_bf16 bfloat16 [n_tokens][n_q_heads][head_dim];
     the chunk's rows must already be appended (through the table) at pos0..pos0+n_tokens-1."""
+    _one_device(pl.pool.k.codes, v_planes=pl.pool.v.codes, block_table=pl.block_table, q_bf16=q_bf16, out=out,
+                dev_status=dev_status, stream=stream)
     T, hq, d = q_bf16.shape
     _need(q_bf16, "q_bf16", torch.bfloat16, (T, hq, pl.pool.k.head_dim))
     if out is None:

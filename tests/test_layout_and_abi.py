@@ -306,3 +306,18 @@ def test_plain_c_example_is_built_and_starts():
     assert os.path.exists(build.C_EXAMPLE_BIN), "build it with block_quantized_kv_amd/build.py"
     r = subprocess.run([build.C_EXAMPLE_BIN], capture_output=True, text=True, timeout=60)
     assert r.returncode == 1 and "usage" in r.stderr
+
+
+def test_binding_rejects_tensors_on_another_device():
+    """Every tensor of a call must sit on the cache's device; the binding
+    refuses a mix before anything reaches the library (here a cache held in
+    host memory and queries on the meta device, so no GPU is needed)."""
+    import torch
+    layer = B.Layer.create("q8_0", "q4_0", 64, 1, 1, 32, device="cpu")
+    q = torch.empty(1, 4, 64, device="meta")
+    lens = torch.empty(1, dtype=torch.int64, device="meta")
+    with pytest.raises(ValueError, match="cache is on"):
+        B.kvq_attend_decode(layer, q, lens, 32, 0.1)
+    with pytest.raises(ValueError, match="cache is on"):
+        B.kvq_append(layer, torch.empty(1, 1, 64, device="meta"), None, torch.zeros(1, dtype=torch.int32),
+                     torch.zeros(1, dtype=torch.int64))
