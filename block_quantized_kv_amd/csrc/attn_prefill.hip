@@ -598,9 +598,9 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
     }
     __syncthreads();
     // Each tile passes through S (matrix cores), softmax (vector ALU) and PV
-    // (matrix cores).  Waves 0-3 run S(k), PV(k-1), softmax(k) between the
+    // (matrix cores).  Waves 0-3 run PV(k-1), S(k), softmax(k) between the
     // barriers of iteration k; waves 4-7 (the other wave of each SIMD) run
-    // softmax(k-1), S(k), PV(k-1): the two waves of a SIMD then use the matrix
+    // softmax(k-1), PV(k-1), S(k): the two waves of a SIMD then use the matrix
     // cores and the vector ALU at the same time instead of in lockstep.  A
     // tile's V_hat is therefore read one iteration after its K_hat (three
     // V_hat buffers).  Without room for three, every wave runs S(k),
@@ -625,12 +625,12 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
         // tile on, for every later one)
         const bool act = tile * kTileRows <= wave_max_diag;
         if (act && have_p) {
-            // the usual case: the products of this tile's scores and of the
-            // previous tile's PV are independent, and in one block the
+            // the usual case: the products of the previous tile's PV and of
+            // this tile's scores are independent, and in one block the
             // scheduler can hide each stream's LDS operand reads behind the
-            // other's matrix products
-            scores(tile);
+            // other's matrix products (PV first measured faster)
             pv(tile - 1);
+            scores(tile);
             have_p = false;
         } else {
             if (act) scores(tile);
