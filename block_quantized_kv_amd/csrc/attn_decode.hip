@@ -506,7 +506,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int h = lane & 15, q4 = lane >> 4;
-    const int x32 = 4 * (lane ^ 32);  // byte index of lane ^ 32 for ds_bpermute
     const int G = a.gqa;
     const int NC = G * a.q_len;  // columns: (query, head) pairs, query-major
     // this lane's column: query qi, head hh; it sees the rows of the split
@@ -655,7 +654,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
         float m = 0.0f;
 #pragma unroll
         for (int s = 0; s < 8; ++s) m = fmaxf(m, fabsf(qv[s]));
-        m = quad_max(m, x32);
+        m = quad_max(m);
         if (q4 == 0) ds_wr(lds0 + (wave * 16 + h) * 4, __builtin_bit_cast(uint32_t, m), C::OFF_TMAX);
     }
     if (tid == 0) {
@@ -690,7 +689,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
         }
         ds_wr(lds0 + wave * 2048 + lane * 16, __builtin_bit_cast(u4, hi8), C::OFF_QOP);
         ds_wr(lds0 + wave * 2048 + lane * 16, __builtin_bit_cast(u4, lo8), C::OFF_QOP + 1024);
-        cpart = quad_sum(cpart, x32);
+        cpart = quad_sum(cpart);
         if (q4 == 0) ds_wr(lds0 + (wave * 16 + h) * 4, __builtin_bit_cast(uint32_t, cpart), C::OFF_CORR);
     }
     lds_barrier();
@@ -797,7 +796,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
         float mx = S[0][0];
 #pragma unroll
         for (int i = 1; i < 8; ++i) mx = __builtin_elementwise_maximum(mx, S[i / 4][i % 4]);
-        mx = quad_max(mx, x32);
+        mx = quad_max(mx);
         const bool raise = mx > m_run + kRescaleThreshold;
         if (__any(raise)) {
             const float m_new = raise ? mx : m_run;
@@ -971,7 +970,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
     }
 
     // ---- merge the waves.
-    l_run = quad_sum(l_run, x32);
+    l_run = quad_sum(l_run);
     constexpr int D4 = D / 4;
     // writes item (col, c) of the merged result: the output when the call has
     // one split, else this split's partial (unnormalized O, max, sum).  A

@@ -289,8 +289,7 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
                 mx = fmaxf(mx, fabsf(__builtin_bit_cast(float, (s2 & 1) ? (wd & 0xFFFF0000u) : (wd << 16))));
             }
         }
-        mx = fmaxf(mx, shfl_xor(mx, 16));
-        mx = fmaxf(mx, shfl_xor(mx, 32));
+        mx = quad_max(mx);
         const int e = mx > 0.0f ? ilogbf(mx) : 0;
         // the scale's sign goes into the operand, so the column's factor is
         // positive (at least FLT_MIN: a zero scale still weighs every visible
@@ -531,6 +530,10 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
     auto softmax = [&](int tile) {
         const int row0 = tile * kTileRows;
         const bool diag_tile = row0 + kTileRows - 1 > wave_min_diag;
+        // the column maxima of all column tiles first, so that their
+        // cross-lane stages overlap, then one rescale decision for the wave
+        float mx[C::NT];
+        bool raise[C::NT];
 #pragma unroll
         for (int nt = 0; nt < C::NT; ++nt) {
             if (diag_tile) {
@@ -540,32 +543,50 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
                     for (int r = 0; r < 4; ++r)
                         if (row0 + 16 * mt + 4 * q4 + r > diag[nt]) S[nt][mt][r] = -INFINITY;
             }
-            float mx = -INFINITY;
+            mx[nt] = -INFINITY;
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) mx = fmaxf(mx, S[nt][mt][r]);
-            mx = fmaxf(mx, shfl_xor(mx, 16));
-            mx = fmaxf(mx, shfl_xor(mx, 32));
-            mx *= cscale[nt];  // -inf stays -inf (the factor is positive)
+                for (int r = 0; r < 4; ++r) mx[nt] = fmaxf(mx[nt], S[nt][mt][r]);
+        }
+#pragma unroll
+        for (int nt = 0; nt < C::NT; ++nt) mx[nt] = swap_max16(mx[nt]);
+        bool any_raise = false;
+#pragma unroll
+        for (int nt = 0; nt < C::NT; ++nt) {
+            // (the two lane-swap stages of all column tiles are interleaved)
+            mx[nt] = swap_max32(mx[nt]) * cscale[nt];  // -inf stays -inf (the factor is positive)
             // a column with every row of this tile masked keeps its state
-            const bool raise = mx > m_run[nt] + kPRescaleThreshold;
-            if (__any(raise)) {
-                const float m_new = raise ? mx : m_run[nt];
-                const float alpha = raise ? fast_exp2(m_run[nt] - m_new) : 1.0f;
+            raise[nt] = mx[nt] > m_run[nt] + kPRescaleThreshold;
+            any_raise |= raise[nt];
+        }
+        if (__any(any_raise)) {
+#pragma unroll
+            for (int nt = 0; nt < C::NT; ++nt) {
+                const float m_new = raise[nt] ? mx[nt] : m_run[nt];
+                const float alpha = raise[nt] ? fast_exp2(m_run[nt] - m_new) : 1.0f;
                 l_run[nt] *= alpha;
 #pragma unroll
                 for (int cb = 0; cb < C::CB; ++cb) O[nt][cb] *= alpha;
                 m_run[nt] = m_new;
             }
+        }
+#pragma unroll
+        for (int nt = 0; nt < C::NT; ++nt) {
 #pragma unroll
             for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float p = fast_exp2(fmaf(S[nt][mt][r], cscale[nt], -m_run[nt]));  // 0 when masked
-                    l_run[nt] += p;
-                    P[nt][mt >> 1][4 * (mt & 1) + r] = (_Float16)p;
-                }
+                for (int r = 0; r < 4; ++r)  // 0 when masked
+                    P[nt][mt >> 1][4 * (mt & 1) + r] = (_Float16)fast_exp2(fmaf(S[nt][mt][r], cscale[nt], -m_run[nt]));
+            // the row sum takes the binary16 probabilities the PV product
+            // uses, two per dot-product instruction (exact products by 1,
+            // fp32 sum)
+            const h2 one = h2{(_Float16)1.0f, (_Float16)1.0f};
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    l_run[nt] = __builtin_amdgcn_fdot2(h2{P[nt][ks][2 * j], P[nt][ks][2 * j + 1]}, one, l_run[nt], false);
         }
     };
     // ---- O^T += V_hat^T P^T; each V_hat operand read serves every column
@@ -674,9 +695,7 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
     bool bad = false;
 #pragma unroll
     for (int nt = 0; nt < C::NT; ++nt) {
-        float L = l_run[nt];
-        L += shfl_xor(L, 16);
-        L += shfl_xor(L, 32);
+        const float L = quad_sum(l_run[nt]);
         if (diag[nt] < 0) continue;
         const int col = col0 + (wave * C::NT + nt) * 16 + h16;
         const int t = col / G, hh = col % G;
