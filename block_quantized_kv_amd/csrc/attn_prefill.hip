@@ -51,8 +51,10 @@ namespace kvq {
 
 namespace {
 
-constexpr int kPWaves = 8;
-constexpr int kPThreads = 64 * kPWaves;
+// waves per workgroup: 8, and 12 at head_dim 256 (16 columns each, so that a
+// 2048-token chunk of 6-head groups over 4 kv-heads is 256 workgroups, one
+// round on the 256 compute units, instead of 384)
+constexpr int prefill_waves(int d) { return d == 256 ? 12 : 8; }
 constexpr int kTileRows = 64;
 constexpr float kPRescaleThreshold = 8.0f;
 
@@ -64,9 +66,11 @@ constexpr int clamp_width(int w, int lo, int hi) { return w < lo ? lo : (w > hi 
 // products: LEAD reads first, then each read follows NM / NR products, so
 // LEAD reads stay in flight ahead of the products that use them (left to
 // itself the scheduler waits on each read right after issuing it).  Four
-// reads ahead measured fastest at every head dim (2, 3, 5, 8 and 12 tried;
-// 6 spills at head_dim 128).
-constexpr int kReadLead = 4;
+// reads ahead measured fastest with 8 waves (2, 3, 5, 8 and 12 tried; 6 spills
+// at head_dim 128); with the 12 waves of head_dim 256 (168 VGPRs each) two
+// spill least and measured fastest.
+template <int D>
+constexpr int read_lead() { return D == 256 ? 2 : 4; }
 template <int NR, int NM, int LEAD_>
 __device__ __forceinline__ void reads_ahead_of_products() {
     constexpr int LEAD = LEAD_ < NR ? LEAD_ : NR - 1;
@@ -85,7 +89,9 @@ struct PCfg {
     static constexpr int KSTEPS = D / 32;
     static constexpr int CB = D / 16;
     static constexpr int NT = D == 256 ? 1 : 2;  // 16-column tiles per wave
-    static constexpr int COLS = kPWaves * 16 * NT;
+    static constexpr int WAVES = prefill_waves(D);
+    static constexpr int THREADS = 64 * WAVES;
+    static constexpr int COLS = WAVES * 16 * NT;
     static constexpr int KG = group_size(KC);
     static constexpr int VG = group_size(VC);
     static constexpr int VNG = D / VG;
@@ -133,13 +139,13 @@ struct PCfg {
     static constexpr int LDS_BYTES = OFF_PAGES + PAGE_LDS;
     static_assert(LDS_BYTES <= 160 * 1024, "the tiles fit in LDS");
     // dequant units per thread, and a tile's scales (both blocks, K then V)
-    static constexpr int UK = (K_UNITS + kPThreads - 1) / kPThreads;
-    static constexpr int UV = (V_UNITS + kPThreads - 1) / kPThreads;
+    static constexpr int UK = (K_UNITS + THREADS - 1) / THREADS;
+    static constexpr int UV = (V_UNITS + THREADS - 1) / THREADS;
     static constexpr int KSC_BYTES = 2 * 2 * K_BLOCK_SCALES;
     static constexpr int VSC_BYTES = 2 * 2 * V_BLOCK_SCALES;
     static constexpr int SC_BYTES = KSC_BYTES + VSC_BYTES;
     static_assert(KSC_BYTES % 16 == 0 && VSC_BYTES % 16 == 0, "scale spans are whole 16-byte pieces");
-    static_assert(SC_BYTES / 16 <= kPThreads, "one 16-byte scale piece per thread");
+    static_assert(SC_BYTES / 16 <= THREADS, "one 16-byte scale piece per thread");
     static_assert(K_UW % K_BPS == 0 && V_UW % V_BPC == 0, "units hold whole k-steps / channel blocks");
 };
 
@@ -259,7 +265,7 @@ __device__ __forceinline__ void deq_v_unit(int u, const uint32_t (&w)[PCfg<D, KC
 
 // PAGED: the planes are a page pool addressed through a.pt (else contiguous).
 template <int D, int KC, int VC, bool PAGED>
-__global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(PrefillArgs a) {
     using C = PCfg<D, KC, VC, PAGED>;
     extern __shared__ __align__(16) unsigned char smem[];
     f16bits *lds = reinterpret_cast<f16bits *>(smem);
@@ -345,7 +351,7 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
                                   ? (int64_t)ntiles * kTileRows : nblocks_plane * kBlockRows;
         const int npages = (int)((trows + a.pt.page_rows - 1) / a.pt.page_rows);
         int32_t *dst = reinterpret_cast<int32_t *>(smem + C::OFF_PAGES);
-        for (int i = tid; i < npages; i += kPThreads) dst[i] = a.pt.table[(int64_t)a.seq * a.pt.table_stride + i];
+        for (int i = tid; i < npages; i += C::THREADS) dst[i] = a.pt.table[(int64_t)a.seq * a.pt.table_stride + i];
     }
     // Where block gb of the sequence lives: code and scale pointers of each
     // plane; false when its page entry points outside the pool (the block
@@ -387,13 +393,13 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
             const uint8_t *vb = vcodes + b0 * C::V_BLOCK_BYTES;
 #pragma unroll
             for (int i = 0; i < C::UK; ++i) {
-                const int u = tid + i * kPThreads;
+                const int u = tid + i * C::THREADS;
                 if (u < C::K_UNITS && (two || u < C::K_UNITS / 2))
                     load_chunk<C::K_UW>(rk[i], kb + k_unit_offset<D, KC, VC>(u));
             }
 #pragma unroll
             for (int i = 0; i < C::UV; ++i) {
-                const int u = tid + i * kPThreads;
+                const int u = tid + i * C::THREADS;
                 if (u < C::V_UNITS && (two || u < C::V_UNITS / 2))
                     load_chunk<C::V_UW>(rv[i], vb + v_unit_offset<D, KC, VC>(u));
             }
@@ -418,7 +424,7 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
         for (int j = 0; j < 2; ++j) ok[j] = (j == 0 || two) && block_at(b0 + j, kb[j], vb[j], ksb[j], vsb[j]);
 #pragma unroll
         for (int i = 0; i < C::UK; ++i) {
-            const int u = tid + i * kPThreads;
+            const int u = tid + i * C::THREADS;
             if (u >= C::K_UNITS) continue;
             const int j = u >= C::K_UNITS / 2;  // units of block 0 come first
             if (ok[j])
@@ -429,7 +435,7 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
         }
 #pragma unroll
         for (int i = 0; i < C::UV; ++i) {
-            const int u = tid + i * kPThreads;
+            const int u = tid + i * C::THREADS;
             if (u >= C::V_UNITS) continue;
             const int j = u >= C::V_UNITS / 2;
             if (ok[j])
@@ -465,13 +471,13 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
         const uint16_t *vsc = ksc + C::KSC_BYTES / 2;
 #pragma unroll
         for (int i = 0; i < C::UK; ++i) {
-            const int u = tid + i * kPThreads;
+            const int u = tid + i * C::THREADS;
             if (u >= C::K_UNITS || (!two && u >= C::K_UNITS / 2)) continue;  // block 1 absent: rows unused
             deq_k_unit<D, KC, VC>(u, rk[i], ksc, khat);
         }
 #pragma unroll
         for (int i = 0; i < C::UV; ++i) {
-            const int u = tid + i * kPThreads;
+            const int u = tid + i * C::THREADS;
             if (u >= C::V_UNITS) continue;
             if (!two && u >= C::V_UNITS / 2) {
                 // absent block: zero its V columns so masked products stay 0
@@ -646,7 +652,7 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
     // tile's V_hat is therefore read one iteration after its K_hat (three
     // V_hat buffers).  Without room for three, every wave runs S(k),
     // softmax(k), PV(k).
-    const bool late = C::PINGPONG && wave >= kPWaves / 2;
+    const bool late = C::PINGPONG && wave >= C::WAVES / 2;
     bool have_s = false;  // S holds the scores of tile - 1 (late waves)
     bool have_p = false;  // P holds the probabilities of tile - 1
     for (int tile = 0; tile < ntiles; ++tile) {
@@ -672,16 +678,16 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
             // other's matrix products (PV first measured faster)
             pv(tile - 1);
             scores(tile);
-            reads_ahead_of_products<C::CB * 2 + 4 * C::KSTEPS, C::CB * 2 * C::NT + 4 * C::NT * C::KSTEPS, kReadLead>();
+            reads_ahead_of_products<C::CB * 2 + 4 * C::KSTEPS, C::CB * 2 * C::NT + 4 * C::NT * C::KSTEPS, read_lead<D>()>();
             have_p = false;
         } else {
             if (act) {
                 scores(tile);
-                reads_ahead_of_products<4 * C::KSTEPS, 4 * C::NT * C::KSTEPS, kReadLead>();
+                reads_ahead_of_products<4 * C::KSTEPS, 4 * C::NT * C::KSTEPS, read_lead<D>()>();
             }
             if (have_p) {
                 pv(tile - 1);
-                reads_ahead_of_products<C::CB * 2, C::CB * 2 * C::NT, kReadLead>();
+                reads_ahead_of_products<C::CB * 2, C::CB * 2 * C::NT, read_lead<D>()>();
                 have_p = false;
             }
         }
@@ -693,7 +699,7 @@ __global__ __launch_bounds__(kPThreads, 1) void prefill_kernel(PrefillArgs a) {
                 if constexpr (C::PINGPONG) have_p = true;
                 else {
                     pv(tile);
-                    reads_ahead_of_products<C::CB * 2, C::CB * 2 * C::NT, kReadLead>();
+                    reads_ahead_of_products<C::CB * 2, C::CB * 2 * C::NT, read_lead<D>()>();
                 }
             }
         }
@@ -751,7 +757,7 @@ hipError_t launch_ptyped_p(const PrefillArgs &a, hipStream_t s) {
     }
     const int ncols = a.n_tokens * a.gqa;
     const dim3 grid((unsigned)((ncols + C::COLS - 1) / C::COLS * a.k.n_kv_heads));
-    prefill_kernel<D, KC, VC, PAGED><<<grid, dim3(kPThreads), lds, s>>>(a);
+    prefill_kernel<D, KC, VC, PAGED><<<grid, dim3(C::THREADS), lds, s>>>(a);
     return hipGetLastError();
 }
 
