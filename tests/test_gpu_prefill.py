@@ -6,8 +6,9 @@ matrix cores see K_hat, V_hat, the scaled query and P rounded to binary16).
 Covered: the tiny prefill enumerated in full, ragged prefix/chunk lengths,
 every codec pair, head_dim 64/128/256, several GQA ratios, a chunk at
 position 0, queries far outside the binary16 range, negative and zero softmax scales, the chunk of a middle sequence of a three-sequence
-cache over several workgroups at every head_dim, graph replays against the eager call, and the 2048-token
-chunk over a 32768-token prefix on every one of its 65536 (token, head) rows.
+cache over several workgroups at every head_dim, the 64K model's heads at head_dim 256 (ragged column groups,
+and the 2048-token chunk over 32768 rows sampled at every column-group boundary), graph replays against the
+eager call, and the 2048-token chunk over a 32768-token prefix on every one of its 65536 (token, head) rows.
 """
 import numpy as np
 import pytest
@@ -114,6 +115,36 @@ def test_workload_prefill_2048_over_32768(gpu, capsys):
     toks = np.repeat(np.arange(T), hq)
     heads = np.tile(np.arange(hq), T)
     _run(gpu, W["k_codec"], W["v_codec"], W["head_dim"], hq, W["n_kv_heads"], P, T, sample=(toks, heads),
+         capsys=capsys)
+
+
+@pytest.mark.parametrize("kc,vc", [("q4_g64", "q4_g64"), ("q8_0", "q4_0")])
+def test_head_dim_256_model_heads(gpu, kc, vc):
+    # the 64K model's heads (24/4, d 256) run 12-wave workgroups of 192
+    # (token, head) columns: 300 tokens x 6 heads = 1800 columns per kv-head
+    # make 10 column groups (the last one ragged), 40 workgroups dealt to the
+    # XCDs by kv-head
+    _run(gpu, kc, vc, 256, 24, 4, 500, 300, seed=21 + len(kc))
+
+
+def test_head_dim_256_chunk_2048_over_32768_sampled(gpu, capsys):
+    """The 2048-token chunk over a 32768-row prefix with the 64K model's heads
+    (24/4, d 256, Q4_G64): 256 workgroups of 192 columns, one per compute
+    unit.  Checked against the oracle on every column on either side of each
+    192-column group boundary of kv-heads 0 and 3, and on 64 evenly spaced
+    tokens with all 24 heads."""
+    P, T, hq, hkv = 32768, 2048, 24, 4
+    G = hq // hkv
+    cols = []
+    for kvh in (0, hkv - 1):
+        for i in range(1, T * G // 192):
+            cols += [(kvh, 192 * i - 1), (kvh, 192 * i)]
+    toks = [c // G for _, c in cols]
+    heads = [kvh * G + c % G for kvh, c in cols]
+    for t in np.linspace(0, T - 1, 64).astype(int):
+        toks += [int(t)] * hq
+        heads += list(range(hq))
+    _run(gpu, "q4_g64", "q4_g64", 256, hq, hkv, P, T, seed=23, sample=(np.array(toks), np.array(heads)),
          capsys=capsys)
 
 
