@@ -51,10 +51,11 @@ namespace kvq {
 
 namespace {
 
-// waves per workgroup: 8, and 12 at head_dim 256 (16 columns each, so that a
-// 2048-token chunk of 6-head groups over 4 kv-heads is 256 workgroups, one
-// round on the 256 compute units, instead of 384)
-constexpr int prefill_waves(int d) { return d == 256 ? 12 : 8; }
+// waves per workgroup: 8 of 32 columns at head_dim 128; 12 of 16 columns at
+// head_dim 256 (so that a 2048-token chunk of 6-head groups over 4 kv-heads is
+// 256 workgroups, one round on the 256 compute units, instead of 384); 16 of
+// 16 columns at head_dim 64 (four waves per SIMD fit in 128 VGPRs there)
+constexpr int prefill_waves(int d) { return d == 256 ? 12 : (d == 64 ? 16 : 8); }
 constexpr int kTileRows = 64;
 constexpr float kPRescaleThreshold = 8.0f;
 
@@ -88,7 +89,7 @@ template <int D, int KC, int VC, bool PAGED = false>
 struct PCfg {
     static constexpr int KSTEPS = D / 32;
     static constexpr int CB = D / 16;
-    static constexpr int NT = D == 256 ? 1 : 2;  // 16-column tiles per wave
+    static constexpr int NT = D == 128 ? 2 : 1;  // 16-column tiles per wave
     static constexpr int WAVES = prefill_waves(D);
     static constexpr int THREADS = 64 * WAVES;
     static constexpr int COLS = WAVES * 16 * NT;
