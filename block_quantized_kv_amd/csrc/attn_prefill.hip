@@ -9,9 +9,10 @@
 //
 // Design:
 //  * A "column" is one (token, head) pair of a kv-head's GQA group, ordered
-//    token-major.  A workgroup of 8 waves owns 256 consecutive columns (16*NT
-//    per wave) of one kv-head, so every K/V tile it dequantizes serves all of
-//    them; tiles are 64 rows (two cache blocks).
+//    token-major.  A workgroup owns consecutive columns of one kv-head (16*NT
+//    per wave: 8 waves of 32 at head_dim 128, 12 of 16 at 256, 16 of 16 at
+//    64), so every K/V tile it dequantizes serves all of them; tiles are 64
+//    rows (two cache blocks).
 //  * Per tile, the workgroup dequantizes K and V into LDS as binary16 (code *
 //    scale, rounded to nearest even once): K_hat row-major, V_hat transposed
 //    [channel][row].  Codes become exact binary16 pairs by bit operations
