@@ -386,7 +386,8 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(Prefi
     uint32_t rk[C::UK][C::K_UW / 4], rv[C::UV][C::V_UW / 4];
     u4 rsc = u4{0u, 0u, 0u, 0u};
     uint16_t *sc_lds = reinterpret_cast<uint16_t *>(lds + C::OFF_SC);  // [2][SC_BYTES / 2]
-    auto load_tile = [&](int tile) {
+    // a tile's code words into this thread's registers
+    auto load_codes = [&](int tile) {
         const int64_t b0 = (int64_t)tile * 2;  // first block of the tile
         const bool two = b0 + 1 < nblocks_plane;  // the second block exists
         if constexpr (!PAGED) {
@@ -404,16 +405,6 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(Prefi
                 const int u = tid + i * C::THREADS;
                 if (u < C::V_UNITS && (two || u < C::V_UNITS / 2))
                     load_chunk<C::V_UW>(rv[i], vb + v_unit_offset<D, KC, VC>(u));
-            }
-            // the tile's scales, 16 bytes per thread: K (both blocks) then V
-            const int o = tid * 16;
-            if (o < C::KSC_BYTES) {
-                if (two || o < C::KSC_BYTES / 2)
-                    rsc = *reinterpret_cast<const u4 *>(reinterpret_cast<const uint8_t *>(kscales + b0 * C::K_BLOCK_SCALES) + o);
-            } else if (o < C::SC_BYTES) {
-                const int ov = o - C::KSC_BYTES;
-                if (two || ov < C::VSC_BYTES / 2)
-                    rsc = *reinterpret_cast<const u4 *>(reinterpret_cast<const uint8_t *>(vscales + b0 * C::V_BLOCK_SCALES) + ov);
             }
             return;
         }
@@ -446,19 +437,43 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(Prefi
 #pragma unroll
                 for (int w = 0; w < C::V_UW / 4; ++w) rv[i][w] = 0u;
         }
-        // the tile's scales, 16 bytes per thread: K (both blocks) then V;
-        // a block outside the pool gets zero scales
+    };
+    // a tile's scales, 16 bytes per thread of the first SC_BYTES / 16: K (both
+    // blocks) then V; under paging a block outside the pool gets zero scales
+    auto load_scales = [&](int tile) {
         const int o = tid * 16;
+        if (o >= C::SC_BYTES) return;
+        const int64_t b0 = (int64_t)tile * 2;
+        const bool two = b0 + 1 < nblocks_plane;
+        if constexpr (!PAGED) {
+            if (o < C::KSC_BYTES) {
+                if (two || o < C::KSC_BYTES / 2)
+                    rsc = *reinterpret_cast<const u4 *>(reinterpret_cast<const uint8_t *>(kscales + b0 * C::K_BLOCK_SCALES) + o);
+            } else {
+                const int ov = o - C::KSC_BYTES;
+                if (two || ov < C::VSC_BYTES / 2)
+                    rsc = *reinterpret_cast<const u4 *>(reinterpret_cast<const uint8_t *>(vscales + b0 * C::V_BLOCK_SCALES) + ov);
+            }
+            return;
+        }
+        const uint8_t *kb, *vb;
+        const uint16_t *ksb, *vsb;
         if (o < C::KSC_BYTES) {
             const int j = o >= C::KSC_BYTES / 2, oj = o - j * (C::KSC_BYTES / 2);
-            if (ok[j]) rsc = *reinterpret_cast<const u4 *>(reinterpret_cast<const uint8_t *>(ksb[j]) + oj);
+            const bool ok = (j == 0 || two) && block_at(b0 + j, kb, vb, ksb, vsb);
+            if (ok) rsc = *reinterpret_cast<const u4 *>(reinterpret_cast<const uint8_t *>(ksb) + oj);
             else rsc = u4{0u, 0u, 0u, 0u};
-        } else if (o < C::SC_BYTES) {
+        } else {
             const int ov = o - C::KSC_BYTES;
             const int j = ov >= C::VSC_BYTES / 2, oj = ov - j * (C::VSC_BYTES / 2);
-            if (ok[j]) rsc = *reinterpret_cast<const u4 *>(reinterpret_cast<const uint8_t *>(vsb[j]) + oj);
+            const bool ok = (j == 0 || two) && block_at(b0 + j, kb, vb, ksb, vsb);
+            if (ok) rsc = *reinterpret_cast<const u4 *>(reinterpret_cast<const uint8_t *>(vsb) + oj);
             else rsc = u4{0u, 0u, 0u, 0u};
         }
+    };
+    auto load_tile = [&](int tile) {
+        load_codes(tile);
+        load_scales(tile);
     };
     auto stage_scales = [&](int tile) {
         if (tid * 16 < C::SC_BYTES)
@@ -664,6 +679,11 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(Prefi
         if (late || !C::PINGPONG) {
             if (tile + 1 < ntiles) dequant_tile(tile + 1, kbuf(tile + 1), vbuf(tile + 1));
             if (tile + 2 < ntiles) load_tile(tile + 2);
+        } else if (tile + 2 < ntiles) {
+            // the early waves hold the staging threads: their scale loads
+            // go out first, so that the staging at the end of the iteration
+            // does not wait a memory round trip in front of the barrier
+            load_scales(tile + 2);
         }
         if (late && have_s) {
             softmax(tile - 1);
@@ -707,12 +727,11 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(Prefi
         }
         if (!late && C::PINGPONG) {
             if (tile + 1 < ntiles) dequant_tile(tile + 1, kbuf(tile + 1), vbuf(tile + 1));
-            if (tile + 2 < ntiles) load_tile(tile + 2);
+            if (tile + 2 < ntiles) load_codes(tile + 2);
         }
         // tile + 2's scales go where tile's were (read by its dequant, one
-        // iteration ago); under ping-pong the staging threads (wave 0) load
-        // them just before, which measured faster than staging them from
-        // the late waves, whose loads start at the top of the iteration
+        // iteration ago); the staging threads (wave 0) loaded them at the top
+        // of this iteration
         if (tile + 2 < ntiles) stage_scales(tile + 2);
         __syncthreads();  // next tile's dequant and staging done; this tile's reads done
     }
