@@ -515,6 +515,8 @@ def main():
         result["f16_control"] = run_f16_control(torch, dev, args)
     if not args.no_prefill:
         result["prefill"] = run_prefill(torch, dev, args)
+        if result["prefill"].get("status") != "unavailable":
+            result["prefill"]["other_head_dims"] = run_prefill_other_dims(torch, dev)
     if not args.no_quality:
         result["quality"] = run_quality(torch, dev, args)
 
@@ -817,6 +819,44 @@ def run_prefill(torch, dev, args):
                          "traffic": read_traffic("prefill"), "kv_bytes": kv_bytes,
                          "measured_mfma_peak": mp, "frac_of_measured_mfma_peak": round(tf / mp["tflops"], 4),
                          "counters": read_busy("prefill")}}
+
+
+def run_prefill_other_dims(torch, dev) -> list:
+    """The same 2048-token chunk over a 32768-row prefix at the other head
+    dims the kernel builds: 256 with the 64K decode model's heads (24/4, Q4_G64
+    and q8_0/q4_0) and 64 (32/8, q8_0/q4_0); 10 timed calls after 3 warm-up
+    calls each.  Context for the head_dim 128 figure above, not a separate
+    workload."""
+    import workloads
+    from block_quantized_kv_amd import Layer, kvq_append, kvq_attend_prefill
+    P, T = workloads.PREFILL["prefix"], workloads.PREFILL["chunk"]
+    res = []
+    for d, hq, hkv, kc, vc in ((256, 24, 4, "q4_g64", "q4_g64"), (256, 24, 4, "q8_0", "q4_0"),
+                               (64, 32, 8, "q8_0", "q4_0")):
+        q, k, v = workloads.prefill_inputs(dev, prefix=P, chunk=T, n_q_heads=hq, n_kv_heads=hkv, head_dim=d)
+        layer = Layer.create(kc, vc, d, hkv, 1, P + T, device=dev)
+        for a in range(0, P + T, 16384):
+            b = min(P + T, a + 16384)
+            kvq_append(layer, k[a:b].contiguous(), v[a:b].contiguous(),
+                       torch.zeros(b - a, dtype=torch.int32, device=dev),
+                       torch.arange(a, b, dtype=torch.int64, device=dev))
+        out = torch.empty(T, hq, d, device=dev)
+        for _ in range(3):
+            kvq_attend_prefill(layer, q, 0, P, 1.0 / d ** 0.5, out=out)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            kvq_attend_prefill(layer, q, 0, P, 1.0 / d ** 0.5, out=out)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 10
+        tf = 4.0 * d * hq * sum(P + t + 1 for t in range(T)) / (ms * 1e-3) / 1e12
+        res.append({"head_dim": d, "n_q_heads": hq, "n_kv_heads": hkv, "k_codec": kc, "v_codec": vc,
+                    "ms_per_chunk": round(ms, 4), "tflops": round(tf, 2),
+                    "frac_of_peak": round(tf / BF16_PEAK_TFLOPS, 4)})
+        del layer, q, k, v, out
+    return res
 
 
 def mfma_peak(torch, dev) -> dict:
