@@ -69,8 +69,9 @@ constexpr int clamp_width(int w, int lo, int hi) { return w < lo ? lo : (w > hi 
 // LEAD reads stay in flight ahead of the products that use them (left to
 // itself the scheduler waits on each read right after issuing it).  Four
 // reads ahead measured fastest with 8 waves (2, 3, 5, 8 and 12 tried; 6 spills
-// at head_dim 128); with the 12 waves of head_dim 256 (168 VGPRs each) two
-// spill least and measured fastest.
+// at head_dim 128) and with the 16 waves of head_dim 64 (6 and 8 no faster);
+// with the 12 waves of head_dim 256 (168 VGPRs each) two measured fastest (one
+// and three slower, the latter by 20 % for q8_0 / q4_0).
 template <int D>
 constexpr int read_lead() { return D == 256 ? 2 : 4; }
 template <int NR, int NM, int LEAD_>
