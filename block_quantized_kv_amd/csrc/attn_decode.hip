@@ -545,10 +545,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecodeArgs a) {
         if constexpr (paged) {
             int page = -1, within = 0;
             if (idx < nblk) {
-                const int64_t gb = blk0 + idx;
-                const int j = (int)(gb / pblk - pg0);
+                const PageSlot ps = page_slot(blk0 + idx, pblk);
+                const int j = (int)(ps.entry - pg0);
                 page = __builtin_amdgcn_readlane(j < 64 ? pages[0] : pages[1], j & 63);
-                within = (int)(gb % pblk);
+                within = ps.within;
             }
             bs = page_block_streams<D, KC, VC>(a, page, kvh, within);
             bidx = 0;

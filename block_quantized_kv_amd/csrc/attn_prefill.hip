@@ -368,10 +368,11 @@ __global__ __launch_bounds__(64 * prefill_waves(D), 1) void prefill_kernel(Prefi
             vs = vscales + gb * C::V_BLOCK_SCALES;
             return true;
         } else {
-            const int page = page_lds[gb / pblk];
+            const PageSlot ps = page_slot(gb, pblk);
+            const int page = page_lds[ps.entry];
             if (page < 0 || page >= a.k.n_seqs) return false;
             const int64_t hl = (int64_t)page * a.k.n_kv_heads + kvh;
-            const int64_t within = gb % pblk;
+            const int64_t within = ps.within;
             kc = a.k.codes + hl * a.k.head_code_stride + within * C::K_BLOCK_BYTES;
             vc = a.v.codes + hl * a.v.head_code_stride + within * C::V_BLOCK_BYTES;
             ks = a.k.scales + hl * a.k.head_scale_stride + within * C::K_BLOCK_SCALES;

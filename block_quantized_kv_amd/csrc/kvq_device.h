@@ -175,4 +175,25 @@ __device__ __forceinline__ float quad_sum(float v) { return swap_sum32(swap_sum1
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Block gb of a paged sequence: its block-table index and its block within
+// that page, for pages of pblk blocks (pblk >= 1).  A power-of-two page is a
+// shift and a mask; otherwise one 32-bit division while the block index fits,
+// and the 64-bit one beyond (a 64-bit division is a long scalar sequence with
+// branches, and the scalar unit is shared by every wave of the compute unit).
+struct PageSlot {
+    int64_t entry;
+    int within;
+};
+__device__ __forceinline__ PageSlot page_slot(int64_t gb, int pblk) {
+    if ((pblk & (pblk - 1)) == 0) {
+        const int sh = __builtin_ctz((unsigned)pblk);
+        return PageSlot{gb >> sh, (int)(gb & (pblk - 1))};
+    }
+    if (gb >= 0 && gb <= 0xFFFFFFFFll) {
+        const uint32_t g = (uint32_t)gb, q = g / (uint32_t)pblk;
+        return PageSlot{(int64_t)q, (int)(g - q * (uint32_t)pblk)};
+    }
+    return PageSlot{gb / pblk, (int)(gb % pblk)};
+}
+
 }  // namespace kvq

@@ -7,7 +7,8 @@ over it must return what attention over the contiguous layer returns: to
 get them, which moves the binary16 rounding of the probabilities), and
 within the decode bar of the oracle, 1e-3 of max|oracle|.
 
-Covered: pages of 32, 64, 256 and 2048 rows; pages shuffled over a pool
+Covered: pages of 32, 64, 96, 160, 256 and 2048 rows (96 and 160: not powers of two,
+so the page lookup divides); pages shuffled over a pool
 larger than needed; ragged lengths (a length inside a page, on a page
 boundary, shorter than a page); several sequences; one and two queries per
 sequence; the fused append + decode through the table; a table entry outside
@@ -130,7 +131,7 @@ def _case(gpu, kc, vc, d, hq, hkv, lens, page_rows, q_len=1, seed=0, fused=False
                 assert rel_err(out[s, i], ref) <= TOL, (kc, vc, d, n, page_rows, q_len, i)
 
 
-@pytest.mark.parametrize("page_rows", [32, 64, 256, 2048])
+@pytest.mark.parametrize("page_rows", [32, 64, 96, 160, 256, 2048])  # 96, 160: not powers of two
 def test_page_sizes(gpu, page_rows):
     _case(gpu, "q4_g64", "q4_0", 128, hq=8, hkv=2, lens=[1500, 700], page_rows=page_rows, seed=page_rows)
 
@@ -248,7 +249,7 @@ def _prefill_case(gpu, kc, vc, d, hq, hkv, P, T, page_rows, seed, seqs=1, seq=0,
     assert err <= PTOL, (kc, vc, d, P, T, page_rows, err)
 
 
-@pytest.mark.parametrize("page_rows", [32, 64, 256])
+@pytest.mark.parametrize("page_rows", [32, 64, 96, 256])  # 96: not a power of two
 @pytest.mark.parametrize("kc,vc,d", [("q8_0", "q4_0", 128), ("q4_g64", "q4_g64", 256), ("q4_0", "q8_0", 64)])
 def test_paged_prefill_matches_contiguous(gpu, kc, vc, d, page_rows):
     _prefill_case(gpu, kc, vc, d, 8, 2, 300, 77, page_rows, seed=page_rows + d)
