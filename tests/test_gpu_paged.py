@@ -250,7 +250,8 @@ def _prefill_case(gpu, kc, vc, d, hq, hkv, P, T, page_rows, seed, seqs=1, seq=0,
 
 
 @pytest.mark.parametrize("page_rows", [32, 64, 96, 256])  # 96: not a power of two
-@pytest.mark.parametrize("kc,vc,d", [("q8_0", "q4_0", 128), ("q4_g64", "q4_g64", 256), ("q4_0", "q8_0", 64)])
+@pytest.mark.parametrize("kc,vc,d", [("q8_0", "q4_0", 128), ("q4_g64", "q4_g64", 256), ("q8_0", "q4_0", 256),
+                                     ("q4_0", "q8_0", 64)])
 def test_paged_prefill_matches_contiguous(gpu, kc, vc, d, page_rows):
     _prefill_case(gpu, kc, vc, d, 8, 2, 300, 77, page_rows, seed=page_rows + d)
 
