@@ -848,8 +848,8 @@ def run_prefill(torch, dev, args):
 def run_prefill_other_dims(torch, dev) -> list:
     """The same 2048-token chunk over a 32768-row prefix at the other head
     dims the kernel builds: 256 with the 64K decode model's heads (24/4, Q4_G64
-    and q8_0/q4_0) and 64 (32/8, q8_0/q4_0); 10 timed calls after 3 warm-up
-    calls each.  Context for the head_dim 128 figure above, not a separate
+    and q8_0/q4_0) and 64 (32/8, q8_0/q4_0); 20 timed calls after a settling
+    run of the same call each.  Context for the head_dim 128 figure above, not a separate
     workload."""
     import workloads
     from block_quantized_kv_amd import Layer, kvq_append, kvq_attend_prefill
