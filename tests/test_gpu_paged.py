@@ -136,8 +136,8 @@ def test_page_sizes(gpu, page_rows):
     _case(gpu, "q4_g64", "q4_0", 128, hq=8, hkv=2, lens=[1500, 700], page_rows=page_rows, seed=page_rows)
 
 
-@pytest.mark.parametrize("kc,vc,d", [("q8_0", "q4_0", 128), ("q4_g64", "q4_g64", 256), ("q8_0", "q8_0", 64),
-                                     ("q4_0", "q4_g64", 64)])
+@pytest.mark.parametrize("kc,vc,d", [("q8_0", "q4_0", 128), ("q4_g64", "q4_g64", 256), ("q8_0", "q4_0", 256),
+                                     ("q8_0", "q8_0", 64), ("q4_0", "q4_g64", 64)])
 def test_codec_pairs(gpu, kc, vc, d):
     _case(gpu, kc, vc, d, hq=12, hkv=2, lens=[640, 65, 1], page_rows=64, seed=d + len(kc))
 
@@ -155,6 +155,12 @@ def test_two_queries(gpu):
 def test_fused_append(gpu, q_len, lens):
     _case(gpu, "q4_0", "q4_g64", 128, hq=8, hkv=2, lens=lens, page_rows=64, q_len=q_len, seed=q_len + 10,
           fused=True)
+
+
+@pytest.mark.parametrize("kc,vc", [("q4_g64", "q4_g64"), ("q8_0", "q4_0")])
+def test_fused_append_head_dim_256(gpu, kc, vc):
+    # the 64K model's head size through pages, two new rows per sequence
+    _case(gpu, kc, vc, 256, hq=12, hkv=2, lens=[1100, 33], page_rows=64, q_len=2, seed=len(kc) + 40, fused=True)
 
 
 def test_entry_outside_the_pool(gpu):
